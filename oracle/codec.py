@@ -1,0 +1,209 @@
+"""The codec end to end: quantize + pack, dequantize, packed-key scoring.
+
+Sources
+-------
+* NexusQuant blog, E8 walkthrough post, "Python Implementation" (the
+  quantizer): pad to a multiple of 8, split into 8-groups, amax per scale
+  group floored at 1e-8, scale = amax / (levels / 2), nearest lattice point
+  of the scaled group, rescale.  levels = 4 / 8 / 16 for 2 / 3 / 4 bits.
+* Same post, "Why Per-Group Scaling?": one fp16 scale per 8 values, or
+  ``quantize_perhead`` with one scale per 128-d head vector (0.125 bit/dim);
+  the scale group G is a parameter here.
+* Same post, "Bit Rate Accounting": b bits per coordinate (24 bits per
+  8-group at 3 bits) plus a 16-bit scale; we add one coset bit per 8-group so
+  that both cosets fit in b bits per coordinate.
+* nexusquant-kv 0.5.1 README, "How it works" steps 3-5 (RoPE removal on keys,
+  zero-padded Hadamard, E8 per 8-float group, K3V2 asymmetric bits) and
+  "Results" (scale_bpe = 16/128 at G = 128).
+* Same post, "What Makes This Hard in Practice" item 3: the compressed form
+  has to stay on the device and be unpacked on the fly -> dequantize.
+* Nedelkoski et al., "E8 Lattice Key Quantization for Low-Bit KV-Cache
+  Compression", Abstract and Table 3: attention scores computed from the
+  packed keys without dequantizing them.  The oracle scores by
+  dequantize-then-dot in fp64 (the kernel's table form is algebraically the
+  same number; the oracle does not use that algebra).
+
+Definitions (one head vector x of d values, n = next power of two >= d):
+  K only, theta > 0:  x' = RoPE^-1(x)       (fp32, transform.rope_inverse_f32)
+  v = (x', 0, ..., 0) in R^n;  u = H_n v     (fp32, transform.fwht_f32)
+  per scale group g of G coordinates:
+      a_g  = max(max_j |u_j|, fp32(1e-8 * sqrt(n)))   (1e-8 in orthonormal
+             units, z = u / sqrt(n))
+      r_g  = fp32((L/2) / a_g);  y_j = fp32(u_j * r_g)   -> max |y| = L/2
+      sigma_g = a_g / ((L/2) sqrt(n))  in fp64, stored as fp16 (RNE)
+  each 8-group of y -> lattice.decode -> idx in [0, L-1]^8, coset bit c
+  Dequantize: p = idx - L/2 + c/2;  z^ = s16 * p;  x^ = (H_n z^ / sqrt(n))[:d];
+  keys then get RoPE back (the README's re-application after quantization).
+  D0 denotes dequantization without the RoPE step (the codec frame).
+
+Packed planes, row-major over [S][H][T] vectors:
+  codes : n*b/8 bytes per vector; coordinate j occupies bits [j*b, j*b+b) of
+          the vector's little-endian bit stream
+  cosets: ceil(n/64) bytes per vector; bit m = coset of 8-group m
+  scales: n/G fp16 per vector
+
+Parity status: pinned (scale range, zero vector, pack/unpack round trip,
+plane sizes, strict parity of every group, lattice-point round trips,
+score = dot with an independent dequantization) -- tests/test_oracle_codec.py.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import lattice, transform
+
+__all__ = ["Codec", "quantize", "dequantize", "score", "pack_codes",
+           "unpack_codes", "pack_cosets", "unpack_cosets", "fp16_kv_bytes"]
+
+
+@dataclass(frozen=True)
+class Codec:
+    head_dim: int
+    bits: int
+    scale_group: int = 0      # 0 -> n (one scale per vector)
+    strict: bool = False
+    rope_theta: float = 0.0   # > 0: keys have RoPE removed before quantizing
+
+    @property
+    def n(self) -> int:
+        return transform.next_pow2(self.head_dim)
+
+    @property
+    def L(self) -> int:
+        return 1 << self.bits
+
+    @property
+    def G(self) -> int:
+        return self.n if self.scale_group == 0 else self.scale_group
+
+    @property
+    def code_bytes(self) -> int:
+        return self.n * self.bits // 8
+
+    @property
+    def coset_bytes(self) -> int:
+        return (self.n // 8 + 7) // 8
+
+    @property
+    def n_scales(self) -> int:
+        return self.n // self.G
+
+    @property
+    def vector_bytes(self) -> int:
+        return self.code_bytes + self.coset_bytes + 2 * self.n_scales
+
+
+def fp16_kv_bytes(layers: int, kv_heads: int, head_dim: int, tokens: int = 1):
+    """2 (K and V) x layers x heads x head_dim x tokens x 2 bytes (fp16).
+
+    NexusQuant blog, post on the KV cache formula, "The formula"."""
+    return 2 * layers * kv_heads * head_dim * tokens * 2
+
+
+def compute_y(x, codec: Codec, positions=None, is_key: bool = False):
+    """fp32 y [.., n], group maxima a [.., n/G] -- the decision input."""
+    x32 = np.asarray(x).astype(np.float32)
+    d = codec.head_dim
+    assert x32.shape[-1] == d
+    if is_key and codec.rope_theta > 0:
+        T = x32.shape[-2]
+        pos = np.arange(T) if positions is None else np.asarray(positions)
+        c32, s32 = transform.rope_table_f32(pos, codec.rope_theta, d)
+        x32 = transform.rope_inverse_f32(x32, c32, s32)
+    n = codec.n
+    v = np.zeros(x32.shape[:-1] + (n,), dtype=np.float32)
+    v[..., :d] = x32
+    u = transform.fwht_f32(v)
+    G = codec.G
+    ug = u.reshape(u.shape[:-1] + (n // G, G))
+    eps = np.float32(1e-8 * math.sqrt(n))
+    a = np.maximum(np.max(np.abs(ug), axis=-1), eps)            # fp32
+    r = np.float32(codec.L / 2) / a                              # fp32 division
+    y = (ug * r[..., None]).reshape(u.shape)                     # fp32 product
+    return y.astype(np.float32), a.astype(np.float32)
+
+
+def scales_from_maxima(a, codec: Codec) -> np.ndarray:
+    k = 1.0 / ((codec.L / 2) * math.sqrt(codec.n))
+    return (np.asarray(a, dtype=np.float32).astype(np.float64) * k).astype(np.float16)
+
+
+def pack_codes(idx, bits: int) -> np.ndarray:
+    """[.., n] codes in [0, 2^b) -> [.., n*b/8] bytes, little-endian stream."""
+    idx = np.asarray(idx, dtype=np.uint8)
+    sh = idx.shape
+    bitarr = ((idx[..., None] >> np.arange(bits, dtype=np.uint8)) & 1).astype(np.uint8)
+    bitarr = bitarr.reshape(sh[:-1] + (sh[-1] * bits,))
+    return np.packbits(bitarr, axis=-1, bitorder="little")
+
+
+def unpack_codes(codes, bits: int, n: int) -> np.ndarray:
+    codes = np.asarray(codes, dtype=np.uint8)
+    bitarr = np.unpackbits(codes, axis=-1, bitorder="little")[..., :n * bits]
+    bitarr = bitarr.reshape(codes.shape[:-1] + (n, bits)).astype(np.uint8)
+    return (bitarr << np.arange(bits, dtype=np.uint8)).sum(-1).astype(np.uint8)
+
+
+def pack_cosets(c, nbytes: int) -> np.ndarray:
+    c = np.asarray(c, dtype=np.uint8)
+    pad = nbytes * 8 - c.shape[-1]
+    if pad:
+        c = np.concatenate([c, np.zeros(c.shape[:-1] + (pad,), np.uint8)], -1)
+    return np.packbits(c, axis=-1, bitorder="little")
+
+
+def unpack_cosets(cs, groups: int) -> np.ndarray:
+    return np.unpackbits(np.asarray(cs, np.uint8), axis=-1,
+                         bitorder="little")[..., :groups]
+
+
+def quantize(x, codec: Codec, positions=None, is_key: bool = False):
+    """Quantize vectors x [.., d] -> dict of planes plus the decision data."""
+    y, a = compute_y(x, codec, positions, is_key)
+    lead = y.shape[:-1]
+    idx, c, _ = lattice.decode(y.reshape(-1, 8), codec.L, codec.strict)
+    ng = codec.n // 8
+    idx = idx.reshape(lead + (codec.n,))
+    c = c.reshape(lead + (ng,))
+    return {
+        "codes": pack_codes(idx, codec.bits),
+        "cosets": pack_cosets(c, codec.coset_bytes),
+        "scales": scales_from_maxima(a, codec),
+        "idx": idx, "c": c, "y": y, "a": a,
+    }
+
+
+def dequantize(codes, cosets, scales, codec: Codec, positions=None,
+               is_key: bool = False, apply_rope: bool = True) -> np.ndarray:
+    """fp64 reconstruction [.., d] of packed vectors."""
+    n, d, G = codec.n, codec.head_dim, codec.G
+    idx = unpack_codes(codes, codec.bits, n).astype(np.float64)
+    c = unpack_cosets(cosets, n // 8).astype(np.float64)
+    p = idx - codec.L / 2 + 0.5 * np.repeat(c, 8, axis=-1)
+    s = np.repeat(np.asarray(scales, np.float16).astype(np.float64), G, axis=-1)
+    z = s * p
+    x = transform.fwht_f64(z)[..., :d] / math.sqrt(n)
+    if is_key and apply_rope and codec.rope_theta > 0:
+        T = x.shape[-2]
+        pos = np.arange(T) if positions is None else np.asarray(positions)
+        x = transform.rope_forward_f64(x, pos, codec.rope_theta)
+    return x
+
+
+def score(q, codes, cosets, scales, codec: Codec) -> np.ndarray:
+    """S[s][h][t] = q[s][h] . D0(K)[s][h // (Hq/H)][t]   (fp64).
+
+    q: [S, Hq, d]; planes: [S, H, T, .]."""
+    q = np.asarray(q).astype(np.float64)
+    k = dequantize(codes, cosets, scales, codec, apply_rope=False)  # [S,H,T,d]
+    S, Hq, _ = q.shape
+    H = k.shape[1]
+    grp = Hq // H
+    out = np.empty((S, Hq, k.shape[2]))
+    for h in range(Hq):
+        out[:, h, :] = np.einsum("sd,std->st", q[:, h, :], k[:, h // grp])
+    return out

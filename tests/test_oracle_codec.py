@@ -1,0 +1,146 @@
+"""Pins of the oracle codec (scale, pack, dequantize, score) -- no GPU."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import codec as oc
+from oracle import lattice, transform
+
+GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "kv_bytes.json")))
+
+
+def _x(shape, seed, outliers=True):
+    rng = np.random.default_rng(seed)
+    x = rng.normal(size=shape)
+    if outliers:
+        x[..., rng.integers(0, shape[-1], 4)] *= 8
+    return x.astype(np.float16)
+
+
+def test_fp16_bytes_per_token_match_pages():
+    for m in GOLD["models"]:
+        assert oc.fp16_kv_bytes(m["layers"], m["kv_heads"], m["head_dim"]) == m["bytes_per_token"]
+
+
+def test_bits_per_element_accounting():
+    # pages' bpe counts codes + fp16 scale per 128; ours adds one coset bit per 8
+    for row in GOLD["bpe"]["rows"]:
+        k = oc.Codec(128, row["k"], 128)
+        v = oc.Codec(128, row["v"], 128)
+        ours = (k.vector_bytes + v.vector_bytes) * 8 / 256
+        assert ours - 1 / 8 == pytest.approx(row["bpe"])
+    # Llama k2v2, G=128: 36 B per vector -> 18,432 B per token (32 x 8 x 2 vectors)
+    assert oc.Codec(128, 2, 128).vector_bytes == 36
+    assert 32 * 8 * 2 * 36 == 18432
+    # Mistral K3 G=64 (54 B) + V2 G=64 (38 B)
+    assert oc.Codec(128, 3, 64).vector_bytes == 54 and oc.Codec(128, 2, 64).vector_bytes == 38
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("n", [8, 64, 128, 256])
+def test_pack_roundtrip(bits, n):
+    rng = np.random.default_rng(bits * n)
+    idx = rng.integers(0, 1 << bits, size=(3, 5, n)).astype(np.uint8)
+    packed = oc.pack_codes(idx, bits)
+    assert packed.shape[-1] == n * bits // 8
+    assert np.array_equal(oc.unpack_codes(packed, bits, n), idx)
+    # coordinate j sits at bits [j*b, j*b + b) of the little-endian stream
+    j = n // 2 + 1
+    stream = int.from_bytes(packed[1, 2].tobytes(), "little")
+    assert (stream >> (j * bits)) & ((1 << bits) - 1) == idx[1, 2, j]
+    c = rng.integers(0, 2, size=(3, 5, n // 8)).astype(np.uint8)
+    cb = oc.pack_cosets(c, (n // 8 + 7) // 8)
+    assert np.array_equal(oc.unpack_cosets(cb, n // 8), c)
+
+
+@pytest.mark.parametrize("cfg", [
+    oc.Codec(128, 2, 0, strict=False, rope_theta=5e5),
+    oc.Codec(128, 3, 64, strict=False, rope_theta=1e6),
+    oc.Codec(96, 2, 0, strict=True, rope_theta=1e4),
+    oc.Codec(8, 2, 8, strict=True),
+])
+def test_quantize_invariants(cfg):
+    x = _x((2, 3, 40, cfg.head_dim), 7)
+    for is_key in (False, True):
+        q = oc.quantize(x, cfg, is_key=is_key)
+        y, a = q["y"], q["a"]
+        g = np.abs(y).reshape(y.shape[:-1] + (cfg.n // cfg.G, cfg.G)).max(-1)
+        # the group maximum lands on L/2 up to one fp32 rounding of u * r
+        assert np.all(np.abs(g - cfg.L / 2) <= cfg.L / 2 * 2.0 ** -23)
+        assert q["codes"].shape[-1] == cfg.code_bytes
+        assert q["cosets"].shape[-1] == cfg.coset_bytes
+        assert q["scales"].shape[-1] == cfg.n_scales
+        p = lattice.codeword_points(q["idx"].reshape(-1, 8), q["c"].reshape(-1), cfg.L)
+        assert np.all(lattice.in_lattice(p, cfg.strict))
+        if cfg.strict:
+            assert np.all(q["idx"].reshape(-1, 8).astype(int).sum(-1) % 2 == 0)
+        # stored scale is sigma = a / ((L/2) sqrt(n)) rounded once to fp16
+        sig = a.astype(np.float64) / ((cfg.L / 2) * math.sqrt(cfg.n))
+        assert np.array_equal(q["scales"], sig.astype(np.float16))
+
+
+def test_zero_vector():
+    cfg = oc.Codec(128, 2, 0, strict=True, rope_theta=5e5)
+    x = np.zeros((1, 1, 3, 128), np.float16)
+    q = oc.quantize(x, cfg, is_key=True)
+    assert np.all(q["idx"] == 2) and np.all(q["c"] == 0)
+    r = oc.dequantize(q["codes"], q["cosets"], q["scales"], cfg, is_key=True)
+    assert np.all(r == 0)
+
+
+@pytest.mark.parametrize("cfg", [oc.Codec(128, 2, 0), oc.Codec(128, 3, 64, strict=True),
+                                 oc.Codec(64, 2, 32)])
+def test_dequantize_error_equals_lattice_error(cfg):
+    """With d = n and no RoPE the rotation is orthonormal, so the
+    reconstruction error equals sum_g sigma16_g^2 |y_g - p_g|^2 (up to the
+    fp16/fp32 roundings of the scale and of y)."""
+    x = _x((1, 2, 64, cfg.head_dim), 11)
+    q = oc.quantize(x, cfg)
+    r = oc.dequantize(q["codes"], q["cosets"], q["scales"], cfg)
+    err = ((r - x.astype(np.float64)) ** 2).sum(-1)
+    p = lattice.codeword_points(q["idx"].reshape(-1, 8), q["c"].reshape(-1), cfg.L)
+    p = p.reshape(q["y"].shape)
+    s16 = np.repeat(q["scales"].astype(np.float64), cfg.G, -1)
+    # z-frame residual with the stored scale: s16 * p vs z = sqrt-normalised u
+    z = transform.fwht_f64(np.pad(x.astype(np.float64),
+                                  [(0, 0)] * 3 + [(0, cfg.n - cfg.head_dim)])) / math.sqrt(cfg.n)
+    pred = ((s16 * p - z) ** 2).sum(-1)
+    np.testing.assert_allclose(err, pred, rtol=1e-9, atol=1e-12)
+    # and that residual is the lattice error up to the scale rounding
+    sig = np.repeat(q["a"].astype(np.float64) / ((cfg.L / 2) * math.sqrt(cfg.n)), cfg.G, -1)
+    lat = ((sig * (p - q["y"])) ** 2).sum(-1)
+    np.testing.assert_allclose(pred, lat, rtol=5e-3, atol=1e-6)
+
+
+def test_dequantize_reapplies_rope():
+    cfg = oc.Codec(128, 2, 0, rope_theta=5e5)
+    x = _x((1, 1, 50, 128), 3)
+    pos = np.arange(1000, 1050)
+    q = oc.quantize(x, cfg, positions=pos, is_key=True)
+    k = oc.dequantize(q["codes"], q["cosets"], q["scales"], cfg, positions=pos, is_key=True)
+    k0 = oc.dequantize(q["codes"], q["cosets"], q["scales"], cfg, apply_rope=False)
+    np.testing.assert_allclose(transform.rope_inverse_f64(k, pos, 5e5), k0, atol=1e-12)
+    rel = np.linalg.norm(k - x.astype(np.float64)) / np.linalg.norm(x.astype(np.float64))
+    assert rel < 0.35  # 2-bit: a coarse but bounded reconstruction
+
+
+def test_score_equals_rotated_query_form():
+    """Oracle score (dequantize-then-dot) against the rotated-query form
+    q~ . (s16 * p), q~ = H pad(q) / sqrt(n): the identity the table kernel
+    uses, computed here independently of codec.score."""
+    cfg = oc.Codec(96, 2, 32, strict=True)
+    S, H, Hq, T = 2, 2, 6, 30
+    k = _x((S, H, T, 96), 5)
+    q = _x((S, Hq, 96), 6, outliers=False)
+    pk = oc.quantize(k, cfg)
+    s = oc.score(q, pk["codes"], pk["cosets"], pk["scales"], cfg)
+    qt = transform.fwht_f64(np.pad(q.astype(np.float64), [(0, 0), (0, 0), (0, 32)])) / math.sqrt(128)
+    p = lattice.codeword_points(pk["idx"].reshape(-1, 8), pk["c"].reshape(-1), cfg.L).reshape(S, H, T, 128)
+    sc = np.repeat(pk["scales"].astype(np.float64), 32, -1)
+    for h in range(Hq):
+        ref = np.einsum("sd,std->st", qt[:, h], sc[:, h // 3] * p[:, h // 3])
+        np.testing.assert_allclose(s[:, h], ref, rtol=1e-12, atol=1e-12)
