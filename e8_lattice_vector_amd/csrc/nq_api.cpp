@@ -1,0 +1,271 @@
+// C-ABI front end of libnq: argument validation, layout arithmetic and
+// kernel launches.  Every check runs on the host before anything is
+// enqueued; nothing is allocated and no state is kept between calls.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/nq.h"
+#include "nq_internal.h"
+
+namespace {
+
+struct Layout {
+  int d, n, G, bits, L, code_bytes, coset_bytes, n_scales;
+};
+
+int next_pow2_min8(int d) {
+  int n = 8;
+  while (n < d) n <<= 1;
+  return n;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Validates the parts of the config that do not depend on K vs V.
+int check_config(const nq_config* c) {
+  if (c == nullptr) return NQ_ERR_INVALID_ARG;
+  const int d = c->head_dim;
+  if (d < 8 || d > 256 || (d % 8) != 0) return NQ_ERR_UNSUPPORTED;
+  if (!(c->bits_k == 2 || c->bits_k == 3)) return NQ_ERR_UNSUPPORTED;
+  if (!(c->bits_v == 2 || c->bits_v == 3)) return NQ_ERR_UNSUPPORTED;
+  if (c->parity != NQ_PARITY_STRICT && c->parity != NQ_PARITY_RELAXED)
+    return NQ_ERR_INVALID_ARG;
+  if (c->in_dtype != NQ_DTYPE_F16 && c->in_dtype != NQ_DTYPE_F32)
+    return NQ_ERR_INVALID_ARG;
+  if (!(c->rope_theta >= 0.0) || !isfinite(c->rope_theta)) return NQ_ERR_INVALID_ARG;
+  if (c->rope_theta > 0.0 && !(d == 8 || d % 16 == 0)) return NQ_ERR_UNSUPPORTED;
+  const int n = next_pow2_min8(d);
+  const int G = c->scale_group == 0 ? n : c->scale_group;
+  if (G < 8 || G > n || (G % 8) != 0 || (n % G) != 0) return NQ_ERR_UNSUPPORTED;
+  return NQ_OK;
+}
+
+Layout layout(const nq_config* c, int is_value) {
+  Layout l;
+  l.d = c->head_dim;
+  l.n = next_pow2_min8(l.d);
+  l.G = c->scale_group == 0 ? l.n : c->scale_group;
+  l.bits = is_value ? c->bits_v : c->bits_k;
+  l.L = 1 << l.bits;
+  l.code_bytes = l.n * l.bits / 8;
+  l.coset_bytes = (l.n / 8 + 7) / 8;
+  l.n_scales = l.n / l.G;
+  return l;
+}
+
+size_t rope_bytes(const nq_config* c, int64_t T) {
+  if (c->rope_theta <= 0.0) return 0;
+  const size_t b = (size_t)T * (size_t)(c->head_dim / 2) * sizeof(float2);
+  return (b + 255) & ~(size_t)255;
+}
+
+int check_packed(const nq_packed* p) {
+  if (p == nullptr || p->codes == nullptr || p->cosets == nullptr ||
+      p->scales == nullptr)
+    return NQ_ERR_INVALID_ARG;
+  if (!aligned16(p->codes) || !aligned16(p->cosets) || !aligned16(p->scales))
+    return NQ_ERR_INVALID_ARG;
+  return NQ_OK;
+}
+
+int check_shape(int64_t S, int32_t H, int64_t T) {
+  if (S <= 0 || H <= 0 || T <= 0) return NQ_ERR_INVALID_ARG;
+  // vector counts must fit the 1-D launch grids (2^31 - 1 blocks of >= 8)
+  if ((double)S * (double)H * (double)T > 8.0e9) return NQ_ERR_UNSUPPORTED;
+  return NQ_OK;
+}
+
+nq::TensorArgs tensor_args(const nq_config* c, const Layout& l, int64_t S,
+                           int32_t H, int64_t T, const nq_packed* p) {
+  nq::TensorArgs a;
+  memset(&a, 0, sizeof(a));
+  a.codes = static_cast<uint8_t*>(p->codes);
+  a.cosets = static_cast<uint8_t*>(p->cosets);
+  a.scales = static_cast<uint16_t*>(p->scales);
+  a.n_vec = S * (int64_t)H * T;
+  a.T = T;
+  a.d = l.d;
+  a.n = l.n;
+  a.G = l.G;
+  a.bits = l.bits;
+  a.strict = c->parity == NQ_PARITY_STRICT ? 1 : 0;
+  a.code_bytes = l.code_bytes;
+  a.coset_bytes = l.coset_bytes;
+  a.n_scales = l.n_scales;
+  a.eps = (float)(1e-8 * sqrt((double)l.n));
+  a.half_L = (float)(l.L / 2);
+  a.sigma_k = 1.0 / ((l.L / 2.0) * sqrt((double)l.n));
+  a.inv_sqrt_n = (float)(1.0 / sqrt((double)l.n));
+  return a;
+}
+
+// Builds the cos/sin table in the workspace when keys need RoPE.
+int prepare_rope(const nq_config* c, int64_t T, const int32_t* positions,
+                 void* ws, size_t ws_bytes, hipStream_t s, const float2** out) {
+  *out = nullptr;
+  const size_t need = rope_bytes(c, T);
+  if (need == 0) return NQ_OK;
+  if (ws == nullptr || ws_bytes < need) return NQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return NQ_ERR_INVALID_ARG;
+  nq::RopeFreqs f;
+  const int d = c->head_dim;
+  for (int i = 0; i < d / 2; ++i) f.omega[i] = pow(c->rope_theta, -(2.0 * i) / d);
+  float2* table = static_cast<float2*>(ws);
+  if (nq::launch_rope_table(positions, T, d, f, table, s) != hipSuccess)
+    return NQ_ERR_HIP;
+  *out = table;
+  return NQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t nq_packed_bytes(const nq_config* cfg, int is_value, int64_t n_vectors,
+                       int plane) {
+  if (check_config(cfg) != NQ_OK || n_vectors < 0) return 0;
+  const Layout l = layout(cfg, is_value);
+  switch (plane) {
+    case NQ_PLANE_CODES: return (size_t)n_vectors * l.code_bytes;
+    case NQ_PLANE_COSETS: return (size_t)n_vectors * l.coset_bytes;
+    case NQ_PLANE_SCALES: return (size_t)n_vectors * l.n_scales * 2;
+    default: return 0;
+  }
+}
+
+size_t nq_workspace_bytes(const nq_config* cfg, int64_t n_tokens) {
+  if (check_config(cfg) != NQ_OK || n_tokens < 0) return 0;
+  return rope_bytes(cfg, n_tokens);
+}
+
+const char* nq_status_string(int status) {
+  switch (status) {
+    case NQ_OK: return "ok";
+    case NQ_ERR_INVALID_ARG: return "invalid argument";
+    case NQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case NQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case NQ_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int nq_quantize_kv(const nq_config* cfg, const void* k, const void* v,
+                   int64_t S, int32_t H, int64_t T, const int32_t* positions,
+                   const nq_packed* pk, const nq_packed* pv, void* ws,
+                   size_t ws_bytes, void* stream) {
+  int st = check_config(cfg);
+  if (st != NQ_OK) return st;
+  if ((st = check_shape(S, H, T)) != NQ_OK) return st;
+  if (k == nullptr && v == nullptr) return NQ_ERR_INVALID_ARG;
+  if (k != nullptr && (!aligned16(k) || (st = check_packed(pk)) != NQ_OK))
+    return st != NQ_OK ? st : NQ_ERR_INVALID_ARG;
+  if (v != nullptr && (!aligned16(v) || (st = check_packed(pv)) != NQ_OK))
+    return st != NQ_OK ? st : NQ_ERR_INVALID_ARG;
+  if (positions != nullptr && !aligned16(positions)) return NQ_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const float2* rope = nullptr;
+  if (k != nullptr) {
+    if ((st = prepare_rope(cfg, T, positions, ws, ws_bytes, s, &rope)) != NQ_OK)
+      return st;
+    nq::TensorArgs a = tensor_args(cfg, layout(cfg, 0), S, H, T, pk);
+    a.x = k;
+    a.rope = rope;
+    if (nq::launch_quantize(a, cfg->in_dtype, s) != hipSuccess) return NQ_ERR_HIP;
+  }
+  if (v != nullptr) {
+    nq::TensorArgs a = tensor_args(cfg, layout(cfg, 1), S, H, T, pv);
+    a.x = v;
+    if (nq::launch_quantize(a, cfg->in_dtype, s) != hipSuccess) return NQ_ERR_HIP;
+  }
+  return NQ_OK;
+}
+
+int nq_dequantize_kv(const nq_config* cfg, const nq_packed* pk,
+                     const nq_packed* pv, int64_t S, int32_t H, int64_t T,
+                     const int32_t* positions, void* k_out, void* v_out,
+                     void* ws, size_t ws_bytes, void* stream) {
+  int st = check_config(cfg);
+  if (st != NQ_OK) return st;
+  if ((st = check_shape(S, H, T)) != NQ_OK) return st;
+  if (k_out == nullptr && v_out == nullptr) return NQ_ERR_INVALID_ARG;
+  if (k_out != nullptr && (!aligned16(k_out) || (st = check_packed(pk)) != NQ_OK))
+    return st != NQ_OK ? st : NQ_ERR_INVALID_ARG;
+  if (v_out != nullptr && (!aligned16(v_out) || (st = check_packed(pv)) != NQ_OK))
+    return st != NQ_OK ? st : NQ_ERR_INVALID_ARG;
+  if (positions != nullptr && !aligned16(positions)) return NQ_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (k_out != nullptr) {
+    const float2* rope = nullptr;
+    if ((st = prepare_rope(cfg, T, positions, ws, ws_bytes, s, &rope)) != NQ_OK)
+      return st;
+    nq::TensorArgs a = tensor_args(cfg, layout(cfg, 0), S, H, T, pk);
+    a.y = k_out;
+    a.rope = rope;
+    if (nq::launch_dequantize(a, cfg->in_dtype, s) != hipSuccess) return NQ_ERR_HIP;
+  }
+  if (v_out != nullptr) {
+    nq::TensorArgs a = tensor_args(cfg, layout(cfg, 1), S, H, T, pv);
+    a.y = v_out;
+    if (nq::launch_dequantize(a, cfg->in_dtype, s) != hipSuccess) return NQ_ERR_HIP;
+  }
+  return NQ_OK;
+}
+
+int nq_score_packed_keys(const nq_config* cfg, const nq_packed* pk, int64_t S,
+                         int32_t H, int32_t Hq, int64_t T, const void* q,
+                         float* scores, void* ws, size_t ws_bytes,
+                         void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  int st = check_config(cfg);
+  if (st != NQ_OK) return st;
+  if ((st = check_shape(S, H, T)) != NQ_OK) return st;
+  if (Hq <= 0 || Hq % H != 0) return NQ_ERR_INVALID_ARG;
+  if (S > 65535 || H > 65535) return NQ_ERR_UNSUPPORTED;
+  if ((st = check_packed(pk)) != NQ_OK) return st;
+  if (q == nullptr || scores == nullptr || !aligned16(q) || !aligned16(scores))
+    return NQ_ERR_INVALID_ARG;
+  const Layout l = layout(cfg, 0);
+  if ((size_t)(Hq / H) * l.n * sizeof(float) > 64 * 1024) return NQ_ERR_UNSUPPORTED;
+  nq::ScoreArgs a;
+  memset(&a, 0, sizeof(a));
+  a.codes = static_cast<const uint8_t*>(pk->codes);
+  a.cosets = static_cast<const uint8_t*>(pk->cosets);
+  a.scales = static_cast<const uint16_t*>(pk->scales);
+  a.q = q;
+  a.out = scores;
+  a.S = S;
+  a.T = T;
+  a.H = H;
+  a.Hq = Hq;
+  a.d = l.d;
+  a.n = l.n;
+  a.G = l.G;
+  a.bits = l.bits;
+  a.code_bytes = l.code_bytes;
+  a.coset_bytes = l.coset_bytes;
+  a.n_scales = l.n_scales;
+  a.half_L = (float)(l.L / 2);
+  a.inv_sqrt_n = (float)(1.0 / sqrt((double)l.n));
+  if (nq::launch_score(a, cfg->in_dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return NQ_ERR_HIP;
+  return NQ_OK;
+}
+
+int nq_e8_decode_debug(const float* y, int64_t n_groups, int32_t bits,
+                       int32_t parity, uint8_t* idx_out, uint8_t* coset_out,
+                       void* stream) {
+  if (y == nullptr || idx_out == nullptr || coset_out == nullptr || n_groups <= 0)
+    return NQ_ERR_INVALID_ARG;
+  if (!(bits == 2 || bits == 3)) return NQ_ERR_UNSUPPORTED;
+  if (parity != NQ_PARITY_STRICT && parity != NQ_PARITY_RELAXED)
+    return NQ_ERR_INVALID_ARG;
+  if (n_groups > ((int64_t)1 << 38)) return NQ_ERR_UNSUPPORTED;
+  if (nq::launch_decode_debug(y, n_groups, bits, parity == NQ_PARITY_STRICT,
+                              idx_out, coset_out,
+                              static_cast<hipStream_t>(stream)) != hipSuccess)
+    return NQ_ERR_HIP;
+  return NQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Internal interface between the C-ABI front end (nq_api.cpp) and the HIP
+// kernels (nq_kernels.hip).  Not installed; the public ABI is include/nq.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nq {
+
+// One KV tensor pass (quantize or dequantize).
+struct TensorArgs {
+  const void* x;        // quantize: input [S][H][T][d]
+  void* y;              // dequantize: output [S][H][T][d]
+  uint8_t* codes;       // packed planes (quantize writes, dequantize reads)
+  uint8_t* cosets;
+  uint16_t* scales;     // fp16 bits
+  const float2* rope;   // [T][d/2] (cos, sin), or nullptr: no RoPE step
+  int64_t n_vec;        // S * H * T
+  int64_t T;
+  int d, n, G, bits, strict, code_bytes, coset_bytes, n_scales;
+  float eps;            // fp32(1e-8 * sqrt(n)): floor of the group maximum of |H v|
+  float half_L;         // L / 2
+  double sigma_k;       // 1 / ((L/2) * sqrt(n)): stored scale = a * sigma_k
+  float inv_sqrt_n;     // fp32(1 / sqrt(n))
+};
+
+struct ScoreArgs {
+  const uint8_t* codes;
+  const uint8_t* cosets;
+  const uint16_t* scales;
+  const void* q;        // [S][Hq][d]
+  float* out;           // [S][Hq][T]
+  int64_t S, T;
+  int H, Hq, d, n, G, bits, code_bytes, coset_bytes, n_scales;
+  float half_L;
+  float inv_sqrt_n;
+};
+
+constexpr int kMaxHalfDim = 128;
+struct RopeFreqs {
+  double omega[kMaxHalfDim];  // theta^(-2i/d), computed on the host
+};
+
+hipError_t launch_rope_table(const int32_t* positions, int64_t T, int d,
+                             const RopeFreqs& f, float2* table,
+                             hipStream_t stream);
+hipError_t launch_quantize(const TensorArgs& a, int in_dtype, hipStream_t s);
+hipError_t launch_dequantize(const TensorArgs& a, int out_dtype, hipStream_t s);
+hipError_t launch_score(const ScoreArgs& a, int in_dtype, hipStream_t s);
+hipError_t launch_decode_debug(const float* y, int64_t n_groups, int bits,
+                               int strict, uint8_t* idx, uint8_t* coset,
+                               hipStream_t s);
+
+}  // namespace nq

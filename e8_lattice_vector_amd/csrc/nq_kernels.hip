@@ -1,0 +1,535 @@
+// HIP kernels for E8 lattice KV-cache quantization on gfx950 (MI355X).
+//
+// Layout on the wave: one 8-group (8 consecutive coordinates of the padded
+// head vector) per lane, n/8 consecutive lanes per vector, 64/(n/8) vectors
+// per wave64.  The Walsh-Hadamard butterflies over strides 1, 2, 4 run inside
+// the lane; strides 8 .. n/2 pair lanes m and m ^ (stride/8).  Every
+// butterfly is one correctly rounded fp32 add or subtract and the stages run
+// in the order 1, 2, 4, ..., n/2, so the rotated vector -- and the scaled
+// value y on which the lattice decision is taken -- is reproducible bit for
+// bit by any implementation of the same stage order.
+//
+// Pages: NexusQuant blog, E8 walkthrough post ("The Conway-Sloane
+// Nearest-Point Algorithm", "Python Implementation", "Why Per-Group
+// Scaling?", "The Relaxed Parity Discovery"); post "The E8 lattice quantizes
+// 8 numbers at once" ("Handling outliers": Hadamard rotation);
+// nexusquant-kv 0.5.1 README ("How it works": RoPE removal, zero padding);
+// Nedelkoski et al., "E8 Lattice Key Quantization for Low-Bit KV-Cache
+// Compression" (Abstract, Table 3: scoring packed keys without
+// dequantizing).
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <math.h>
+
+#include "nq_internal.h"
+
+namespace nq {
+namespace {
+
+constexpr int kBlock = 256;
+
+__device__ __forceinline__ float h2f(uint16_t h) {
+  return __half2float(__ushort_as_half(h));
+}
+__device__ __forceinline__ uint16_t f2h_rn(float f) {
+  return __half_as_ushort(__float2half_rn(f));
+}
+
+// fp64 -> fp16 with a single rounding to nearest-even: round to odd into
+// fp32 first (24 bits >= 11 + 2), then round to nearest-even into fp16.
+__device__ __forceinline__ uint16_t f64_to_f16_rn(double x) {
+  float f = (float)x;
+  const double back = (double)f;
+  if (back != x) {
+    uint32_t b = __float_as_uint(f);
+    if (fabs(back) > fabs(x)) b -= 1u;
+    b |= 1u;
+    f = __uint_as_float(b);
+  }
+  return f2h_rn(f);
+}
+
+template <typename T>
+struct Io;
+
+template <>
+struct Io<__half> {
+  static __device__ __forceinline__ void load8(const void* base, int64_t off,
+                                               float v[8]) {
+    const uint4 w = *reinterpret_cast<const uint4*>(
+        static_cast<const uint16_t*>(base) + off);
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = h2f((uint16_t)(u[i] & 0xffffu));
+      v[2 * i + 1] = h2f((uint16_t)(u[i] >> 16));
+    }
+  }
+  static __device__ __forceinline__ void store8(void* base, int64_t off,
+                                                const float v[8]) {
+    uint32_t u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      u[i] = (uint32_t)f2h_rn(v[2 * i]) | ((uint32_t)f2h_rn(v[2 * i + 1]) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off) =
+        make_uint4(u[0], u[1], u[2], u[3]);
+  }
+  static __device__ __forceinline__ float load1(const void* base, int64_t off) {
+    return h2f(static_cast<const uint16_t*>(base)[off]);
+  }
+};
+
+template <>
+struct Io<float> {
+  static __device__ __forceinline__ void load8(const void* base, int64_t off,
+                                               float v[8]) {
+    const float4* p =
+        reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    const float4 a = p[0], b = p[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  static __device__ __forceinline__ void store8(void* base, int64_t off,
+                                                const float v[8]) {
+    float4* p = reinterpret_cast<float4*>(static_cast<float*>(base) + off);
+    p[0] = make_float4(v[0], v[1], v[2], v[3]);
+    p[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+  static __device__ __forceinline__ float load1(const void* base, int64_t off) {
+    return static_cast<const float*>(base)[off];
+  }
+};
+
+// Walsh-Hadamard stages 1, 2, 4 inside the lane.
+__device__ __forceinline__ void fwht_lane(float v[8]) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if ((k & h) == 0) {
+        const float a = v[k], b = v[k + h];
+        v[k] = __fadd_rn(a, b);
+        v[k + h] = __fsub_rn(a, b);
+      }
+    }
+  }
+}
+
+// Stages 8 .. 4*VL across the VL lanes of one vector (lane m holds
+// coordinates 8m .. 8m+7).  The lane with the stride bit clear keeps a + b,
+// its partner a - b.
+template <int VL>
+__device__ __forceinline__ void fwht_cross(float v[8], int m) {
+#pragma unroll
+  for (int s = 1; s < VL; s <<= 1) {
+    const bool upper = (m & s) != 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float o = __shfl_xor(v[k], s);
+      v[k] = upper ? __fsub_rn(o, v[k]) : __fadd_rn(v[k], o);
+    }
+  }
+}
+
+// Split-half RoPE on the lane's 8 coordinates.  inverse: x'_i = x_i c + x_{i+h}
+// s, x'_{i+h} = x_{i+h} c - x_i s; forward flips the sign of s.  Products and
+// sums are rounded separately.  All lanes of the wave must call this.
+template <bool INVERSE>
+__device__ __forceinline__ void rope_lane(float v[8], int m, int d,
+                                          const float2* row) {
+  const int h = d >> 1;
+  const int j0 = 8 * m;
+  float xp[8];
+  if (d == 8) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) xp[k] = v[k ^ 4];
+  } else {
+    const int hl = h >> 3;
+    const int pm = (m < hl) ? m + hl : m - hl;
+    const int src = (int)(threadIdx.x & 63) - m + pm;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) xp[k] = __shfl(v[k], src);
+  }
+  if (j0 < d) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int j = j0 + k;
+      const bool up = j >= h;
+      const float2 cs = row[up ? j - h : j];
+      const float a = __fmul_rn(v[k], cs.x);
+      const float b = __fmul_rn(xp[k], cs.y);
+      v[k] = (up == INVERSE) ? __fsub_rn(a, b) : __fadd_rn(a, b);
+    }
+  }
+}
+
+// Nearest codeword of the b-bit cube codebook for one 8-group.
+//
+// Works on g = 2y (exact) and a = |g|: with f = floor(a), the nearest even
+// integer to a is f + (f & 1) and the nearest odd one is f | 1 (ties away
+// from zero), clamped to the cube (L-2 resp. L-1 in these doubled units).
+// The parity step moves the coordinate with the largest "kappa" (|delta| if
+// the step toward y stays in the cube, -|delta| if it has to go away) by two;
+// its extra squared cost is 4 - 4 kappa.  The closer coset wins, the integer
+// coset on ties.  Output: b-bit codes idx = p + L/2 - c/2 packed little
+// endian, and the coset bit c.
+template <int BITS, bool STRICT>
+__device__ __forceinline__ void e8_decode(const float y[8], uint32_t& code,
+                                          int& coset) {
+  constexpr int L = 1 << BITS;
+  int P0[8], P1[8];
+  float d0[8], d1[8];
+  int neg[8];
+  float D0 = 0.f, D1 = 0.f;
+  int S0 = 0, S1 = 0, NS = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float g = __fadd_rn(y[k], y[k]);
+    neg[k] = signbit(g) ? 1 : 0;
+    const float a = fabsf(g);
+    const int fi = (int)floorf(a);
+    P0[k] = min(fi + (fi & 1), L - 2);
+    P1[k] = min(fi | 1, L - 1);
+    d0[k] = __fsub_rn(a, (float)P0[k]);
+    d1[k] = __fsub_rn(a, (float)P1[k]);
+    D0 = __fmaf_rn(d0[k], d0[k], D0);
+    D1 = __fmaf_rn(d1[k], d1[k], D1);
+    S0 += P0[k];
+    S1 += P1[k];
+    NS += neg[k];
+  }
+  const int odd0 = (S0 >> 1) & 1;
+  const int odd1 = STRICT ? (((S1 + 2 * NS) >> 1) & 1) : 0;
+  float b0 = -INFINITY, b1 = -INFINITY;
+  int i0 = 0, i1 = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const bool ok0 = (d0[k] < 0.f) || (P0[k] <= L - 4);
+    const float k0 = ok0 ? fabsf(d0[k]) : -fabsf(d0[k]);
+    if (k0 > b0) { b0 = k0; i0 = k; }
+    if (STRICT) {
+      const bool ok1 = (d1[k] < 0.f) || (P1[k] <= L - 3);
+      const float k1 = ok1 ? fabsf(d1[k]) : -fabsf(d1[k]);
+      if (k1 > b1) { b1 = k1; i1 = k; }
+    }
+  }
+  if (odd0) D0 = __fadd_rn(D0, __fmaf_rn(-4.f, b0, 4.f));
+  if (STRICT && odd1) D1 = __fadd_rn(D1, __fmaf_rn(-4.f, b1, 4.f));
+  const int c = (D1 < D0) ? 1 : 0;
+  const int odd = c ? odd1 : odd0;
+  const int is = c ? i1 : i0;
+  uint32_t w = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    int P = c ? P1[k] : P0[k];
+    if (odd && k == is) {
+      const float dd = c ? d1[k] : d0[k];
+      const bool ok = (dd < 0.f) || (P <= L - 4 + c);
+      const int t = (dd >= 0.f) ? 2 : -2;
+      P = ok ? P + t : P - t;
+    }
+    const int p2 = neg[k] ? -P : P;
+    const int idx = (p2 + L - c) >> 1;
+    w |= (uint32_t)idx << (BITS * k);
+  }
+  code = w;
+  coset = c;
+}
+
+template <int N, int BITS, bool STRICT, typename InT>
+__global__ __launch_bounds__(kBlock) void quantize_kernel(TensorArgs a) {
+  constexpr int VL = N / 8;
+  constexpr int VPB = kBlock / VL;
+  const int m = threadIdx.x % VL;
+  const int64_t vec = (int64_t)blockIdx.x * VPB + threadIdx.x / VL;
+  const bool live = vec < a.n_vec;
+  const int64_t vv = live ? vec : 0;
+  const int j0 = 8 * m;
+  float v[8];
+  if (j0 < a.d) {
+    Io<InT>::load8(a.x, vv * a.d + j0, v);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = 0.f;
+  }
+  if (a.rope != nullptr) {
+    const int64_t t = vv % a.T;
+    rope_lane<true>(v, m, a.d, a.rope + t * (a.d >> 1));
+  }
+  fwht_lane(v);
+  fwht_cross<VL>(v, m);
+  float mx = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) mx = fmaxf(mx, fabsf(v[k]));
+  const int gl = a.G >> 3;
+  for (int s = 1; s < gl; s <<= 1) mx = fmaxf(mx, __shfl_xor(mx, s));
+  const float amax = fmaxf(mx, a.eps);
+  const float r = __fdiv_rn(a.half_L, amax);
+  float y[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) y[k] = __fmul_rn(v[k], r);
+  uint32_t code;
+  int c;
+  e8_decode<BITS, STRICT>(y, code, c);
+  const uint64_t bal = __ballot(c);
+  if (!live) return;
+  uint8_t* cp = a.codes + vec * a.code_bytes + m * BITS;
+  if (BITS == 2) {
+    *reinterpret_cast<uint16_t*>(cp) = (uint16_t)code;
+  } else {
+    cp[0] = (uint8_t)(code & 0xffu);
+    cp[1] = (uint8_t)((code >> 8) & 0xffu);
+    cp[2] = (uint8_t)(code >> 16);
+  }
+  if (m == 0) {
+    const int lane = threadIdx.x & 63;
+    const uint32_t bits = (uint32_t)(bal >> lane) &
+                          (VL >= 32 ? 0xffffffffu : ((1u << VL) - 1u));
+    uint8_t* q = a.cosets + vec * a.coset_bytes;
+    for (int b = 0; b < a.coset_bytes; ++b) q[b] = (uint8_t)(bits >> (8 * b));
+  }
+  if (m % gl == 0) {
+    a.scales[vec * a.n_scales + m / gl] = f64_to_f16_rn((double)amax * a.sigma_k);
+  }
+}
+
+template <int N, int BITS, typename OutT>
+__global__ __launch_bounds__(kBlock) void dequantize_kernel(TensorArgs a) {
+  constexpr int VL = N / 8;
+  constexpr int VPB = kBlock / VL;
+  constexpr int L = 1 << BITS;
+  const int m = threadIdx.x % VL;
+  const int64_t vec = (int64_t)blockIdx.x * VPB + threadIdx.x / VL;
+  const bool live = vec < a.n_vec;
+  const int64_t vv = live ? vec : 0;
+  const uint8_t* cp = a.codes + vv * a.code_bytes + m * BITS;
+  uint32_t code;
+  if (BITS == 2) {
+    code = *reinterpret_cast<const uint16_t*>(cp);
+  } else {
+    code = (uint32_t)cp[0] | ((uint32_t)cp[1] << 8) | ((uint32_t)cp[2] << 16);
+  }
+  const int c = (a.cosets[vv * a.coset_bytes + (m >> 3)] >> (m & 7)) & 1;
+  const int gl = a.G >> 3;
+  const float s = h2f(a.scales[vv * a.n_scales + m / gl]) * a.inv_sqrt_n;
+  const float off = 0.5f * (float)c - a.half_L;
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int idx = (int)((code >> (BITS * k)) & (L - 1));
+    v[k] = ((float)idx + off) * s;
+  }
+  fwht_lane(v);
+  fwht_cross<VL>(v, m);
+  if (a.rope != nullptr) {
+    const int64_t t = vv % a.T;
+    rope_lane<false>(v, m, a.d, a.rope + t * (a.d >> 1));
+  }
+  const int j0 = 8 * m;
+  if (live && j0 < a.d) Io<OutT>::store8(a.y, vec * a.d + j0, v);
+}
+
+// One key per thread; the rotated queries of the GQA group (q~ = H pad(q))
+// sit in LDS and are read as broadcasts.  score = s16 . sum_j q~_j p_j / sqrt(n).
+constexpr int kScoreKeys = 1024;
+constexpr int kMaxGroup = 8;
+
+template <int N, int BITS, typename QT>
+__global__ __launch_bounds__(kBlock) void score_kernel(ScoreArgs a) {
+  constexpr int L = 1 << BITS;
+  constexpr int CB = N * BITS / 8;
+  extern __shared__ float qt[];
+  const int64_t s = blockIdx.z;
+  const int h = blockIdx.y;
+  const int grp = a.Hq / a.H;
+  for (int i = threadIdx.x; i < grp * N; i += blockDim.x) {
+    const int g = i / N, j = i % N;
+    const int64_t qh = s * a.Hq + (int64_t)h * grp + g;
+    qt[i] = (j < a.d) ? Io<QT>::load1(a.q, qh * a.d + j) : 0.f;
+  }
+  __syncthreads();
+  for (int hs = 1; hs < N; hs <<= 1) {
+    for (int i = threadIdx.x; i < grp * (N / 2); i += blockDim.x) {
+      const int g = i / (N / 2), r = i % (N / 2);
+      const int j = (r / hs) * 2 * hs + (r % hs);
+      const float x0 = qt[g * N + j], x1 = qt[g * N + j + hs];
+      qt[g * N + j] = x0 + x1;
+      qt[g * N + j + hs] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  const int64_t t_end = min(a.T, (int64_t)(blockIdx.x + 1) * kScoreKeys);
+  const int gl = a.G >> 3;
+  for (int64_t t = (int64_t)blockIdx.x * kScoreKeys + threadIdx.x; t < t_end;
+       t += blockDim.x) {
+    const int64_t vec = (s * a.H + h) * a.T + t;
+    uint8_t cb[CB];
+    const uint8_t* cp = a.codes + vec * a.code_bytes;
+#pragma unroll
+    for (int i = 0; i < CB; ++i) cb[i] = cp[i];
+    const uint8_t* csp = a.cosets + vec * a.coset_bytes;
+    for (int g0 = 0; g0 < grp; g0 += kMaxGroup) {
+      const int gn = min(kMaxGroup, grp - g0);
+      float acc[kMaxGroup];
+#pragma unroll
+      for (int g = 0; g < kMaxGroup; ++g) acc[g] = 0.f;
+      for (int sg = 0; sg < N / (gl * 8); ++sg) {
+        float part[kMaxGroup];
+#pragma unroll
+        for (int g = 0; g < kMaxGroup; ++g) part[g] = 0.f;
+        for (int mm = sg * gl; mm < (sg + 1) * gl; ++mm) {
+          const int c = (csp[mm >> 3] >> (mm & 7)) & 1;
+          const float off = 0.5f * (float)c - a.half_L;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int j = 8 * mm + k;
+            const int bit = j * BITS;
+            uint32_t two = (uint32_t)cb[bit >> 3] |
+                           ((bit >> 3) + 1 < CB ? (uint32_t)cb[(bit >> 3) + 1] << 8 : 0u);
+            const int idx = (int)((two >> (bit & 7)) & (L - 1));
+            const float p = (float)idx + off;
+            for (int g = 0; g < gn; ++g) part[g] = fmaf(qt[(g0 + g) * N + j], p, part[g]);
+          }
+        }
+        const float sc = h2f(a.scales[vec * a.n_scales + sg]);
+        for (int g = 0; g < gn; ++g) acc[g] = fmaf(part[g], sc, acc[g]);
+      }
+      for (int g = 0; g < gn; ++g) {
+        const int64_t qh = s * a.Hq + (int64_t)h * grp + g0 + g;
+        a.out[qh * a.T + t] = acc[g] * a.inv_sqrt_n;
+      }
+    }
+  }
+}
+
+template <int BITS, bool STRICT>
+__global__ __launch_bounds__(kBlock) void decode_debug_kernel(
+    const float* y, int64_t n, uint8_t* idx, uint8_t* coset) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  float v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = y[i * 8 + k];
+  uint32_t code;
+  int c;
+  e8_decode<BITS, STRICT>(v, code, c);
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+    idx[i * 8 + k] = (uint8_t)((code >> (BITS * k)) & ((1u << BITS) - 1u));
+  coset[i] = (uint8_t)c;
+}
+
+__global__ __launch_bounds__(kBlock) void rope_table_kernel(
+    const int32_t* pos, int64_t T, int h, RopeFreqs f, float2* table) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= T * h) return;
+  const int64_t t = i / h;
+  const int k = (int)(i % h);
+  const double p = pos ? (double)pos[t] : (double)t;
+  const double ang = p * f.omega[k];
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  table[i] = make_float2((float)cs, (float)sn);
+}
+
+template <int N, int BITS, typename T>
+hipError_t quantize_n(const TensorArgs& a, hipStream_t s) {
+  constexpr int VPB = kBlock / (N / 8);
+  const int64_t blocks = (a.n_vec + VPB - 1) / VPB;
+  if (a.strict)
+    hipLaunchKernelGGL((quantize_kernel<N, BITS, true, T>), dim3((unsigned)blocks),
+                       dim3(kBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL((quantize_kernel<N, BITS, false, T>), dim3((unsigned)blocks),
+                       dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int N, int BITS, typename T>
+hipError_t dequantize_n(const TensorArgs& a, hipStream_t s) {
+  constexpr int VPB = kBlock / (N / 8);
+  const int64_t blocks = (a.n_vec + VPB - 1) / VPB;
+  hipLaunchKernelGGL((dequantize_kernel<N, BITS, T>), dim3((unsigned)blocks),
+                     dim3(kBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int N, int BITS, typename T>
+hipError_t score_n(const ScoreArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.T + kScoreKeys - 1) / kScoreKeys), (unsigned)a.H,
+                  (unsigned)a.S);
+  const size_t lds = sizeof(float) * (size_t)(a.Hq / a.H) * N;
+  hipLaunchKernelGGL((score_kernel<N, BITS, T>), grid, dim3(kBlock), lds, s, a);
+  return hipGetLastError();
+}
+
+#define NQ_DISPATCH_N(n, FN, BITS, T, ...)                \
+  switch (n) {                                            \
+    case 8: return FN<8, BITS, T>(__VA_ARGS__);           \
+    case 16: return FN<16, BITS, T>(__VA_ARGS__);         \
+    case 32: return FN<32, BITS, T>(__VA_ARGS__);         \
+    case 64: return FN<64, BITS, T>(__VA_ARGS__);         \
+    case 128: return FN<128, BITS, T>(__VA_ARGS__);       \
+    case 256: return FN<256, BITS, T>(__VA_ARGS__);       \
+    default: return hipErrorInvalidValue;                 \
+  }
+
+template <typename T>
+hipError_t quantize_t(const TensorArgs& a, hipStream_t s) {
+  if (a.bits == 2) { NQ_DISPATCH_N(a.n, quantize_n, 2, T, a, s) }
+  if (a.bits == 3) { NQ_DISPATCH_N(a.n, quantize_n, 3, T, a, s) }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t dequantize_t(const TensorArgs& a, hipStream_t s) {
+  if (a.bits == 2) { NQ_DISPATCH_N(a.n, dequantize_n, 2, T, a, s) }
+  if (a.bits == 3) { NQ_DISPATCH_N(a.n, dequantize_n, 3, T, a, s) }
+  return hipErrorInvalidValue;
+}
+
+template <typename T>
+hipError_t score_t(const ScoreArgs& a, hipStream_t s) {
+  if (a.bits == 2) { NQ_DISPATCH_N(a.n, score_n, 2, T, a, s) }
+  if (a.bits == 3) { NQ_DISPATCH_N(a.n, score_n, 3, T, a, s) }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_rope_table(const int32_t* positions, int64_t T, int d,
+                             const RopeFreqs& f, float2* table,
+                             hipStream_t stream) {
+  const int h = d / 2;
+  const int64_t total = T * h;
+  const int64_t blocks = (total + kBlock - 1) / kBlock;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(kBlock), 0,
+                     stream, positions, T, h, f, table);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const TensorArgs& a, int in_dtype, hipStream_t s) {
+  return in_dtype == 0 ? quantize_t<__half>(a, s) : quantize_t<float>(a, s);
+}
+
+hipError_t launch_dequantize(const TensorArgs& a, int out_dtype, hipStream_t s) {
+  return out_dtype == 0 ? dequantize_t<__half>(a, s) : dequantize_t<float>(a, s);
+}
+
+hipError_t launch_score(const ScoreArgs& a, int in_dtype, hipStream_t s) {
+  return in_dtype == 0 ? score_t<__half>(a, s) : score_t<float>(a, s);
+}
+
+hipError_t launch_decode_debug(const float* y, int64_t n, int bits, int strict,
+                               uint8_t* idx, uint8_t* coset, hipStream_t s) {
+  const int64_t blocks = (n + kBlock - 1) / kBlock;
+  const dim3 g((unsigned)blocks), b(kBlock);
+  if (bits == 2 && strict) hipLaunchKernelGGL((decode_debug_kernel<2, true>), g, b, 0, s, y, n, idx, coset);
+  else if (bits == 2) hipLaunchKernelGGL((decode_debug_kernel<2, false>), g, b, 0, s, y, n, idx, coset);
+  else if (bits == 3 && strict) hipLaunchKernelGGL((decode_debug_kernel<3, true>), g, b, 0, s, y, n, idx, coset);
+  else if (bits == 3) hipLaunchKernelGGL((decode_debug_kernel<3, false>), g, b, 0, s, y, n, idx, coset);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace nq

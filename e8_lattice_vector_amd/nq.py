@@ -1,0 +1,255 @@
+"""ctypes binding of libnq (include/nq.h).  Argument marshalling only: every
+step of quantize / dequantize / score runs in the HIP kernels of libnq.so.
+
+Tensors are torch tensors in device memory; torch supplies allocation and
+the current stream.  The library itself allocates nothing.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnq.so")
+
+NQ_OK = 0
+NQ_ERR_INVALID_ARG = -1
+NQ_ERR_UNSUPPORTED = -2
+NQ_ERR_WORKSPACE = -3
+NQ_ERR_HIP = -4
+PARITY_STRICT = 0
+PARITY_RELAXED = 1
+DTYPE_F16 = 0
+DTYPE_F32 = 1
+PLANE_CODES, PLANE_COSETS, PLANE_SCALES = 0, 1, 2
+
+EXPORTED = ("nq_packed_bytes", "nq_workspace_bytes", "nq_status_string",
+            "nq_quantize_kv", "nq_dequantize_kv", "nq_score_packed_keys",
+            "nq_e8_decode_debug")
+
+
+class _Config(ctypes.Structure):
+    _fields_ = [("head_dim", ctypes.c_int32), ("bits_k", ctypes.c_int32),
+                ("bits_v", ctypes.c_int32), ("scale_group", ctypes.c_int32),
+                ("parity", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
+                ("rope_theta", ctypes.c_double)]
+
+
+class _Packed(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("cosets", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p)]
+
+
+class NQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libnq.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"libnq.so not built at {path}; run "
+                          "`python -m e8_lattice_vector_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    cfgp, pkp = ctypes.POINTER(_Config), ctypes.POINTER(_Packed)
+    lib.nq_packed_bytes.argtypes = [cfgp, ctypes.c_int, i64, ctypes.c_int]
+    lib.nq_packed_bytes.restype = sz
+    lib.nq_workspace_bytes.argtypes = [cfgp, i64]
+    lib.nq_workspace_bytes.restype = sz
+    lib.nq_status_string.argtypes = [ctypes.c_int]
+    lib.nq_status_string.restype = ctypes.c_char_p
+    lib.nq_quantize_kv.argtypes = [cfgp, vp, vp, i64, i32, i64, vp, pkp, pkp, vp, sz, vp]
+    lib.nq_quantize_kv.restype = ctypes.c_int
+    lib.nq_dequantize_kv.argtypes = [cfgp, pkp, pkp, i64, i32, i64, vp, vp, vp, vp, sz, vp]
+    lib.nq_dequantize_kv.restype = ctypes.c_int
+    lib.nq_score_packed_keys.argtypes = [cfgp, pkp, i64, i32, i32, i64, vp, vp, vp, sz, vp]
+    lib.nq_score_packed_keys.restype = ctypes.c_int
+    lib.nq_e8_decode_debug.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+    lib.nq_e8_decode_debug.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().nq_status_string(int(status)).decode()
+
+
+@dataclass(frozen=True)
+class Config:
+    """Mirror of nq_config."""
+    head_dim: int = 128
+    bits_k: int = 2
+    bits_v: int = 2
+    scale_group: int = 0
+    parity: int = PARITY_RELAXED
+    in_dtype: int = DTYPE_F16
+    rope_theta: float = 0.0
+
+    def c(self) -> _Config:
+        return _Config(self.head_dim, self.bits_k, self.bits_v, self.scale_group,
+                       self.parity, self.in_dtype, float(self.rope_theta))
+
+    @property
+    def n(self) -> int:
+        n = 8
+        while n < self.head_dim:
+            n *= 2
+        return n
+
+    @property
+    def torch_dtype(self):
+        return torch.float16 if self.in_dtype == DTYPE_F16 else torch.float32
+
+
+@dataclass
+class Packed:
+    codes: torch.Tensor
+    cosets: torch.Tensor
+    scales: torch.Tensor
+
+    def c(self) -> _Packed:
+        return _Packed(self.codes.data_ptr(), self.cosets.data_ptr(),
+                       self.scales.data_ptr())
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.codes, self.cosets, self.scales))
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
+def _check(status: int, what: str):
+    if status != NQ_OK:
+        raise NQError(status, what)
+
+
+def packed_bytes(cfg: Config, is_value: bool, n_vectors: int, plane: int) -> int:
+    cc = cfg.c()
+    return int(load().nq_packed_bytes(ctypes.byref(cc), int(is_value), int(n_vectors), plane))
+
+
+def workspace_bytes(cfg: Config, n_tokens: int) -> int:
+    cc = cfg.c()
+    return int(load().nq_workspace_bytes(ctypes.byref(cc), int(n_tokens)))
+
+
+def alloc_packed(cfg: Config, is_value: bool, S: int, H: int, T: int, device) -> Packed:
+    """Caller-side allocation of the three planes (torch owns the memory)."""
+    nv = S * H * T
+    planes = []
+    for plane in (PLANE_CODES, PLANE_COSETS, PLANE_SCALES):
+        nb = packed_bytes(cfg, is_value, nv, plane)
+        if nb == 0:
+            raise NQError(NQ_ERR_INVALID_ARG, "packed_bytes")
+        planes.append(torch.empty(nb, dtype=torch.uint8, device=device))
+    codes, cosets, scales = planes
+    return Packed(codes.view(S, H, T, -1), cosets.view(S, H, T, -1),
+                  scales.view(torch.float16).view(S, H, T, -1))
+
+
+def alloc_workspace(cfg: Config, T: int, device):
+    nb = workspace_bytes(cfg, T)
+    return None if nb == 0 else torch.empty(nb, dtype=torch.uint8, device=device)
+
+
+def quantize_kv(cfg: Config, k, v, positions=None, pk: Packed | None = None,
+                pv: Packed | None = None, workspace=None, stream=None):
+    """Quantize + pack K and/or V ([S][H][T][d] device tensors)."""
+    ref = k if k is not None else v
+    S, H, T, d = ref.shape
+    if d != cfg.head_dim:
+        raise NQError(NQ_ERR_INVALID_ARG, "quantize_kv head_dim")
+    for t in (k, v):
+        if t is not None and (t.dtype != cfg.torch_dtype or not t.is_contiguous()
+                              or tuple(t.shape) != (S, H, T, d)):
+            raise NQError(NQ_ERR_INVALID_ARG, "quantize_kv tensor")
+    if k is not None and pk is None:
+        pk = alloc_packed(cfg, False, S, H, T, k.device)
+    if v is not None and pv is None:
+        pv = alloc_packed(cfg, True, S, H, T, v.device)
+    if workspace is None and k is not None:
+        workspace = alloc_workspace(cfg, T, ref.device)
+    if positions is not None and (positions.dtype != torch.int32 or positions.numel() != T):
+        raise NQError(NQ_ERR_INVALID_ARG, "quantize_kv positions")
+    cc = cfg.c()
+    ck = pk.c() if pk is not None else None
+    cv = pv.c() if pv is not None else None
+    st = load().nq_quantize_kv(
+        ctypes.byref(cc), _ptr(k), _ptr(v), S, H, T, _ptr(positions),
+        ctypes.byref(ck) if ck is not None else None,
+        ctypes.byref(cv) if cv is not None else None,
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream))
+    _check(st, "nq_quantize_kv")
+    return pk, pv
+
+
+def dequantize_kv(cfg: Config, pk: Packed | None, pv: Packed | None, S: int, H: int,
+                  T: int, positions=None, k_out=None, v_out=None, workspace=None,
+                  stream=None):
+    dev = (pk if pk is not None else pv).codes.device
+    shape = (S, H, T, cfg.head_dim)
+    if pk is not None and k_out is None:
+        k_out = torch.empty(shape, dtype=cfg.torch_dtype, device=dev)
+    if pv is not None and v_out is None:
+        v_out = torch.empty(shape, dtype=cfg.torch_dtype, device=dev)
+    if workspace is None and pk is not None:
+        workspace = alloc_workspace(cfg, T, dev)
+    cc = cfg.c()
+    ck = pk.c() if pk is not None else None
+    cv = pv.c() if pv is not None else None
+    st = load().nq_dequantize_kv(
+        ctypes.byref(cc), ctypes.byref(ck) if ck is not None else None,
+        ctypes.byref(cv) if cv is not None else None, S, H, T, _ptr(positions),
+        _ptr(k_out if pk is not None else None), _ptr(v_out if pv is not None else None),
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream))
+    _check(st, "nq_dequantize_kv")
+    return (k_out if pk is not None else None), (v_out if pv is not None else None)
+
+
+def score_packed_keys(cfg: Config, pk: Packed, q, S: int, H: int, T: int,
+                      scores=None, stream=None):
+    """q: [S][Hq][d] device tensor -> fp32 scores [S][Hq][T]."""
+    Hq = q.shape[1]
+    if q.dtype != cfg.torch_dtype or not q.is_contiguous() or q.shape != (S, Hq, cfg.head_dim):
+        raise NQError(NQ_ERR_INVALID_ARG, "score_packed_keys q")
+    if scores is None:
+        scores = torch.empty((S, Hq, T), dtype=torch.float32, device=q.device)
+    cc = cfg.c()
+    ck = pk.c()
+    st = load().nq_score_packed_keys(ctypes.byref(cc), ctypes.byref(ck), S, H, Hq, T,
+                                     q.data_ptr(), scores.data_ptr(), None, 0,
+                                     _stream(stream))
+    _check(st, "nq_score_packed_keys")
+    return scores
+
+
+def e8_decode_debug(y, bits: int, parity: int, stream=None):
+    """y: device fp32 [N, 8] -> (idx uint8 [N, 8], coset uint8 [N])."""
+    if y.dtype != torch.float32 or y.dim() != 2 or y.shape[1] != 8 or not y.is_contiguous():
+        raise NQError(NQ_ERR_INVALID_ARG, "e8_decode_debug y")
+    n = y.shape[0]
+    idx = torch.empty((n, 8), dtype=torch.uint8, device=y.device)
+    cos = torch.empty((n,), dtype=torch.uint8, device=y.device)
+    st = load().nq_e8_decode_debug(y.data_ptr(), n, bits, parity, idx.data_ptr(),
+                                   cos.data_ptr(), _stream(stream))
+    _check(st, "nq_e8_decode_debug")
+    return idx, cos

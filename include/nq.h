@@ -1,0 +1,177 @@
+/*
+ * nq.h -- C ABI of libnq: E8 lattice quantization of a transformer KV cache
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Sources (cited by page and section):
+ *  [Walk]  NexusQuant blog (nexusquant.hashnode.dev), E8 walkthrough post:
+ *          "The E8 Lattice, Briefly", "The Conway-Sloane Nearest-Point
+ *          Algorithm", "Python Implementation", "Why Per-Group Scaling?",
+ *          "The Relaxed Parity Discovery", "Bit Rate Accounting",
+ *          "What Makes This Hard in Practice".
+ *  [Had]   Same blog, post "The E8 lattice quantizes 8 numbers at once",
+ *          "Handling outliers".
+ *  [RM]    nexusquant-kv 0.5.1 README, "How it works", "API reference"
+ *          (compress_kv_cache: head_dim, rope_base, bits), "Results".
+ *  [E8KQ]  Nedelkoski et al., "E8 Lattice Key Quantization for Low-Bit
+ *          KV-Cache Compression", Abstract and Table 3 (table-based
+ *          asymmetric scoring of packed keys).
+ *
+ * Conventions for every entry point
+ *  - Device pointers are HIP device (or managed) memory; host pointers are
+ *    marked "host".  The caller owns every buffer; the library allocates
+ *    nothing, keeps no state between calls and may be called from several
+ *    host threads at once (on different output buffers).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued asynchronously; the call returns once it is enqueued.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    negative nq_status means nothing was launched.  NQ_ERR_HIP reports a
+ *    launch failure.  Faults during execution surface at the caller's next
+ *    synchronisation.  Nothing throws across the ABI.
+ *  - Device pointers must be 16-byte aligned.
+ *  - Tensors are row-major.  A KV tensor is [S][H][T][d] ("slabs" S =
+ *    layers x batch, H KV heads, T tokens, head_dim d), fp16 (or fp32 when
+ *    cfg->in_dtype == NQ_DTYPE_F32).
+ *  - Inputs that are not finite, or whose group scale overflows fp16, give
+ *    unspecified codes (not checked).
+ */
+#ifndef NQ_H_
+#define NQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NQ_OK = 0,
+  NQ_ERR_INVALID_ARG = -1, /* null / misaligned pointer, bad size or shape */
+  NQ_ERR_UNSUPPORTED = -2, /* valid but not implemented (see nq_config)    */
+  NQ_ERR_WORKSPACE = -3,   /* workspace missing or smaller than required   */
+  NQ_ERR_HIP = -4          /* a HIP launch or API call failed              */
+} nq_status;
+
+enum { NQ_PARITY_STRICT = 0, NQ_PARITY_RELAXED = 1 };
+enum { NQ_DTYPE_F16 = 0, NQ_DTYPE_F32 = 1 };
+enum { NQ_PLANE_CODES = 0, NQ_PLANE_COSETS = 1, NQ_PLANE_SCALES = 2 };
+
+/* Codec parameters ([RM] "API reference": head_dim, rope_base, bits;
+ * [Walk] "Why Per-Group Scaling?": scale group; "The Relaxed Parity
+ * Discovery": parity mode).
+ *  head_dim    d, a multiple of 8 in [8, 256]; vectors are zero-padded to
+ *              n = the next power of two >= d ([RM] "How it works" step 4).
+ *              With rope_theta > 0, d must be 8 or a multiple of 16.
+ *  bits_k/v    2 or 3 bits per coordinate for keys / values (levels L = 2^b,
+ *              [Walk] "Python Implementation": 4 levels = 2-bit, 8 = 3-bit).
+ *  scale_group G: coordinates per fp16 scale; a multiple of 8 dividing n,
+ *              or 0 for G = n (one scale per head vector).
+ *  parity      NQ_PARITY_STRICT: E8 = D8 u (D8 + 1/2) (even coordinate sum
+ *              on both cosets); NQ_PARITY_RELAXED: D8 u (Z^8 + 1/2).
+ *  in_dtype    NQ_DTYPE_F16 or NQ_DTYPE_F32 for K/V/query inputs and for
+ *              dequantized outputs.
+ *  rope_theta  > 0: keys carry split-half RoPE with base theta (frequency
+ *              theta^(-2i/d), pair (i, i + d/2)); it is removed before
+ *              quantizing and re-applied on dequantize.  0: keys are
+ *              quantized as given (the README's "fast" mode, no RoPE removal).
+ */
+typedef struct {
+  int32_t head_dim;
+  int32_t bits_k;
+  int32_t bits_v;
+  int32_t scale_group;
+  int32_t parity;
+  int32_t in_dtype;
+  double rope_theta;
+} nq_config;
+
+/* Packed form of one KV tensor: three device planes, each row-major over the
+ * S*H*T vectors ([Walk] "Bit Rate Accounting": b bits per coordinate plus a
+ * 16-bit scale; one coset bit per 8-group is added so both cosets fit):
+ *   codes  : n*b/8 bytes per vector; coordinate j at bits [j*b, j*b+b) of the
+ *            vector's little-endian bit stream, value idx = p - c/2 + L/2
+ *   cosets : ceil(n/64) bytes per vector; bit m = 1 when 8-group m lies on
+ *            the half-integer coset
+ *   scales : n/G fp16 per vector, sigma = max|z| / (L/2) over the group, z the
+ *            orthonormally rotated vector
+ * The three pointers must be 16-byte aligned; sizes from nq_packed_bytes. */
+typedef struct {
+  void* codes;
+  void* cosets;
+  void* scales;
+} nq_packed;
+
+/* Host.  Bytes of one plane for n_vectors vectors of keys (is_value = 0) or
+ * values (is_value = 1).  Returns 0 for an invalid config or plane. */
+size_t nq_packed_bytes(const nq_config* cfg, int is_value, int64_t n_vectors,
+                       int plane);
+
+/* Host.  Workspace bytes that quantize / dequantize need for n_tokens tokens
+ * (the per-call RoPE cos/sin table, T * d/2 * 8 bytes rounded up to 256; 0
+ * when rope_theta == 0).  Scoring needs no workspace. */
+size_t nq_workspace_bytes(const nq_config* cfg, int64_t n_tokens);
+
+/* Host.  Static text for a status code. */
+const char* nq_status_string(int status);
+
+/* Quantize + pack a post-prefill KV cache ([RM] "How it works" steps 3-5,
+ * [Walk] "Python Implementation").  Per token and head: keys lose RoPE
+ * (rope_theta > 0), the vector is zero-padded to n and rotated by the
+ * Walsh-Hadamard matrix, scaled per group of G, and each 8-group is replaced
+ * by its nearest codeword of the lattice restricted to b-bit coordinates.
+ *  k, v        device [S][H][T][d] inputs; either may be NULL (then the
+ *              matching packed planes are not touched)
+ *  positions   device int32 [T] token positions for RoPE, or NULL for
+ *              0..T-1; values must be >= 0
+ *  pk, pv      host structs holding device plane pointers (outputs)
+ *  workspace   device scratch of nq_workspace_bytes(cfg, T) bytes
+ * Errors: NQ_ERR_INVALID_ARG (sizes <= 0, null config, misalignment),
+ * NQ_ERR_UNSUPPORTED (see nq_config), NQ_ERR_WORKSPACE, NQ_ERR_HIP. */
+int nq_quantize_kv(const nq_config* cfg, const void* k, const void* v,
+                   int64_t n_slabs, int32_t n_kv_heads, int64_t n_tokens,
+                   const int32_t* positions, const nq_packed* pk,
+                   const nq_packed* pv, void* workspace, size_t ws_bytes,
+                   void* stream);
+
+/* Inverse path ([Walk] "What Makes This Hard in Practice", item 3: unpack on
+ * the device; [RM] "How it works": RoPE re-applied after quantization):
+ * p = idx - L/2 + c/2, z = s16 * p, x = (H z / sqrt(n))[:d], keys get RoPE
+ * at `positions` (rope_theta > 0), rounded to the output dtype (RNE).
+ *  k_out, v_out  device [S][H][T][d] outputs (either may be NULL)
+ * Errors as nq_quantize_kv. */
+int nq_dequantize_kv(const nq_config* cfg, const nq_packed* pk,
+                     const nq_packed* pv, int64_t n_slabs, int32_t n_kv_heads,
+                     int64_t n_tokens, const int32_t* positions, void* k_out,
+                     void* v_out, void* workspace, size_t ws_bytes,
+                     void* stream);
+
+/* Table-based asymmetric q.k scoring on packed keys without dequantizing
+ * them ([E8KQ] Abstract, Table 3).  For query head h of slab s:
+ *   scores[s][h][t] = q[s][h] . D0(K)[s][h / (n_q_heads / n_kv_heads)][t]
+ * where D0 is the dequantization without the RoPE step (scores are taken in
+ * the codec frame; with rope_theta == 0 they are plain q.k logits).
+ *  q       device [S][n_q_heads][d] queries (in_dtype)
+ *  scores  device fp32 [S][n_q_heads][T]
+ * n_q_heads must be a positive multiple of n_kv_heads.  workspace may be NULL.
+ * Errors as nq_quantize_kv. */
+int nq_score_packed_keys(const nq_config* cfg, const nq_packed* pk,
+                         int64_t n_slabs, int32_t n_kv_heads,
+                         int32_t n_q_heads, int64_t n_tokens, const void* q,
+                         float* scores, void* workspace, size_t ws_bytes,
+                         void* stream);
+
+/* Test hook: the nearest-codeword decoder alone ([Walk] "The Conway-Sloane
+ * Nearest-Point Algorithm") on caller-given groups y (lattice units).
+ *  y          device fp32 [n_groups][8]
+ *  idx_out    device uint8 [n_groups][8], idx = p - c/2 + 2^bits/2
+ *  coset_out  device uint8 [n_groups]
+ * bits 2 or 3; parity NQ_PARITY_STRICT or NQ_PARITY_RELAXED. */
+int nq_e8_decode_debug(const float* y, int64_t n_groups, int32_t bits,
+                       int32_t parity, uint8_t* idx_out, uint8_t* coset_out,
+                       void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NQ_H_ */

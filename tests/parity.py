@@ -1,0 +1,88 @@
+"""Comparison helpers for GPU-vs-oracle parity tests.
+
+Acceptance (codes): packed code and coset bytes equal per 8-group, except
+groups where the GPU's codeword is a valid codeword whose squared distance to
+y exceeds the oracle's by less than 1e-6 (y in lattice units, fp64); such
+exempt groups must number at most 1e-6 of all groups.  Scales: equal bits.
+Dequantized vectors: |x_gpu - x_ref| <= 1e-3 |x_ref| per vector (plus 1e-6
+absolute for near-zero vectors).  Scores: |S_gpu - S_ref| <= 1e-3 |q| |D0 k|.
+"""
+
+import math
+
+import numpy as np
+
+from oracle import codec as oc
+from oracle import lattice
+
+REGRET_TOL = 1e-6
+EXEMPT_FRAC = 1e-6
+
+
+def oracle_codec(cfg, is_value: bool) -> oc.Codec:
+    return oc.Codec(cfg.head_dim, cfg.bits_v if is_value else cfg.bits_k,
+                    cfg.scale_group, cfg.parity == 0,
+                    0.0 if is_value else cfg.rope_theta)
+
+
+def to_np(packed):
+    return (packed.codes.cpu().numpy(), packed.cosets.cpu().numpy(),
+            packed.scales.cpu().numpy())
+
+
+def check_codes(codes, cosets, scales, ref, codec: oc.Codec, label=""):
+    """Compare GPU planes (numpy, [..., bytes]) with oracle.quantize output."""
+    n, L = codec.n, codec.L
+    codes = codes.reshape(-1, codec.code_bytes)
+    cosets = cosets.reshape(-1, codec.coset_bytes)
+    scales = scales.reshape(-1, codec.n_scales)
+    rc = ref["codes"].reshape(-1, codec.code_bytes)
+    rs = ref["cosets"].reshape(-1, codec.coset_bytes)
+    rsc = ref["scales"].reshape(-1, codec.n_scales)
+    assert codes.shape == rc.shape, (label, codes.shape, rc.shape)
+    # scales: bit-exact (both sides round a * (1/((L/2) sqrt n)) once to fp16)
+    bad_sc = np.nonzero(scales.view(np.uint16) != rsc.view(np.uint16))
+    assert len(bad_sc[0]) == 0, f"{label}: {len(bad_sc[0])} scale mismatches, first at {bad_sc[0][:5]}"
+    idx_g = oc.unpack_codes(codes, codec.bits, n).reshape(-1, 8)
+    c_g = oc.unpack_cosets(cosets, n // 8).reshape(-1)
+    idx_r = ref["idx"].reshape(-1, 8)
+    c_r = ref["c"].reshape(-1)
+    mism = np.any(idx_g != idx_r, axis=1) | (c_g != c_r)
+    n_groups = idx_r.shape[0]
+    n_bad = int(mism.sum())
+    stats = {"groups": n_groups, "exempt": n_bad, "max_regret": 0.0}
+    if n_bad:
+        y = ref["y"].reshape(-1, 8)[mism].astype(np.float64)
+        pg = lattice.codeword_points(idx_g[mism], c_g[mism], L)
+        pr = lattice.codeword_points(idx_r[mism], c_r[mism], L)
+        valid = lattice.in_lattice(pg, codec.strict)
+        regret = ((y - pg) ** 2).sum(-1) - ((y - pr) ** 2).sum(-1)
+        stats["max_regret"] = float(regret.max())
+        assert valid.all(), f"{label}: GPU emitted non-codewords"
+        assert (regret < REGRET_TOL).all(), f"{label}: regret {regret.max()} in {n_bad} groups"
+        assert n_bad <= math.floor(EXEMPT_FRAC * n_groups), \
+            f"{label}: {n_bad} exempt groups of {n_groups} (> 1e-6)"
+    # every byte of groups that agree is equal (also the unused coset bits)
+    vec_bad = mism.reshape(codes.shape[0], -1).any(axis=1)
+    assert np.array_equal(codes[~vec_bad], rc[~vec_bad]), label
+    assert np.array_equal(cosets[~vec_bad], rs[~vec_bad]), label
+    return stats
+
+
+def check_dequant(x_gpu, x_ref, label=""):
+    x_gpu = np.asarray(x_gpu, dtype=np.float64).reshape(-1, x_ref.shape[-1])
+    x_ref = np.asarray(x_ref, dtype=np.float64).reshape(x_gpu.shape)
+    err = np.linalg.norm(x_gpu - x_ref, axis=1)
+    lim = 1e-3 * np.linalg.norm(x_ref, axis=1) + 1e-6
+    bad = np.nonzero(err > lim)[0]
+    assert len(bad) == 0, f"{label}: {len(bad)} vectors off, worst rel {np.max(err / lim)}"
+    return float(np.max(err / lim))
+
+
+def check_scores(s_gpu, s_ref, qnorm, knorm, label=""):
+    s_gpu = np.asarray(s_gpu, dtype=np.float64)
+    lim = 1e-3 * qnorm * knorm + 1e-9
+    err = np.abs(s_gpu - s_ref)
+    bad = err > lim
+    assert not bad.any(), f"{label}: {int(bad.sum())} scores off, worst {np.max(err / lim)}"
+    return float(np.max(err / lim))

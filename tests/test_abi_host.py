@@ -1,0 +1,89 @@
+"""Host-side checks of libnq: it loads, exports every symbol include/nq.h
+declares, and rejects bad arguments before touching the GPU (no GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from e8_lattice_vector_amd import nq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "nq.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(nq_\w+)\s*\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    lib = nq.load()
+    names = _declared()
+    assert set(names) == set(nq.EXPORTED)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_plane_sizes_and_workspace():
+    c = nq.Config(128, 2, 2, 0, nq.PARITY_RELAXED, nq.DTYPE_F16, 5e5)
+    assert [nq.packed_bytes(c, 0, 10, p) for p in range(3)] == [320, 20, 20]
+    c3 = nq.Config(128, 3, 2, 64, nq.PARITY_RELAXED, nq.DTYPE_F16, 1e6)
+    assert [nq.packed_bytes(c3, 0, 1, p) for p in range(3)] == [48, 2, 4]
+    assert [nq.packed_bytes(c3, 1, 1, p) for p in range(3)] == [32, 2, 4]
+    c96 = nq.Config(96, 2, 2, 0, nq.PARITY_STRICT, nq.DTYPE_F16, 1e4)
+    assert [nq.packed_bytes(c96, 0, 1, p) for p in range(3)] == [32, 2, 2]
+    c8 = nq.Config(8, 2, 2, 8, nq.PARITY_STRICT, nq.DTYPE_F32, 0.0)
+    assert [nq.packed_bytes(c8, 0, 64, p) for p in range(3)] == [128, 64, 128]
+    assert nq.workspace_bytes(c, 32768) == 32768 * 64 * 8
+    assert nq.workspace_bytes(c, 3) == 1536
+    assert nq.workspace_bytes(nq.Config(8, 2, 2, 8, 0, 0, 1e4), 3) == 256
+    assert nq.workspace_bytes(c8, 64) == 0
+    assert nq.packed_bytes(c, 0, 1, 7) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(head_dim=7), dict(head_dim=264), dict(bits_k=4),
+                                dict(bits_v=1), dict(scale_group=24), dict(scale_group=256),
+                                dict(head_dim=40, rope_theta=1e4)])
+def test_unsupported_configs(kw):
+    base = dict(head_dim=128, bits_k=2, bits_v=2, scale_group=0, parity=1, in_dtype=0,
+                rope_theta=0.0)
+    base.update(kw)
+    c = nq.Config(**base)
+    assert nq.packed_bytes(c, 0, 1, 0) == 0
+    cc = c.c()
+    pk = nq._Packed(0x1000, 0x2000, 0x3000)
+    st = nq.load().nq_quantize_kv(ctypes.byref(cc), 0x10000, None, 1, 1, 4, None,
+                                  ctypes.byref(pk), None, None, 0, None)
+    assert st == nq.NQ_ERR_UNSUPPORTED
+
+
+def test_invalid_arguments_rejected_before_launch():
+    lib = nq.load()
+    c = nq.Config(128, 2, 2, 0, nq.PARITY_RELAXED, nq.DTYPE_F16, 5e5).c()
+    pk = nq._Packed(0x1000, 0x2000, 0x3000)
+    bad = nq._Packed(0x1008, 0x2000, 0x3000)
+    q = lambda *a: lib.nq_quantize_kv(*a)  # noqa: E731
+    # null config, no tensors, bad shape, misaligned input / plane / positions
+    assert q(None, 0x10000, None, 1, 1, 4, None, ctypes.byref(pk), None, None, 0, None) == -1
+    assert q(ctypes.byref(c), None, None, 1, 1, 4, None, None, None, None, 0, None) == -1
+    assert q(ctypes.byref(c), 0x10000, None, 0, 1, 4, None, ctypes.byref(pk), None, None, 0, None) == -1
+    assert q(ctypes.byref(c), 0x10004, None, 1, 1, 4, None, ctypes.byref(pk), None, None, 0, None) == -1
+    assert q(ctypes.byref(c), 0x10000, None, 1, 1, 4, None, ctypes.byref(bad), None, None, 0, None) == -1
+    assert q(ctypes.byref(c), 0x10000, None, 1, 1, 4, 0x5004, ctypes.byref(pk), None, None, 0, None) == -1
+    assert q(ctypes.byref(c), 0x10000, None, 1, 1, 4, None, None, None, None, 0, None) == -1
+    # keys with RoPE need the workspace table
+    assert q(ctypes.byref(c), 0x10000, None, 1, 1, 4, None, ctypes.byref(pk), None, None, 0, None) == -3
+    assert q(ctypes.byref(c), 0x10000, None, 1, 1, 4, None, ctypes.byref(pk), None, 0x8000, 128, None) == -3
+    dq = lib.nq_dequantize_kv
+    assert dq(ctypes.byref(c), ctypes.byref(pk), None, 1, 1, 4, None, None, None, None, 0, None) == -1
+    assert dq(ctypes.byref(c), ctypes.byref(pk), None, 1, 1, 4, None, 0x10000, None, None, 0, None) == -3
+    sc = lib.nq_score_packed_keys
+    assert sc(ctypes.byref(c), ctypes.byref(pk), 1, 3, 4, 8, 0x10000, 0x20000, None, 0, None) == -1
+    assert sc(ctypes.byref(c), ctypes.byref(pk), 1, 2, 4, 8, 0x10000, 0x20008, None, 0, None) == -1
+    dd = lib.nq_e8_decode_debug
+    assert dd(0x1000, 10, 4, 0, 0x2000, 0x3000, None) == -2
+    assert dd(0x1000, 0, 2, 0, 0x2000, 0x3000, None) == -1
+    assert dd(0x1000, 10, 2, 5, 0x2000, 0x3000, None) == -1
+    for s in (0, -1, -2, -3, -4, 9):
+        assert isinstance(nq.status_string(s), str)
