@@ -236,6 +236,311 @@ __device__ __forceinline__ void e8_decode(const float y[8], uint32_t& code,
   coset = c;
 }
 
+// ---------------------------------------------------------------------------
+// Fast path for n <= 128 (one 16-lane DPP row or less per vector).
+//
+// Lane relabelling: the cross-lane butterfly stages pair lanes l and l ^ a_k
+// with a = (1, 2, 7, 15), which are the DPP patterns quad_perm [1,0,3,2],
+// quad_perm [2,3,0,1], row_half_mirror and row_mirror.  Lane l of a row holds
+// 8-group m(l) = A^-1 l, A = [a_0 a_1 a_2 a_3] over GF(2); then the stage-k
+// pair (l, l ^ a_k) is exactly the group pair (m, m ^ 2^k), i.e. the stride
+// 8 * 2^k butterfly of the textbook transform, in the textbook order.
+//
+// Sign twist: lane l keeps w = sigma_l * u.  Every lane then computes
+// w + coef_k * w_partner with one v_fmac_f32_dpp (coef_k = -1 where bit k of m
+// is set, else +1); the sum is rounded once, exactly like a + b or a - b, and
+// sigma_l = (-1)^popcount(m) is folded into the scale at the end.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lane_group(int l) {
+  return l ^ (((l >> 2) & 1) * 3) ^ (((l >> 3) & 1) * 4);
+}
+__device__ __forceinline__ int group_lane(int m) {
+  return (m & 1) ^ (m & 2) ^ (((m >> 2) & 1) * 7) ^ (((m >> 3) & 1) * 15);
+}
+
+#define NQ_FMAC8(CTRL, v, c)                                            \
+  asm volatile("s_nop 1\n\t"                                             \
+               "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf"  \
+               : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), \
+                 "+v"(v[5]), "+v"(v[6]), "+v"(v[7])                       \
+               : "v"(c))
+
+// x * c + partner(x) * s for 8 values: the partner read goes through DPP.
+#define NQ_MULDPP8(CTRL, out, v, s)                                      \
+  asm volatile("s_nop 1\n\t"                                             \
+               "v_mul_f32_dpp %0, %8, %16 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_mul_f32_dpp %1, %9, %17 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_mul_f32_dpp %2, %10, %18 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_mul_f32_dpp %3, %11, %19 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_mul_f32_dpp %4, %12, %20 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_mul_f32_dpp %5, %13, %21 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_mul_f32_dpp %6, %14, %22 " CTRL " row_mask:0xf bank_mask:0xf\n\t" \
+               "v_mul_f32_dpp %7, %15, %23 " CTRL " row_mask:0xf bank_mask:0xf"  \
+               : "=&v"(out[0]), "=&v"(out[1]), "=&v"(out[2]), "=&v"(out[3]), \
+                 "=&v"(out[4]), "=&v"(out[5]), "=&v"(out[6]), "=&v"(out[7]) \
+               : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]),   \
+                 "v"(v[5]), "v"(v[6]), "v"(v[7]), "v"(s[0]), "v"(s[1]),  \
+                 "v"(s[2]), "v"(s[3]), "v"(s[4]), "v"(s[5]), "v"(s[6]),   \
+                 "v"(s[7]))
+
+#define NQ_DPP_A0 "quad_perm:[1,0,3,2]"
+#define NQ_DPP_A1 "quad_perm:[2,3,0,1]"
+#define NQ_DPP_A2 "row_half_mirror"
+#define NQ_DPP_A3 "row_mirror"
+
+template <int K>
+__device__ __forceinline__ void stage_fmac(float v[8], float c) {
+  if (K == 0) NQ_FMAC8(NQ_DPP_A0, v, c);
+  if (K == 1) NQ_FMAC8(NQ_DPP_A1, v, c);
+  if (K == 2) NQ_FMAC8(NQ_DPP_A2, v, c);
+  if (K == 3) NQ_FMAC8(NQ_DPP_A3, v, c);
+}
+
+template <int K>
+__device__ __forceinline__ void partner_mul(float out[8], const float v[8],
+                                            const float s[8]) {
+  if (K == 0) NQ_MULDPP8(NQ_DPP_A0, out, v, s);
+  if (K == 1) NQ_MULDPP8(NQ_DPP_A1, out, v, s);
+  if (K == 2) NQ_MULDPP8(NQ_DPP_A2, out, v, s);
+  if (K == 3) NQ_MULDPP8(NQ_DPP_A3, out, v, s);
+}
+
+template <int K>
+__device__ __forceinline__ float dpp_a(float x) {
+  constexpr int ctrl = K == 0 ? 0xB1 : K == 1 ? 0x4E : K == 2 ? 0x141 : 0x140;
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), ctrl, 0xF, 0xF, true));
+}
+template <int K>
+__device__ __forceinline__ uint32_t dpp_a_u(uint32_t x) {
+  constexpr int ctrl = K == 0 ? 0xB1 : K == 1 ? 0x4E : K == 2 ? 0x141 : 0x140;
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, ctrl, 0xF, 0xF, true);
+}
+
+// Max over the lanes of one scale group (gl = G/8 lanes, a subspace spanned
+// by a_0 .. a_{log2 gl - 1}).
+template <int VL>
+__device__ __forceinline__ float group_max(float x, int gl) {
+  if (VL > 1 && gl > 1) x = fmaxf(x, dpp_a<0>(x));
+  if (VL > 2 && gl > 2) x = fmaxf(x, dpp_a<1>(x));
+  if (VL > 4 && gl > 4) x = fmaxf(x, dpp_a<2>(x));
+  if (VL > 8 && gl > 8) x = fmaxf(x, dpp_a<3>(x));
+  return x;
+}
+template <int VL>
+__device__ __forceinline__ uint32_t row_or(uint32_t x) {
+  if (VL > 1) x |= dpp_a_u<0>(x);
+  if (VL > 2) x |= dpp_a_u<1>(x);
+  if (VL > 4) x |= dpp_a_u<2>(x);
+  if (VL > 8) x |= dpp_a_u<3>(x);
+  return x;
+}
+
+// Spread the low 8 bits of x (and of y) to the even bits of 16; returns the
+// 2-bit fields (x_k | y_k << 1) at bits 2k.
+__device__ __forceinline__ uint32_t interleave8(uint32_t x, uint32_t y) {
+  uint32_t z = (x & 0xffu) | ((y & 0xffu) << 16);
+  z = (z | (z << 4)) & 0x0f0f0f0fu;
+  z = (z | (z << 2)) & 0x33333333u;
+  z = (z | (z << 1)) & 0x55555555u;
+  return (z & 0xffffu) | ((z >> 16) << 1);
+}
+
+// 2-bit decoder (L = 4) on g = 2y.  With a = |g| and t = a - 1:
+//  integer coset: p = 0 if a < 1 else sign(g) (bit B = a >= 1);
+//  half coset:    |p| = 1/2 if a < 2 else 3/2 (bit E = a >= 2), sign S;
+//  D1 - D0 = sum_k [2|t_k| - 1 + min(0, 8 - 4 a_k)]  (doubled units);
+//  integer-coset parity step: the coordinate with the smallest |t| toggles
+//  B, extra cost 4 |t|;  strict half-coset step: kappa = |t| (a < 2) or
+//  3 - a (a >= 2), extra cost 4 - 4 kappa, toggles E (a >= 1) or S (a < 1).
+// Coordinates are scanned from 7 down to 0 so that the lowest index wins ties
+// and bit k of each mask belongs to coordinate k.
+template <bool STRICT>
+__device__ __forceinline__ void e8_decode2(const float g[8], uint32_t& code,
+                                           int& coset) {
+  uint32_t Bm = 0, Em = 0, Sm = 0, f0 = 0, f1 = 0;
+  float acc = 0.f, best0 = INFINITY, best1 = -INFINITY;
+#pragma unroll
+  for (int k = 7; k >= 0; --k) {
+    const float a = fabsf(g[k]);
+    const float t = a - 1.0f;
+    const float at = fabsf(t);
+    Bm = 2u * Bm + (t >= 0.f ? 1u : 0u);
+    Em = 2u * Em + (a >= 2.f ? 1u : 0u);
+    Sm = 2u * Sm + (signbit(g[k]) ? 1u : 0u);
+    acc = __fmaf_rn(2.f, at, acc);
+    acc = acc + fminf(__fmaf_rn(-4.f, a, 8.f), 0.f);
+    if (at <= best0) { best0 = at; f0 = 1u << k; }
+    if (STRICT) {
+      const float k1 = (a >= 2.f) ? 3.0f - a : at;
+      if (k1 >= best1) { best1 = k1; f1 = 1u << k; }
+    }
+  }
+  const uint32_t odd0 = __builtin_popcount(Bm) & 1u;
+  float lhs = acc - 8.f;
+  uint32_t odd1 = 0;
+  if (STRICT) {
+    odd1 = __builtin_popcount(Em ^ Sm) & 1u;
+    if (odd1) lhs = lhs + __fmaf_rn(-4.f, best1, 4.f);
+  }
+  const float rhs = odd0 ? 4.f * best0 : 0.f;
+  const int c = lhs < rhs ? 1 : 0;
+  uint32_t x0, x1;
+  if (c == 0) {
+    const uint32_t b = Bm ^ (odd0 ? f0 : 0u);
+    x0 = b;
+    x1 = ~(b & Sm);
+  } else {
+    uint32_t e = Em, s = Sm;
+    if (STRICT && odd1) {
+      e ^= f1 & Bm;
+      s ^= f1 & ~Bm;
+    }
+    x0 = e ^ s;
+    x1 = ~s;
+  }
+  code = interleave8(x0, x1);
+  coset = c;
+}
+
+// ROPE: 0 none, 1 partner through DPP (d == n >= 16), 2 partner through
+// ds_bpermute (other d, a multiple of 16), 3 partner inside the lane (d == 8).
+template <int N, int BITS, bool STRICT, typename InT, int ROPE>
+__global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
+                                                               int sh_chunk) {
+  constexpr int VL = N / 8;
+  constexpr int TPW = 64 / VL;  // tokens per wave iteration
+  const int lane = threadIdx.x & 63;
+  const int row = lane / VL;
+  const int l = lane % VL;
+  const int m = lane_group(l);
+  const int64_t n_tt = (a.T + TPW - 1) / TPW;
+  const int64_t SH = a.n_vec / a.T;
+  const int64_t wave = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  const int64_t tt = wave % n_tt;
+  const int64_t sh0 = (wave / n_tt) * sh_chunk;
+  if (sh0 >= SH) return;
+  const int64_t sh1 = min(SH, sh0 + sh_chunk);
+  const int64_t t = tt * TPW + row;
+  const bool tvalid = t < a.T;
+  const int64_t tc = tvalid ? t : a.T - 1;
+  const int j0 = 8 * m;
+  const bool data_lane = j0 < a.d;
+  const int h = a.d >> 1;
+  const int gl = a.G >> 3;
+
+  // RoPE table slice for this lane's token and coordinates, kept in registers
+  float rc[8], rs[8];
+  int pl = 0;
+  if (ROPE != 0) {
+    const float2* row_p = a.rope + tc * h;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int j = j0 + k;
+      const bool up = j >= h;
+      const float2 cs = data_lane ? row_p[up ? j - h : j] : make_float2(0.f, 0.f);
+      rc[k] = cs.x;
+      rs[k] = up ? -cs.y : cs.y;
+    }
+    if (ROPE == 2) {
+      const int hl = h >> 3;
+      const int pm = (m < hl) ? m + hl : (m < 2 * hl ? m - hl : m);
+      pl = (lane - l) + group_lane(pm);
+    }
+  }
+  // per-lane butterfly coefficients and final sign
+  float coef[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) coef[k] = ((m >> k) & 1) ? -1.f : 1.f;
+  const bool neg_sigma = (__builtin_popcount(m) & 1) != 0;
+  const uint32_t my_cbit = 1u << m;
+  const bool scale_lane = (m % gl) == 0;
+
+  for (int64_t sh = sh0; sh < sh1; ++sh) {
+    const int64_t vec = sh * a.T + tc;
+    float v[8];
+    if (data_lane) {
+      Io<InT>::load8(a.x, vec * a.d + j0, v);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = 0.f;
+    }
+    if (ROPE == 1) {
+      float pv[8];
+      constexpr int KR = N == 128 ? 3 : N == 64 ? 2 : N == 32 ? 1 : 0;
+      partner_mul<KR>(pv, v, rs);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = __fadd_rn(__fmul_rn(v[k], rc[k]), pv[k]);
+    } else if (ROPE == 2) {
+      float pv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) pv[k] = __shfl(v[k], pl);
+      if (data_lane) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          v[k] = __fadd_rn(__fmul_rn(v[k], rc[k]), __fmul_rn(pv[k], rs[k]));
+      }
+    } else if (ROPE == 3) {
+      float x[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = v[k];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        v[k] = __fadd_rn(__fmul_rn(x[k], rc[k]), __fmul_rn(x[k ^ 4], rs[k]));
+    }
+    fwht_lane(v);
+    if (VL > 1) stage_fmac<0>(v, coef[0]);
+    if (VL > 2) stage_fmac<1>(v, coef[1]);
+    if (VL > 4) stage_fmac<2>(v, coef[2]);
+    if (VL > 8) stage_fmac<3>(v, coef[3]);
+    float mx = fmaxf(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))),
+                     fmaxf(fmaxf(fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7]))));
+    mx = group_max<VL>(mx, gl);
+    const float amax = fmaxf(mx, a.eps);
+    const float r = __fdiv_rn(a.half_L, amax);
+    const float rsig = neg_sigma ? -r : r;
+    uint32_t code;
+    int c;
+    if (BITS == 2) {
+      float g[8];
+      const float r2 = rsig + rsig;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) g[k] = __fmul_rn(v[k], r2);
+      e8_decode2<STRICT>(g, code, c);
+    } else {
+      float y[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) y[k] = __fmul_rn(v[k], rsig);
+      e8_decode<BITS, STRICT>(y, code, c);
+    }
+    const uint32_t cw = row_or<VL>(c ? my_cbit : 0u);
+    if (tvalid) {
+      uint8_t* cp = a.codes + vec * a.code_bytes + m * BITS;
+      if (BITS == 2) {
+        *reinterpret_cast<uint16_t*>(cp) = (uint16_t)code;
+      } else {
+        cp[0] = (uint8_t)(code & 0xffu);
+        cp[1] = (uint8_t)((code >> 8) & 0xffu);
+        cp[2] = (uint8_t)(code >> 16);
+      }
+      if (m == 0) {
+        uint8_t* q = a.cosets + vec * a.coset_bytes;
+        if (VL > 8) *reinterpret_cast<uint16_t*>(q) = (uint16_t)cw;
+        else q[0] = (uint8_t)cw;
+      }
+      if (scale_lane)
+        a.scales[vec * a.n_scales + m / gl] = f64_to_f16_rn((double)amax * a.sigma_k);
+    }
+  }
+}
+
 template <int N, int BITS, bool STRICT, typename InT>
 __global__ __launch_bounds__(kBlock) void quantize_kernel(TensorArgs a) {
   constexpr int VL = N / 8;
@@ -432,8 +737,33 @@ __global__ __launch_bounds__(kBlock) void rope_table_kernel(
   table[i] = make_float2((float)cs, (float)sn);
 }
 
+template <int N, int BITS, bool STRICT, typename T, int ROPE>
+hipError_t quantize_fast_launch(const TensorArgs& a, hipStream_t s) {
+  constexpr int TPW = 64 / (N / 8);
+  const int64_t SH = a.n_vec / a.T;
+  const int chunk = (int)(SH < 16 ? SH : 16);
+  const int64_t n_tt = (a.T + TPW - 1) / TPW;
+  const int64_t waves = n_tt * ((SH + chunk - 1) / chunk);
+  const int64_t blocks = (waves + kBlock / 64 - 1) / (kBlock / 64);
+  hipLaunchKernelGGL((quantize_fast_kernel<N, BITS, STRICT, T, ROPE>),
+                     dim3((unsigned)blocks), dim3(kBlock), 0, s, a, chunk);
+  return hipGetLastError();
+}
+
+template <int N, int BITS, bool STRICT, typename T>
+hipError_t quantize_fast_rope(const TensorArgs& a, hipStream_t s) {
+  if (a.rope == nullptr) return quantize_fast_launch<N, BITS, STRICT, T, 0>(a, s);
+  if (a.d == 8) return quantize_fast_launch<N, BITS, STRICT, T, 3>(a, s);
+  if (N >= 16 && a.d == N) return quantize_fast_launch<N, BITS, STRICT, T, 1>(a, s);
+  return quantize_fast_launch<N, BITS, STRICT, T, 2>(a, s);
+}
+
 template <int N, int BITS, typename T>
 hipError_t quantize_n(const TensorArgs& a, hipStream_t s) {
+  if constexpr (N <= 128) {
+    return a.strict ? quantize_fast_rope<N, BITS, true, T>(a, s)
+                    : quantize_fast_rope<N, BITS, false, T>(a, s);
+  }
   constexpr int VPB = kBlock / (N / 8);
   const int64_t blocks = (a.n_vec + VPB - 1) / VPB;
   if (a.strict)
