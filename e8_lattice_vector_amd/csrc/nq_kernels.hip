@@ -598,6 +598,142 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(TensorArgs a) {
   }
 }
 
+template <typename T>
+struct OutIo;
+template <>
+struct OutIo<__half> {
+  // fp16 RNE, two values per v_cvt_pk_f16_f32; `flip` xors the sign bits
+  static __device__ __forceinline__ void store8(void* base, int64_t off,
+                                                const float v[8], uint32_t flip) {
+    uint32_t u[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      u[i] = __builtin_bit_cast(uint32_t, __floats2half2_rn(v[2 * i], v[2 * i + 1])) ^ flip;
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off) =
+        make_uint4(u[0], u[1], u[2], u[3]);
+  }
+  static constexpr uint32_t kFlip = 0x80008000u;
+};
+template <>
+struct OutIo<float> {
+  static __device__ __forceinline__ void store8(void* base, int64_t off,
+                                                const float v[8], uint32_t flip) {
+    float w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      w[i] = __uint_as_float(__float_as_uint(v[i]) ^ flip);
+    Io<float>::store8(base, off, w);
+  }
+  static constexpr uint32_t kFlip = 0x80000000u;
+};
+
+// Inverse path with the quantize kernel's wave layout: lane l holds 8-group
+// m(l); z = s16 / sqrt(n) * (idx - L/2 + c/2) goes through the same
+// sign-twisted DPP butterflies, so lane l ends with sigma_l * x^; sigma_l is
+// removed by flipping sign bits at the store.  Keys then get RoPE forward:
+// x_i = y_i c - y_{i+h} s, x_{i+h} = y_{i+h} c + y_i s.
+template <int N, int BITS, typename OutT, int ROPE>
+__global__ __launch_bounds__(kBlock) void dequantize_fast_kernel(TensorArgs a,
+                                                                 int sh_chunk) {
+  constexpr int VL = N / 8;
+  constexpr int TPW = 64 / VL;
+  constexpr int L = 1 << BITS;
+  const int lane = threadIdx.x & 63;
+  const int row = lane / VL;
+  const int l = lane % VL;
+  const int m = lane_group(l);
+  const int64_t n_tt = (a.T + TPW - 1) / TPW;
+  const int64_t SH = a.n_vec / a.T;
+  const int64_t wave = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
+  const int64_t tt = wave % n_tt;
+  const int64_t sh0 = (wave / n_tt) * sh_chunk;
+  if (sh0 >= SH) return;
+  const int64_t sh1 = min(SH, sh0 + sh_chunk);
+  const int64_t t = tt * TPW + row;
+  const bool tvalid = t < a.T;
+  const int64_t tc = tvalid ? t : a.T - 1;
+  const int j0 = 8 * m;
+  const bool data_lane = j0 < a.d;
+  const int h = a.d >> 1;
+  const int gl = a.G >> 3;
+  const bool neg_sigma = (__builtin_popcount(m) & 1) != 0;
+  float coef[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) coef[k] = ((m >> k) & 1) ? -1.f : 1.f;
+
+  // RoPE forward, in the twisted frame: lane value w = sigma y, so
+  // sigma x = w c + w_partner * (sigma sigma_partner) * s_fwd; for the DPP
+  // partner sigma sigma_partner = -1.
+  float rc[8], rs[8];
+  int pl = 0;
+  bool pneg = false;
+  if (ROPE != 0) {
+    const float2* row_p = a.rope + tc * h;
+    int pm = m;
+    if (ROPE == 2) {
+      const int hl = h >> 3;
+      pm = (m < hl) ? m + hl : (m < 2 * hl ? m - hl : m);
+      pl = (lane - l) + group_lane(pm);
+      pneg = ((__builtin_popcount(m) ^ __builtin_popcount(pm)) & 1) != 0;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int j = j0 + k;
+      const bool up = j >= h;
+      const float2 cs = data_lane ? row_p[up ? j - h : j] : make_float2(0.f, 0.f);
+      const float sf = up ? cs.y : -cs.y;        // forward sign
+      rc[k] = cs.x;
+      rs[k] = (ROPE == 1) ? -sf : (ROPE == 2 ? (pneg ? -sf : sf) : sf);
+    }
+  }
+  const uint32_t flip = neg_sigma ? OutIo<OutT>::kFlip : 0u;
+
+  for (int64_t sh = sh0; sh < sh1; ++sh) {
+    const int64_t vec = sh * a.T + tc;
+    const uint8_t* cp = a.codes + vec * a.code_bytes + m * BITS;
+    uint32_t code;
+    if (BITS == 2) {
+      code = *reinterpret_cast<const uint16_t*>(cp);
+    } else {
+      code = (uint32_t)cp[0] | ((uint32_t)cp[1] << 8) | ((uint32_t)cp[2] << 16);
+    }
+    const int c = (a.cosets[vec * a.coset_bytes + (m >> 3)] >> (m & 7)) & 1;
+    const float sc = h2f(a.scales[vec * a.n_scales + m / gl]) * a.inv_sqrt_n;
+    const float off = (0.5f * (float)c - a.half_L) * sc;
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t idx = (code >> (BITS * k)) & (uint32_t)(L - 1);
+      v[k] = __fmaf_rn((float)idx, sc, off);
+    }
+    fwht_lane(v);
+    if (VL > 1) stage_fmac<0>(v, coef[0]);
+    if (VL > 2) stage_fmac<1>(v, coef[1]);
+    if (VL > 4) stage_fmac<2>(v, coef[2]);
+    if (VL > 8) stage_fmac<3>(v, coef[3]);
+    if (ROPE == 1) {
+      float pv[8];
+      constexpr int KR = N == 128 ? 3 : N == 64 ? 2 : N == 32 ? 1 : 0;
+      partner_mul<KR>(pv, v, rs);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = __fmaf_rn(v[k], rc[k], pv[k]);
+    } else if (ROPE == 2) {
+      float pv[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) pv[k] = __shfl(v[k], pl);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = __fmaf_rn(v[k], rc[k], pv[k] * rs[k]);
+    } else if (ROPE == 3) {
+      float x[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = v[k];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = __fmaf_rn(x[k], rc[k], x[k ^ 4] * rs[k]);
+    }
+    if (tvalid && data_lane) OutIo<OutT>::store8(a.y, vec * a.d + j0, v, flip);
+  }
+}
+
 template <int N, int BITS, typename OutT>
 __global__ __launch_bounds__(kBlock) void dequantize_kernel(TensorArgs a) {
   constexpr int VL = N / 8;
@@ -707,6 +843,161 @@ __global__ __launch_bounds__(kBlock) void score_kernel(ScoreArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Table-based asymmetric scoring (Nedelkoski et al., Abstract and Table 3:
+// q.k from packed keys without dequantizing them).
+//
+// With q~ = H pad(q) (unnormalised) and p = idx - L/2 + c/2,
+//   q . D0(k) = (1/sqrt n) sum_g s_g sum_{j in g} q~_j p_j .
+// The code index is linear in the packed bits (idx_j = sum_b bit * 2^b), so
+// every code byte contributes sum_{bits i} (bit_i - 1/2) w_i with
+// w_i = q~_{j(i)} 2^{b(i)}: one 256-entry table per code byte covers 2- and
+// 3-bit codes alike.  Each coset byte adds sum_i Q_{m(i)} (bit_i - 1) / 2 with
+// Q_m the sum of q~ over 8-group m; the centring constant sum_j q~_j (L-1)/2 -
+// sum_m Q_m L/2 + sum_m Q_m / 2 cancels exactly.  Tables hold HPP query heads
+// side by side so one LDS vector read serves all of them.
+// ---------------------------------------------------------------------------
+constexpr int kLutBlock = 512;
+
+template <int HPP>
+struct LutVec;
+template <> struct LutVec<1> { using T = float; };
+template <> struct LutVec<2> { using T = float2; };
+template <> struct LutVec<3> { using T = float3; };
+template <> struct LutVec<4> { using T = float4; };
+
+__device__ __forceinline__ void lut_add(float* acc, float v) { acc[0] += v; }
+__device__ __forceinline__ void lut_add(float* acc, float2 v) { acc[0] += v.x; acc[1] += v.y; }
+__device__ __forceinline__ void lut_add(float* acc, float3 v) {
+  acc[0] += v.x; acc[1] += v.y; acc[2] += v.z;
+}
+__device__ __forceinline__ void lut_add(float* acc, float4 v) {
+  acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
+}
+
+template <int BITS, int N, int HPP, typename QT>
+__global__ __launch_bounds__(kLutBlock) void score_lut_kernel(ScoreArgs a,
+                                                              int n_pass,
+                                                              int64_t chunk) {
+  constexpr int CB = N * BITS / 8;        // code bytes per key
+  constexpr int NG = N / 8;               // 8-groups per key
+  constexpr int CSB = (NG + 7) / 8;       // coset bytes per key
+  constexpr int NT = CB + CSB;            // tables
+  using V = typename LutVec<HPP>::T;
+  extern __shared__ float lds[];
+  float* lut = lds;                       // [NT][256][HPP]
+  float* qt = lds + NT * 256 * HPP;       // [HPP][N] rotated queries
+  float* qm = qt + HPP * N;               // [HPP][NG] group sums
+  const int64_t s = blockIdx.z;
+  const int h = blockIdx.y / n_pass;
+  const int pass = blockIdx.y % n_pass;
+  const int grp = a.Hq / a.H;
+  const int hq0 = h * grp + pass * HPP;
+  const int nh = min(HPP, h * grp + grp - hq0);  // heads in this pass
+
+  // rotated queries q~ = H pad(q) (in LDS), then group sums
+  for (int i = threadIdx.x; i < HPP * N; i += blockDim.x) {
+    const int hh = i / N, j = i % N;
+    qt[i] = (hh < nh && j < a.d)
+                ? Io<QT>::load1(a.q, (s * a.Hq + hq0 + hh) * (int64_t)a.d + j)
+                : 0.f;
+  }
+  __syncthreads();
+  for (int hs = 1; hs < N; hs <<= 1) {
+    for (int i = threadIdx.x; i < HPP * (N / 2); i += blockDim.x) {
+      const int hh = i / (N / 2), r = i % (N / 2);
+      const int j = (r / hs) * 2 * hs + (r % hs);
+      const float x0 = qt[hh * N + j], x1 = qt[hh * N + j + hs];
+      qt[hh * N + j] = x0 + x1;
+      qt[hh * N + j + hs] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < HPP * NG; i += blockDim.x) {
+    const int hh = i / NG, mm = i % NG;
+    float sum = 0.f;
+    for (int k = 0; k < 8; ++k) sum += qt[hh * N + 8 * mm + k];
+    qm[i] = sum;
+  }
+  __syncthreads();
+  // tables
+  for (int e = threadIdx.x; e < NT * 256 * HPP; e += blockDim.x) {
+    const int hh = e % HPP;
+    const int v = (e / HPP) & 255;
+    const int tb = e / (HPP * 256);
+    float acc = 0.f;
+    if (tb < CB) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int bit = 8 * tb + i;           // position in the key's bit stream
+        const float w = qt[hh * N + bit / BITS] * (float)(1 << (bit % BITS));
+        acc += (((v >> i) & 1) ? 0.5f : -0.5f) * w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int mm = 8 * (tb - CB) + i;
+        if (mm < NG && !((v >> i) & 1)) acc -= 0.5f * qm[hh * NG + mm];
+      }
+    }
+    lut[e] = acc;
+  }
+  __syncthreads();
+
+  const int gl = a.G >> 3;                 // 8-groups per scale group
+  const int ns = NG / gl;                  // scale groups per key
+  const int64_t t0 = (int64_t)blockIdx.x * chunk;
+  const int64_t t1 = min(a.T, t0 + chunk);
+  const int64_t base = (s * a.H + h) * a.T;
+  for (int64_t t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
+    const int64_t vec = base + t;
+    uint32_t cw[CB / 4 + 1];
+    const uint8_t* cp = a.codes + vec * CB;
+    if (CB % 16 == 0) {
+#pragma unroll
+      for (int i = 0; i < CB / 16; ++i) {
+        const uint4 w = reinterpret_cast<const uint4*>(cp)[i];
+        cw[4 * i] = w.x; cw[4 * i + 1] = w.y; cw[4 * i + 2] = w.z; cw[4 * i + 3] = w.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < CB / 4; ++i) cw[i] = reinterpret_cast<const uint32_t*>(cp)[i];
+    }
+    uint32_t cs = 0;
+    const uint8_t* csp = a.cosets + vec * CSB;
+#pragma unroll
+    for (int i = 0; i < CSB; ++i) cs |= (uint32_t)csp[i] << (8 * i);
+    float score[HPP];
+#pragma unroll
+    for (int hh = 0; hh < HPP; ++hh) score[hh] = 0.f;
+    for (int g = 0; g < ns; ++g) {
+      float acc[HPP];
+#pragma unroll
+      for (int hh = 0; hh < HPP; ++hh) acc[hh] = 0.f;
+      const int b0 = g * gl * BITS, b1 = b0 + gl * BITS;   // code bytes of group
+#pragma unroll
+      for (int b = 0; b < CB; ++b) {
+        if (b < b0 || b >= b1) continue;
+        const uint32_t v = (cw[b >> 2] >> (8 * (b & 3))) & 0xffu;
+        lut_add(acc, reinterpret_cast<const V*>(lut)[b * 256 + v]);
+      }
+      const int k0 = (g * gl) >> 3, k1 = ((g + 1) * gl + 7) >> 3;
+#pragma unroll
+      for (int k = 0; k < CSB; ++k) {
+        if (k < k0 || k >= k1) continue;
+        const uint32_t v = (cs >> (8 * k)) & 0xffu;
+        lut_add(acc, reinterpret_cast<const V*>(lut)[(CB + k) * 256 + v]);
+      }
+      const float sc = h2f(a.scales[vec * a.n_scales + g]);
+#pragma unroll
+      for (int hh = 0; hh < HPP; ++hh) score[hh] = fmaf(acc[hh], sc, score[hh]);
+    }
+#pragma unroll
+    for (int hh = 0; hh < HPP; ++hh)
+      if (hh < nh) a.out[(s * a.Hq + hq0 + hh) * a.T + t] = score[hh] * a.inv_sqrt_n;
+  }
+}
+
 template <int BITS, bool STRICT>
 __global__ __launch_bounds__(kBlock) void decode_debug_kernel(
     const float* y, int64_t n, uint8_t* idx, uint8_t* coset) {
@@ -775,8 +1066,27 @@ hipError_t quantize_n(const TensorArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int N, int BITS, typename T, int ROPE>
+hipError_t dequantize_fast_launch(const TensorArgs& a, hipStream_t s) {
+  constexpr int TPW = 64 / (N / 8);
+  const int64_t SH = a.n_vec / a.T;
+  const int chunk = (int)(SH < 16 ? SH : 16);
+  const int64_t n_tt = (a.T + TPW - 1) / TPW;
+  const int64_t waves = n_tt * ((SH + chunk - 1) / chunk);
+  const int64_t blocks = (waves + kBlock / 64 - 1) / (kBlock / 64);
+  hipLaunchKernelGGL((dequantize_fast_kernel<N, BITS, T, ROPE>), dim3((unsigned)blocks),
+                     dim3(kBlock), 0, s, a, chunk);
+  return hipGetLastError();
+}
+
 template <int N, int BITS, typename T>
 hipError_t dequantize_n(const TensorArgs& a, hipStream_t s) {
+  if constexpr (N <= 128) {
+    if (a.rope == nullptr) return dequantize_fast_launch<N, BITS, T, 0>(a, s);
+    if (a.d == 8) return dequantize_fast_launch<N, BITS, T, 3>(a, s);
+    if (N >= 16 && a.d == N) return dequantize_fast_launch<N, BITS, T, 1>(a, s);
+    return dequantize_fast_launch<N, BITS, T, 2>(a, s);
+  }
   constexpr int VPB = kBlock / (N / 8);
   const int64_t blocks = (a.n_vec + VPB - 1) / VPB;
   hipLaunchKernelGGL((dequantize_kernel<N, BITS, T>), dim3((unsigned)blocks),
@@ -784,8 +1094,55 @@ hipError_t dequantize_n(const TensorArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BITS, int N, int HPP, typename T>
+hipError_t score_lut_launch(const ScoreArgs& a, int n_pass, hipStream_t s) {
+  constexpr int CB = N * BITS / 8, NG = N / 8, CSB = (NG + 7) / 8;
+  const size_t lds = sizeof(float) * ((size_t)(CB + CSB) * 256 * HPP + HPP * N + HPP * NG);
+  auto kern = score_lut_kernel<BITS, N, HPP, T>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  // enough workgroups to cover the chip when there are few (slab, head) pairs
+  const int64_t pairs = a.S * a.H * n_pass;
+  int64_t n_chunks = (1024 + pairs - 1) / pairs;
+  const int64_t min_chunk = 4 * kLutBlock;
+  n_chunks = max((int64_t)1, min(n_chunks, (a.T + min_chunk - 1) / min_chunk));
+  const int64_t chunk = (a.T + n_chunks - 1) / n_chunks;
+  const dim3 grid((unsigned)n_chunks, (unsigned)(a.H * n_pass), (unsigned)a.S);
+  hipLaunchKernelGGL(kern, grid, dim3(kLutBlock), lds, s, a, n_pass, chunk);
+  return hipGetLastError();
+}
+
+template <int BITS, int N, typename T>
+hipError_t score_lut_n(const ScoreArgs& a, int max_lds, hipStream_t s) {
+  constexpr int CB = N * BITS / 8, NG = N / 8, CSB = (NG + 7) / 8;
+  const int grp = a.Hq / a.H;
+  const size_t per_head = sizeof(float) * ((size_t)(CB + CSB) * 256 + N + NG);
+  int hpp_max = (int)((size_t)max_lds / per_head);
+  if (hpp_max < 1) return hipErrorInvalidValue;
+  if (hpp_max > 4) hpp_max = 4;
+  const int n_pass = (grp + hpp_max - 1) / hpp_max;
+  const int hpp = (grp + n_pass - 1) / n_pass;
+  switch (hpp) {
+    case 1: return score_lut_launch<BITS, N, 1, T>(a, n_pass, s);
+    case 2: return score_lut_launch<BITS, N, 2, T>(a, n_pass, s);
+    case 3: return score_lut_launch<BITS, N, 3, T>(a, n_pass, s);
+    default: return score_lut_launch<BITS, N, 4, T>(a, n_pass, s);
+  }
+}
+
 template <int N, int BITS, typename T>
 hipError_t score_n(const ScoreArgs& a, hipStream_t s) {
+  if constexpr (N >= 64) {
+    const bool coset_bytes_align = (a.G == N) || (a.G % 64 == 0);
+    int dev = 0, max_lds = 0;
+    if (coset_bytes_align && hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock,
+                              dev) == hipSuccess &&
+        max_lds >= 32 * 1024) {
+      return score_lut_n<BITS, N, T>(a, max_lds, s);
+    }
+  }
   const dim3 grid((unsigned)((a.T + kScoreKeys - 1) / kScoreKeys), (unsigned)a.H,
                   (unsigned)a.S);
   const size_t lds = sizeof(float) * (size_t)(a.Hq / a.H) * N;

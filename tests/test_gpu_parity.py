@@ -93,6 +93,9 @@ def test_magnitude_edges(scale):
     (nq.Config(96, 2, 2, 32, S_, F16, 1e4), 3),
     (nq.Config(128, 3, 2, 64, R_, F16, 1e6), 4),
     (nq.Config(64, 2, 2, 0, R_, F32, 0.0), 12),
+    (nq.Config(256, 3, 2, 0, S_, F16, 1e4), 2),
+    (nq.Config(128, 2, 2, 64, R_, F16, 5e5), 8),
+    (nq.Config(32, 2, 2, 0, R_, F16, 0.0), 2),
 ])
 def test_score_parity(cfg, grp):
     S, H, T = 2, 2, 1500
