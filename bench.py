@@ -36,6 +36,27 @@ def parse():
     return ap.parse_args()
 
 
+def profiled_traffic(profile):
+    """HBM bytes per launch from a committed rocprofv3 summary (FETCH_SIZE and
+    WRITE_SIZE, each scaled by the copy-kernel calibration), or None when the
+    kernel source has changed since the counters were taken."""
+    import hashlib
+    import re
+
+    path = os.path.join(ROOT, "profiles", profile)
+    src = os.path.join(ROOT, "e8_lattice_vector_amd", "csrc", "nq_kernels.hip")
+    try:
+        text = open(path).read()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    m_sha = re.search(r"nq_kernels.hip sha256: ([0-9a-f]{64})", text)
+    m_tr = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    if not m_sha or not m_tr or m_sha.group(1) != sha:
+        return None
+    return int(m_tr.group(1))
+
+
 def cpu_baseline(w, tokens):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np  # noqa: F401
@@ -192,7 +213,8 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": q_gbps / HBM_PEAK_GBPS,
-            "traffic": None,
+            "traffic": profiled_traffic("quantize_fast_kernel-llama-3.1-8b-32k.md"),
+            "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
             "kernel": "quantize_kernel (K launch incl. RoPE-table build, and V launch)",
             "avg_launch_ms": tq / 2,
         },
