@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "nq_internal.h"
 
 namespace nq {
@@ -77,6 +79,18 @@ struct Io<__half> {
   static __device__ __forceinline__ float load1(const void* base, int64_t off) {
     return h2f(static_cast<const uint16_t*>(base)[off]);
   }
+  using Raw = uint4;
+  static __device__ __forceinline__ Raw load_raw(const void* base, int64_t off) {
+    return *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + off);
+  }
+  static __device__ __forceinline__ void cvt(const Raw& w, float v[8]) {
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = h2f((uint16_t)(u[i] & 0xffffu));
+      v[2 * i + 1] = h2f((uint16_t)(u[i] >> 16));
+    }
+  }
 };
 
 template <>
@@ -98,6 +112,18 @@ struct Io<float> {
   static __device__ __forceinline__ float load1(const void* base, int64_t off) {
     return static_cast<const float*>(base)[off];
   }
+  struct Raw {
+    float4 a, b;
+  };
+  static __device__ __forceinline__ Raw load_raw(const void* base, int64_t off) {
+    const float4* p =
+        reinterpret_cast<const float4*>(static_cast<const float*>(base) + off);
+    return Raw{p[0], p[1]};
+  }
+  static __device__ __forceinline__ void cvt(const Raw& w, float v[8]) {
+    v[0] = w.a.x; v[1] = w.a.y; v[2] = w.a.z; v[3] = w.a.w;
+    v[4] = w.b.x; v[5] = w.b.y; v[6] = w.b.z; v[7] = w.b.w;
+  }
 };
 
 // Walsh-Hadamard stages 1, 2, 4 inside the lane.
@@ -112,6 +138,36 @@ __device__ __forceinline__ void fwht_lane(float v[8]) {
         v[k + h] = __fsub_rn(a, b);
       }
     }
+  }
+}
+
+// Stages 2 and 4 inside the lane (stage 1 already done).
+__device__ __forceinline__ void fwht_lane_24(float v[8]) {
+#pragma unroll
+  for (int h = 2; h < 8; h <<= 1) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      if ((k & h) == 0) {
+        const float a = v[k], b = v[k + h];
+        v[k] = __fadd_rn(a, b);
+        v[k + h] = __fsub_rn(a, b);
+      }
+    }
+  }
+}
+
+// Load 8 fp16 values and apply Walsh-Hadamard stage 1 in the same
+// instructions: v_fma_mix_f32 reads both fp16 halves of a word (exactly
+// widened) and rounds a*1 + b (or a*1 - b) once to fp32, i.e. fl(a + b).
+__device__ __forceinline__ void load8_h_stage1(const void* p, float v[8]) {
+  const uint4 w = *reinterpret_cast<const uint4*>(p);
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    asm("v_fma_mix_f32 %0, %2, 1.0, %2 op_sel:[0,0,1] op_sel_hi:[1,0,1]\n\t"
+        "v_fma_mix_f32 %1, %2, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[1,0,1]"
+        : "=&v"(v[2 * i]), "=&v"(v[2 * i + 1])
+        : "v"(u[i]));
   }
 }
 
@@ -326,12 +382,32 @@ __device__ __forceinline__ uint32_t dpp_a_u(uint32_t x) {
 
 // Max over the lanes of one scale group (gl = G/8 lanes, a subspace spanned
 // by a_0 .. a_{log2 gl - 1}).
+// max |v_k| over the lane's 8 values (v_max3_f32 with abs modifiers)
+__device__ __forceinline__ float abs_max8(const float v[8]) {
+  float m;
+  asm("v_max3_f32 %0, |%1|, |%2|, |%3|\n\t"
+      "v_max3_f32 %0, %0, |%4|, |%5|\n\t"
+      "v_max3_f32 %0, %0, |%6|, |%7|\n\t"
+      "v_max_f32_e64 %0, %0, |%8|"
+      : "=&v"(m)
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]),
+        "v"(v[6]), "v"(v[7]));
+  return m;
+}
+
+#define NQ_DPP_MAX(CTRL, x)                                                  \
+  asm volatile("s_nop 1\n\tv_max_f32_dpp %0, %0, %0 " CTRL                  \
+               " row_mask:0xf bank_mask:0xf"                                   \
+               : "+v"(x))
+
+// Max over the lanes of one scale group (gl = G/8 lanes, a subspace spanned
+// by a_0 .. a_{log2 gl - 1}).
 template <int VL>
 __device__ __forceinline__ float group_max(float x, int gl) {
-  if (VL > 1 && gl > 1) x = fmaxf(x, dpp_a<0>(x));
-  if (VL > 2 && gl > 2) x = fmaxf(x, dpp_a<1>(x));
-  if (VL > 4 && gl > 4) x = fmaxf(x, dpp_a<2>(x));
-  if (VL > 8 && gl > 8) x = fmaxf(x, dpp_a<3>(x));
+  if (VL > 1 && gl > 1) NQ_DPP_MAX(NQ_DPP_A0, x);
+  if (VL > 2 && gl > 2) NQ_DPP_MAX(NQ_DPP_A1, x);
+  if (VL > 4 && gl > 4) NQ_DPP_MAX(NQ_DPP_A2, x);
+  if (VL > 8 && gl > 8) NQ_DPP_MAX(NQ_DPP_A3, x);
   return x;
 }
 template <int VL>
@@ -343,78 +419,102 @@ __device__ __forceinline__ uint32_t row_or(uint32_t x) {
   return x;
 }
 
-// Spread the low 8 bits of x (and of y) to the even bits of 16; returns the
-// 2-bit fields (x_k | y_k << 1) at bits 2k.
-__device__ __forceinline__ uint32_t interleave8(uint32_t x, uint32_t y) {
-  uint32_t z = (x & 0xffu) | ((y & 0xffu) << 16);
-  z = (z | (z << 4)) & 0x0f0f0f0fu;
-  z = (z | (z << 2)) & 0x33333333u;
-  z = (z | (z << 1)) & 0x55555555u;
-  return (z & 0xffffu) | ((z >> 16) << 1);
+// Spread the low 8 bits of x to the even bits of a 16-bit word.
+__device__ __forceinline__ uint32_t spread8(uint32_t x) {
+  x &= 0xffu;
+  x = (x | (x << 4)) & 0x0f0fu;
+  x = (x | (x << 2)) & 0x3333u;
+  x = (x | (x << 1)) & 0x5555u;
+  return x;
+}
+
+// (x << n) | (the top n bits of w): v_alignbit_b32
+__device__ __forceinline__ uint32_t shift_in(uint32_t x, float w, int n) {
+  return __builtin_amdgcn_alignbit(x, __float_as_uint(w), (uint32_t)(32 - n));
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
+// that consecutive logical workgroups share an XCD and its L2.  The wave
+// order is then either tile-fastest (neighbouring waves stream neighbouring
+// memory and share the cache lines of the small coset / scale planes: the
+// memory-bound dequantize) or tile-major (the waves walking different
+// (slab, head) chunks of one token tile are neighbours and share its RoPE
+// rows in L2: the ALU-bound quantize, which wants many short waves).
+// gridDim.x is a multiple of 8.
+__device__ __forceinline__ int64_t xcd_wave_id() {
+  const uint32_t nb = gridDim.x;
+  const uint32_t lb = (blockIdx.x & 7u) * (nb >> 3) + (blockIdx.x >> 3);
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  return (int64_t)lb * (kBlock / 64) + w;
 }
 
 // 2-bit decoder (L = 4) on g = 2y.  With a = |g| and t = a - 1:
 //  integer coset: p = 0 if a < 1 else sign(g) (bit B = a >= 1);
 //  half coset:    |p| = 1/2 if a < 2 else 3/2 (bit E = a >= 2), sign S;
-//  D1 - D0 = sum_k [2|t_k| - 1 + min(0, 8 - 4 a_k)]  (doubled units);
+//  D1 - D0 = sum_k 2 min(|t_k|, 3 - a_k) - 8        (doubled units);
 //  integer-coset parity step: the coordinate with the smallest |t| toggles
 //  B, extra cost 4 |t|;  strict half-coset step: kappa = |t| (a < 2) or
 //  3 - a (a >= 2), extra cost 4 - 4 kappa, toggles E (a >= 1) or S (a < 1).
-// Coordinates are scanned from 7 down to 0 so that the lowest index wins ties
-// and bit k of each mask belongs to coordinate k.
+// The two top bits of g's fp32 pattern are (S, E), so shifting them in for
+// k = 7 .. 0 builds the half-coset code word with (S_k, E_k) at bits
+// (2k+1, 2k); the sign bit of t gives not-B.  Scanning k downward also makes
+// the lowest index win ties.  Code word: 2-bit idx_k = p_k + 2 - c/2 at bits
+// [2k, 2k+2): integer coset bit0 = B, bit1 = ~(B & S); half coset
+// bit0 = E ^ S, bit1 = ~S.
 template <bool STRICT>
 __device__ __forceinline__ void e8_decode2(const float g[8], uint32_t& code,
                                            int& coset) {
-  uint32_t Bm = 0, Em = 0, Sm = 0, f0 = 0, f1 = 0;
-  float acc = 0.f, best0 = INFINITY, best1 = -INFINITY;
+  uint32_t X = 0, Bn = 0, f0 = 1u << 14, f1 = 0;
+  float acc = 0.f, best0, best1 = -INFINITY;
 #pragma unroll
   for (int k = 7; k >= 0; --k) {
     const float a = fabsf(g[k]);
     const float t = a - 1.0f;
     const float at = fabsf(t);
-    Bm = 2u * Bm + (t >= 0.f ? 1u : 0u);
-    Em = 2u * Em + (a >= 2.f ? 1u : 0u);
-    Sm = 2u * Sm + (signbit(g[k]) ? 1u : 0u);
-    acc = __fmaf_rn(2.f, at, acc);
-    acc = acc + fminf(__fmaf_rn(-4.f, a, 8.f), 0.f);
-    if (at <= best0) { best0 = at; f0 = 1u << k; }
+    const float w = 3.0f - a;
+    X = shift_in(X, g[k], 2);
+    Bn = shift_in(Bn, t, 1);
+    acc = acc + fminf(at, w);
+    if (k == 7) {
+      best0 = at;
+    } else if (at <= best0) {
+      best0 = at;
+      f0 = 1u << (2 * k);
+    }
     if (STRICT) {
-      const float k1 = (a >= 2.f) ? 3.0f - a : at;
-      if (k1 >= best1) { best1 = k1; f1 = 1u << k; }
+      const float k1 = (a >= 2.f) ? w : at;
+      if (k1 >= best1) { best1 = k1; f1 = 1u << (2 * k); }
     }
   }
-  const uint32_t odd0 = __builtin_popcount(Bm) & 1u;
-  float lhs = acc - 8.f;
+  const uint32_t odd0 = __builtin_popcount(Bn) & 1u;
+  float lhs = __fmaf_rn(2.f, acc, -8.f);
   uint32_t odd1 = 0;
   if (STRICT) {
-    odd1 = __builtin_popcount(Em ^ Sm) & 1u;
+    odd1 = __builtin_popcount(X) & 1u;
     if (odd1) lhs = lhs + __fmaf_rn(-4.f, best1, 4.f);
   }
   const float rhs = odd0 ? 4.f * best0 : 0.f;
   const int c = lhs < rhs ? 1 : 0;
-  uint32_t x0, x1;
+  const uint32_t Bsp = spread8(~Bn);
+  uint32_t w;
   if (c == 0) {
-    const uint32_t b = Bm ^ (odd0 ? f0 : 0u);
-    x0 = b;
-    x1 = ~(b & Sm);
+    const uint32_t b = Bsp ^ (odd0 ? f0 : 0u);
+    w = b | (~((b << 1) & X) & 0xaaaau);
   } else {
-    uint32_t e = Em, s = Sm;
-    if (STRICT && odd1) {
-      e ^= f1 & Bm;
-      s ^= f1 & ~Bm;
-    }
-    x0 = e ^ s;
-    x1 = ~s;
+    uint32_t x = X;
+    if (STRICT && odd1) x ^= (f1 & Bsp) | ((f1 & ~Bsp) << 1);
+    w = ((x ^ (x >> 1)) & 0x5555u) | (~x & 0xaaaau);
   }
-  code = interleave8(x0, x1);
+  code = w;
   coset = c;
 }
 
 // ROPE: 0 none, 1 partner through DPP (d == n >= 16), 2 partner through
 // ds_bpermute (other d, a multiple of 16), 3 partner inside the lane (d == 8).
-template <int N, int BITS, bool STRICT, typename InT, int ROPE>
+template <int N, int BITS, bool STRICT, typename InT, int ROPE, bool PAD>
 __global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
-                                                               int sh_chunk) {
+                                                               int sh_chunk,
+                                                               int tile_major) {
   constexpr int VL = N / 8;
   constexpr int TPW = 64 / VL;  // tokens per wave iteration
   const int lane = threadIdx.x & 63;
@@ -423,10 +523,11 @@ __global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
   const int m = lane_group(l);
   const int64_t n_tt = (a.T + TPW - 1) / TPW;
   const int64_t SH = a.n_vec / a.T;
-  const int64_t wave = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
-  const int64_t tt = wave % n_tt;
-  const int64_t sh0 = (wave / n_tt) * sh_chunk;
-  if (sh0 >= SH) return;
+  const int64_t wave = xcd_wave_id();
+  const int64_t n_shc = (SH + sh_chunk - 1) / sh_chunk;
+  const int64_t tt = tile_major ? wave / n_shc : wave % n_tt;
+  const int64_t sh0 = (tile_major ? wave % n_shc : wave / n_tt) * sh_chunk;
+  if (tt >= n_tt || sh0 >= SH) return;
   const int64_t sh1 = min(SH, sh0 + sh_chunk);
   const int64_t t = tt * TPW + row;
   const bool tvalid = t < a.T;
@@ -463,11 +564,23 @@ __global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
   const uint32_t my_cbit = 1u << m;
   const bool scale_lane = (m % gl) == 0;
 
+  // per-lane byte offsets inside one (slab, head) plane (the host keeps
+  // them below 2^31); the plane bases advance uniformly with sh
+  const uint32_t off_x = (uint32_t)(tc * a.d + j0) * (uint32_t)sizeof(InT);
+  const uint32_t off_c = (uint32_t)(tc * a.code_bytes) + (uint32_t)(m * BITS);
+  const uint32_t off_s = (uint32_t)(tc * a.coset_bytes);
+  const uint32_t off_g = (uint32_t)(tc * a.n_scales) + (uint32_t)(m / gl);
+  const int64_t plane_x = a.T * a.d * (int64_t)sizeof(InT);
+  const int64_t plane_c = a.T * a.code_bytes;
+  const int64_t plane_s = a.T * a.coset_bytes;
+  const int64_t plane_g = a.T * a.n_scales;
   for (int64_t sh = sh0; sh < sh1; ++sh) {
-    const int64_t vec = sh * a.T + tc;
     float v[8];
-    if (data_lane) {
-      Io<InT>::load8(a.x, vec * a.d + j0, v);
+    const char* xb = static_cast<const char*>(a.x) + sh * plane_x;
+    constexpr bool kFuse = ROPE == 0 && std::is_same<InT, __half>::value;
+    if (!PAD || data_lane) {
+      if constexpr (kFuse) load8_h_stage1(xb + off_x, v);
+      else Io<InT>::load8(xb + off_x, 0, v);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] = 0.f;
@@ -495,13 +608,13 @@ __global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
       for (int k = 0; k < 8; ++k)
         v[k] = __fadd_rn(__fmul_rn(x[k], rc[k]), __fmul_rn(x[k ^ 4], rs[k]));
     }
-    fwht_lane(v);
+    if constexpr (kFuse) fwht_lane_24(v);
+    else fwht_lane(v);
     if (VL > 1) stage_fmac<0>(v, coef[0]);
     if (VL > 2) stage_fmac<1>(v, coef[1]);
     if (VL > 4) stage_fmac<2>(v, coef[2]);
     if (VL > 8) stage_fmac<3>(v, coef[3]);
-    float mx = fmaxf(fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))),
-                     fmaxf(fmaxf(fabsf(v[4]), fabsf(v[5])), fmaxf(fabsf(v[6]), fabsf(v[7]))));
+    float mx = abs_max8(v);
     mx = group_max<VL>(mx, gl);
     const float amax = fmaxf(mx, a.eps);
     const float r = __fdiv_rn(a.half_L, amax);
@@ -522,7 +635,7 @@ __global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
     }
     const uint32_t cw = row_or<VL>(c ? my_cbit : 0u);
     if (tvalid) {
-      uint8_t* cp = a.codes + vec * a.code_bytes + m * BITS;
+      uint8_t* cp = a.codes + sh * plane_c + off_c;
       if (BITS == 2) {
         *reinterpret_cast<uint16_t*>(cp) = (uint16_t)code;
       } else {
@@ -531,12 +644,12 @@ __global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
         cp[2] = (uint8_t)(code >> 16);
       }
       if (m == 0) {
-        uint8_t* q = a.cosets + vec * a.coset_bytes;
+        uint8_t* q = a.cosets + sh * plane_s + off_s;
         if (VL > 8) *reinterpret_cast<uint16_t*>(q) = (uint16_t)cw;
         else q[0] = (uint8_t)cw;
       }
       if (scale_lane)
-        a.scales[vec * a.n_scales + m / gl] = f64_to_f16_rn((double)amax * a.sigma_k);
+        a.scales[sh * plane_g + off_g] = f64_to_f16_rn((double)amax * a.sigma_k);
     }
   }
 }
@@ -634,7 +747,8 @@ struct OutIo<float> {
 // x_i = y_i c - y_{i+h} s, x_{i+h} = y_{i+h} c + y_i s.
 template <int N, int BITS, typename OutT, int ROPE>
 __global__ __launch_bounds__(kBlock) void dequantize_fast_kernel(TensorArgs a,
-                                                                 int sh_chunk) {
+                                                                 int sh_chunk,
+                                                                 int tile_major) {
   constexpr int VL = N / 8;
   constexpr int TPW = 64 / VL;
   constexpr int L = 1 << BITS;
@@ -644,10 +758,11 @@ __global__ __launch_bounds__(kBlock) void dequantize_fast_kernel(TensorArgs a,
   const int m = lane_group(l);
   const int64_t n_tt = (a.T + TPW - 1) / TPW;
   const int64_t SH = a.n_vec / a.T;
-  const int64_t wave = (int64_t)blockIdx.x * (kBlock / 64) + (threadIdx.x >> 6);
-  const int64_t tt = wave % n_tt;
-  const int64_t sh0 = (wave / n_tt) * sh_chunk;
-  if (sh0 >= SH) return;
+  const int64_t wave = xcd_wave_id();
+  const int64_t n_shc = (SH + sh_chunk - 1) / sh_chunk;
+  const int64_t tt = tile_major ? wave / n_shc : wave % n_tt;
+  const int64_t sh0 = (tile_major ? wave % n_shc : wave / n_tt) * sh_chunk;
+  if (tt >= n_tt || sh0 >= SH) return;
   const int64_t sh1 = min(SH, sh0 + sh_chunk);
   const int64_t t = tt * TPW + row;
   const bool tvalid = t < a.T;
@@ -688,17 +803,28 @@ __global__ __launch_bounds__(kBlock) void dequantize_fast_kernel(TensorArgs a,
   }
   const uint32_t flip = neg_sigma ? OutIo<OutT>::kFlip : 0u;
 
-  for (int64_t sh = sh0; sh < sh1; ++sh) {
-    const int64_t vec = sh * a.T + tc;
+  // code word, coset byte and scale of the next (slab, head) are loaded one
+  // iteration ahead
+  auto load_meta = [&](int64_t vec, uint32_t& code, uint32_t& cbyte, uint16_t& sbits) {
     const uint8_t* cp = a.codes + vec * a.code_bytes + m * BITS;
-    uint32_t code;
     if (BITS == 2) {
       code = *reinterpret_cast<const uint16_t*>(cp);
     } else {
       code = (uint32_t)cp[0] | ((uint32_t)cp[1] << 8) | ((uint32_t)cp[2] << 16);
     }
-    const int c = (a.cosets[vec * a.coset_bytes + (m >> 3)] >> (m & 7)) & 1;
-    const float sc = h2f(a.scales[vec * a.n_scales + m / gl]) * a.inv_sqrt_n;
+    cbyte = a.cosets[vec * a.coset_bytes + (m >> 3)];
+    sbits = a.scales[vec * a.n_scales + m / gl];
+  };
+  uint32_t code_n, cbyte_n;
+  uint16_t sbits_n;
+  load_meta(sh0 * a.T + tc, code_n, cbyte_n, sbits_n);
+  for (int64_t sh = sh0; sh < sh1; ++sh) {
+    const int64_t vec = sh * a.T + tc;
+    const uint32_t code = code_n, cbyte = cbyte_n;
+    const uint16_t sbits = sbits_n;
+    if (sh + 1 < sh1) load_meta(vec + a.T, code_n, cbyte_n, sbits_n);
+    const int c = (int)((cbyte >> (m & 7)) & 1u);
+    const float sc = h2f(sbits) * a.inv_sqrt_n;
     const float off = (0.5f * (float)c - a.half_L) * sc;
     float v[8];
 #pragma unroll
@@ -1028,32 +1154,46 @@ __global__ __launch_bounds__(kBlock) void rope_table_kernel(
   table[i] = make_float2((float)cs, (float)sn);
 }
 
-template <int N, int BITS, bool STRICT, typename T, int ROPE>
+// (slab, head) pairs per wave: about 8192 waves in all (32 per CU, the
+// resident limit at <= 64 VGPRs), so that on long caches each wave walks all
+// pairs of its token tile and reads its RoPE rows once.
+inline int sh_chunk_for(int64_t SH, int64_t n_tt) {
+  int64_t n_shc = (8192 + n_tt - 1) / n_tt;
+  if (n_shc < 1) n_shc = 1;
+  if (n_shc > SH) n_shc = SH;
+  return (int)((SH + n_shc - 1) / n_shc);
+}
+
+template <int N, int BITS, bool STRICT, typename T, int ROPE, bool PAD>
 hipError_t quantize_fast_launch(const TensorArgs& a, hipStream_t s) {
   constexpr int TPW = 64 / (N / 8);
   const int64_t SH = a.n_vec / a.T;
-  const int chunk = (int)(SH < 16 ? SH : 16);
   const int64_t n_tt = (a.T + TPW - 1) / TPW;
+  const int chunk = (int)(SH < 64 ? SH : 64);
   const int64_t waves = n_tt * ((SH + chunk - 1) / chunk);
-  const int64_t blocks = (waves + kBlock / 64 - 1) / (kBlock / 64);
-  hipLaunchKernelGGL((quantize_fast_kernel<N, BITS, STRICT, T, ROPE>),
-                     dim3((unsigned)blocks), dim3(kBlock), 0, s, a, chunk);
+  const int64_t blocks = ((waves + kBlock / 64 - 1) / (kBlock / 64) + 7) / 8 * 8;
+  hipLaunchKernelGGL((quantize_fast_kernel<N, BITS, STRICT, T, ROPE, PAD>),
+                     dim3((unsigned)blocks), dim3(kBlock), 0, s, a, chunk, 1);
   return hipGetLastError();
 }
 
 template <int N, int BITS, bool STRICT, typename T>
 hipError_t quantize_fast_rope(const TensorArgs& a, hipStream_t s) {
-  if (a.rope == nullptr) return quantize_fast_launch<N, BITS, STRICT, T, 0>(a, s);
-  if (a.d == 8) return quantize_fast_launch<N, BITS, STRICT, T, 3>(a, s);
-  if (N >= 16 && a.d == N) return quantize_fast_launch<N, BITS, STRICT, T, 1>(a, s);
-  return quantize_fast_launch<N, BITS, STRICT, T, 2>(a, s);
+  if (a.rope == nullptr) {
+    return a.d == N ? quantize_fast_launch<N, BITS, STRICT, T, 0, false>(a, s)
+                    : quantize_fast_launch<N, BITS, STRICT, T, 0, true>(a, s);
+  }
+  if (a.d == 8) return quantize_fast_launch<N, BITS, STRICT, T, 3, false>(a, s);
+  if (N >= 16 && a.d == N) return quantize_fast_launch<N, BITS, STRICT, T, 1, false>(a, s);
+  return quantize_fast_launch<N, BITS, STRICT, T, 2, true>(a, s);
 }
 
 template <int N, int BITS, typename T>
 hipError_t quantize_n(const TensorArgs& a, hipStream_t s) {
   if constexpr (N <= 128) {
-    return a.strict ? quantize_fast_rope<N, BITS, true, T>(a, s)
-                    : quantize_fast_rope<N, BITS, false, T>(a, s);
+    if (a.T * a.d * (int64_t)sizeof(T) < ((int64_t)1 << 31))
+      return a.strict ? quantize_fast_rope<N, BITS, true, T>(a, s)
+                      : quantize_fast_rope<N, BITS, false, T>(a, s);
   }
   constexpr int VPB = kBlock / (N / 8);
   const int64_t blocks = (a.n_vec + VPB - 1) / VPB;
@@ -1070,12 +1210,12 @@ template <int N, int BITS, typename T, int ROPE>
 hipError_t dequantize_fast_launch(const TensorArgs& a, hipStream_t s) {
   constexpr int TPW = 64 / (N / 8);
   const int64_t SH = a.n_vec / a.T;
-  const int chunk = (int)(SH < 16 ? SH : 16);
   const int64_t n_tt = (a.T + TPW - 1) / TPW;
+  const int chunk = sh_chunk_for(SH, n_tt);
   const int64_t waves = n_tt * ((SH + chunk - 1) / chunk);
-  const int64_t blocks = (waves + kBlock / 64 - 1) / (kBlock / 64);
+  const int64_t blocks = ((waves + kBlock / 64 - 1) / (kBlock / 64) + 7) / 8 * 8;
   hipLaunchKernelGGL((dequantize_fast_kernel<N, BITS, T, ROPE>), dim3((unsigned)blocks),
-                     dim3(kBlock), 0, s, a, chunk);
+                     dim3(kBlock), 0, s, a, chunk, 0);
   return hipGetLastError();
 }
 
