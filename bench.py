@@ -160,6 +160,23 @@ def main():
     tq = tk + tv
     q_gbps = q_bytes / (tq * 1e-3) / 1e9
 
+    # next row: value half of decode attention on the packed V, weights =
+    # softmax of the step's scores (timed on its own, not part of the step)
+    wts = torch.softmax(scores, dim=-1).contiguous()
+    att = torch.empty((w.S, Hq, w.d), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        nq.attend_packed_values(cfg, pv, wts, w.S, w.H, w.T, out=att)
+    ea = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ea[0].record(stream)
+    for _ in range(args.steps):
+        nq.attend_packed_values(cfg, pv, wts, w.S, w.H, w.T, out=att)
+    ea[1].record(stream)
+    torch.cuda.synchronize()
+    tat = ea[0].elapsed_time(ea[1]) / args.steps
+    at_bytes = packed + w.S * Hq * w.T * 4 + w.S * Hq * w.d * 4
+    del wts, att
+
     # plain device copy of 4 GiB for context
     src = torch.empty(1 << 31, dtype=torch.float16, device=dev)
     dst = torch.empty_like(src)
@@ -207,6 +224,13 @@ def main():
         "dequantize_GBps": dq_bytes / (tdq * 1e-3) / 1e9,
         "score_GBps": sc_bytes / (tsc * 1e-3) / 1e9,
         "copy_GBps": copy_gbps,
+        "next_rows": {
+            "attend_packed_values": {
+                "ms": tat,
+                "GBps": at_bytes / (tat * 1e-3) / 1e9,
+                "what": "sum_t softmax(scores)_t * V_t over the packed V, 32 query heads",
+            },
+        },
         "roofline": {
             "bound": "hbm",
             "achieved": q_gbps,

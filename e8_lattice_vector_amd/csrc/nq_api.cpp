@@ -252,6 +252,42 @@ int nq_score_packed_keys(const nq_config* cfg, const nq_packed* pk, int64_t S,
   return NQ_OK;
 }
 
+int nq_attend_packed_values(const nq_config* cfg, const nq_packed* pv,
+                            int64_t S, int32_t H, int32_t Hq, int64_t T,
+                            const float* weights, float* out, void* stream) {
+  int st = check_config(cfg);
+  if (st != NQ_OK) return st;
+  if ((st = check_shape(S, H, T)) != NQ_OK) return st;
+  if (Hq <= 0 || Hq % H != 0) return NQ_ERR_INVALID_ARG;
+  if (S > 65535 || (int64_t)H * ((Hq / H + 3) / 4 + 1) > 65535) return NQ_ERR_UNSUPPORTED;
+  if ((st = check_packed(pv)) != NQ_OK) return st;
+  if (weights == nullptr || out == nullptr || !aligned16(weights) || !aligned16(out))
+    return NQ_ERR_INVALID_ARG;
+  const Layout l = layout(cfg, 1);
+  nq::AttendArgs a;
+  memset(&a, 0, sizeof(a));
+  a.codes = static_cast<const uint8_t*>(pv->codes);
+  a.cosets = static_cast<const uint8_t*>(pv->cosets);
+  a.scales = static_cast<const uint16_t*>(pv->scales);
+  a.w = weights;
+  a.out = out;
+  a.S = S;
+  a.T = T;
+  a.H = H;
+  a.Hq = Hq;
+  a.d = l.d;
+  a.n = l.n;
+  a.G = l.G;
+  a.bits = l.bits;
+  a.code_bytes = l.code_bytes;
+  a.coset_bytes = l.coset_bytes;
+  a.n_scales = l.n_scales;
+  a.half_L = (float)(l.L / 2);
+  a.inv_sqrt_n = (float)(1.0 / sqrt((double)l.n));
+  if (nq::launch_attend(a, static_cast<hipStream_t>(stream)) != hipSuccess) return NQ_ERR_HIP;
+  return NQ_OK;
+}
+
 int nq_e8_decode_debug(const float* y, int64_t n_groups, int32_t bits,
                        int32_t parity, uint8_t* idx_out, uint8_t* coset_out,
                        void* stream) {

@@ -36,6 +36,18 @@ struct ScoreArgs {
   float inv_sqrt_n;
 };
 
+struct AttendArgs {
+  const uint8_t* codes;
+  const uint8_t* cosets;
+  const uint16_t* scales;
+  const float* w;       // [S][Hq][T]
+  float* out;           // [S][Hq][d]
+  int64_t S, T;
+  int H, Hq, d, n, G, bits, code_bytes, coset_bytes, n_scales;
+  float half_L;
+  float inv_sqrt_n;
+};
+
 constexpr int kMaxHalfDim = 128;
 struct RopeFreqs {
   double omega[kMaxHalfDim];  // theta^(-2i/d), computed on the host
@@ -47,6 +59,7 @@ hipError_t launch_rope_table(const int32_t* positions, int64_t T, int d,
 hipError_t launch_quantize(const TensorArgs& a, int in_dtype, hipStream_t s);
 hipError_t launch_dequantize(const TensorArgs& a, int out_dtype, hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, int in_dtype, hipStream_t s);
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 hipError_t launch_decode_debug(const float* y, int64_t n_groups, int bits,
                                int strict, uint8_t* idx, uint8_t* coset,
                                hipStream_t s);

@@ -1124,6 +1124,133 @@ __global__ __launch_bounds__(kLutBlock) void score_lut_kernel(ScoreArgs a,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Value half of decode attention on the packed cache:
+//   out[s][h] = sum_t w[s][h][t] * D(V)[s][h / (Hq/H)][t].
+// D is linear, so the sum is taken in the codec frame,
+//   z = sum_t w_t s_t (idx_t - L/2 + c_t/2),   out = (H z / sqrt n)[:d],
+// with one Walsh-Hadamard transform per query head instead of one per key.
+// One workgroup per (slab, KV head, head pass); each VL-lane row takes one
+// key per step, lane m accumulates its 8-group; rows and waves are reduced
+// through LDS in a fixed order (deterministic).
+// ---------------------------------------------------------------------------
+constexpr int kAttBlock = 1024;
+
+template <int BITS, int N, int HPP>
+__global__ __launch_bounds__(kAttBlock) void attend_kernel(AttendArgs a, int n_pass) {
+  constexpr int VL = N / 8;
+  constexpr int KPW = 64 / VL;             // keys per wave per step
+  constexpr int L = 1 << BITS;
+  extern __shared__ float lds[];           // [n_waves][HPP][N]
+  const int64_t s = blockIdx.z;
+  const int h = blockIdx.y / n_pass;
+  const int pass = blockIdx.y % n_pass;
+  const int grp = a.Hq / a.H;
+  const int hq0 = h * grp + pass * HPP;
+  const int nh = min(HPP, h * grp + grp - hq0);
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int row = lane / VL;
+  const int m = lane % VL;
+  const int gl = a.G >> 3;
+  float acc[HPP][8];
+  float offacc[HPP];
+#pragma unroll
+  for (int g = 0; g < HPP; ++g) {
+    offacc[g] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[g][k] = 0.f;
+  }
+  const int64_t base = (s * a.H + h) * a.T;
+  const float* wrow = a.w + (s * a.Hq + hq0) * a.T;
+  const int64_t stride = (int64_t)nw * KPW;
+  // U keys per row per step, all loads issued before any use so that U
+  // HBM round trips overlap
+  constexpr int U = 8;
+  for (int64_t t0 = (int64_t)wv * KPW + row; t0 < a.T; t0 += U * stride) {
+    uint32_t code[U], cbyte[U];
+    uint16_t sbits[U];
+    float wt[U][HPP];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t tu = t0 + u * stride;
+      const bool ok = tu < a.T;
+      const int64_t vec = base + (ok ? tu : t0);
+      const uint8_t* cp = a.codes + vec * a.code_bytes + m * BITS;
+      if (BITS == 2) {
+        code[u] = *reinterpret_cast<const uint16_t*>(cp);
+      } else {
+        code[u] = (uint32_t)cp[0] | ((uint32_t)cp[1] << 8) | ((uint32_t)cp[2] << 16);
+      }
+      cbyte[u] = a.cosets[vec * a.coset_bytes + (m >> 3)];
+      sbits[u] = a.scales[vec * a.n_scales + m / gl];
+#pragma unroll
+      for (int g = 0; g < HPP; ++g)
+        wt[u][g] = (ok && g < nh) ? wrow[(int64_t)g * a.T + tu] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = (int)((cbyte[u] >> (m & 7)) & 1u);
+      const float sc = h2f(sbits[u]);
+      const float off = 0.5f * (float)c - a.half_L;
+      float p[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        p[k] = (float)((code[u] >> (BITS * k)) & (uint32_t)(L - 1));
+#pragma unroll
+      for (int g = 0; g < HPP; ++g) {
+        const float ws = wt[u][g] * sc;
+        offacc[g] = fmaf(ws, off, offacc[g]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[g][k] = fmaf(ws, p[k], acc[g][k]);
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < HPP; ++g) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[g][k] += offacc[g];
+  }
+  // rows of a wave hold the same 8-group: add lanes l, l + VL, l + 2 VL, ...
+#pragma unroll
+  for (int sft = VL; sft < 64; sft <<= 1) {
+#pragma unroll
+    for (int g = 0; g < HPP; ++g) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[g][k] += __shfl_xor(acc[g][k], sft);
+    }
+  }
+  if (lane < VL) {
+#pragma unroll
+    for (int g = 0; g < HPP; ++g) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) lds[(wv * HPP + g) * N + 8 * m + k] = acc[g][k];
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < HPP * N; i += blockDim.x) {
+    float sum = 0.f;
+    for (int w = 0; w < nw; ++w) sum += lds[w * HPP * N + i];
+    lds[i] = sum;
+  }
+  __syncthreads();
+  for (int hs = 1; hs < N; hs <<= 1) {
+    for (int i = threadIdx.x; i < HPP * (N / 2); i += blockDim.x) {
+      const int g = i / (N / 2), r = i % (N / 2);
+      const int j = (r / hs) * 2 * hs + (r % hs);
+      const float x0 = lds[g * N + j], x1 = lds[g * N + j + hs];
+      lds[g * N + j] = x0 + x1;
+      lds[g * N + j + hs] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < nh * a.d; i += blockDim.x) {
+    const int g = i / a.d, j = i % a.d;
+    a.out[(s * a.Hq + hq0 + g) * (int64_t)a.d + j] = lds[g * N + j] * a.inv_sqrt_n;
+  }
+}
+
 template <int BITS, bool STRICT>
 __global__ __launch_bounds__(kBlock) void decode_debug_kernel(
     const float* y, int64_t n, uint8_t* idx, uint8_t* coset) {
@@ -1322,6 +1449,52 @@ hipError_t score_t(const ScoreArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+
+template <int BITS, int N, int HPP>
+hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
+  const int grp = a.Hq / a.H;
+  const int n_pass = (grp + HPP - 1) / HPP;
+  const size_t lds = sizeof(float) * (size_t)(kAttBlock / 64) * HPP * N;
+  auto kern = attend_kernel<BITS, N, HPP>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const dim3 grid(1u, (unsigned)(a.H * n_pass), (unsigned)a.S);
+  hipLaunchKernelGGL(kern, grid, dim3(kAttBlock), lds, s, a, n_pass);
+  return hipGetLastError();
+}
+
+template <int BITS, int N>
+hipError_t attend_n(const AttendArgs& a, hipStream_t s) {
+  const int grp = a.Hq / a.H;
+  if (grp <= 1) return attend_launch<BITS, N, 1>(a, s);
+  if (grp <= 2) return attend_launch<BITS, N, 2>(a, s);
+  if (grp <= 4 || N > 128) return attend_launch<BITS, N, 4>(a, s);
+  return attend_launch<BITS, N, 8>(a, s);
+}
+
+template <int BITS>
+hipError_t attend_b(const AttendArgs& a, hipStream_t s) {
+  switch (a.n) {
+    case 8: return attend_n<BITS, 8>(a, s);
+    case 16: return attend_n<BITS, 16>(a, s);
+    case 32: return attend_n<BITS, 32>(a, s);
+    case 64: return attend_n<BITS, 64>(a, s);
+    case 128: return attend_n<BITS, 128>(a, s);
+    case 256: return attend_n<BITS, 256>(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
+  if (a.bits == 2) return attend_b<2>(a, s);
+  if (a.bits == 3) return attend_b<3>(a, s);
+  return hipErrorInvalidValue;
+}
+
+namespace {
 }  // namespace
 
 hipError_t launch_rope_table(const int32_t* positions, int64_t T, int d,

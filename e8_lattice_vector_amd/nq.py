@@ -29,7 +29,7 @@ PLANE_CODES, PLANE_COSETS, PLANE_SCALES = 0, 1, 2
 
 EXPORTED = ("nq_packed_bytes", "nq_workspace_bytes", "nq_status_string",
             "nq_quantize_kv", "nq_dequantize_kv", "nq_score_packed_keys",
-            "nq_e8_decode_debug")
+            "nq_attend_packed_values", "nq_e8_decode_debug")
 
 
 class _Config(ctypes.Structure):
@@ -76,6 +76,8 @@ def load(path: str = LIB_PATH):
     lib.nq_dequantize_kv.restype = ctypes.c_int
     lib.nq_score_packed_keys.argtypes = [cfgp, pkp, i64, i32, i32, i64, vp, vp, vp, sz, vp]
     lib.nq_score_packed_keys.restype = ctypes.c_int
+    lib.nq_attend_packed_values.argtypes = [cfgp, pkp, i64, i32, i32, i64, vp, vp, vp]
+    lib.nq_attend_packed_values.restype = ctypes.c_int
     lib.nq_e8_decode_debug.argtypes = [vp, i64, i32, i32, vp, vp, vp]
     lib.nq_e8_decode_debug.restype = ctypes.c_int
     _lib = lib
@@ -240,6 +242,23 @@ def score_packed_keys(cfg: Config, pk: Packed, q, S: int, H: int, T: int,
                                      _stream(stream))
     _check(st, "nq_score_packed_keys")
     return scores
+
+
+def attend_packed_values(cfg: Config, pv: Packed, weights, S: int, H: int, T: int,
+                         out=None, stream=None):
+    """weights: fp32 [S][Hq][T] device tensor -> fp32 [S][Hq][d] sum_t w_t * V_t."""
+    Hq = weights.shape[1]
+    if (weights.dtype != torch.float32 or not weights.is_contiguous()
+            or tuple(weights.shape) != (S, Hq, T)):
+        raise NQError(NQ_ERR_INVALID_ARG, "attend_packed_values weights")
+    if out is None:
+        out = torch.empty((S, Hq, cfg.head_dim), dtype=torch.float32, device=weights.device)
+    cc = cfg.c()
+    cv = pv.c()
+    st = load().nq_attend_packed_values(ctypes.byref(cc), ctypes.byref(cv), S, H, Hq, T,
+                                        weights.data_ptr(), out.data_ptr(), _stream(stream))
+    _check(st, "nq_attend_packed_values")
+    return out
 
 
 def e8_decode_debug(y, bits: int, parity: int, stream=None):

@@ -160,6 +160,22 @@ int nq_score_packed_keys(const nq_config* cfg, const nq_packed* pk,
                          float* scores, void* workspace, size_t ws_bytes,
                          void* stream);
 
+/* Value half of decode attention on the packed cache ([Walk] "What Makes
+ * This Hard in Practice", item 3: the packed form stays on the device and is
+ * used there; [E8KQ] Abstract: attention over the compressed cache):
+ *   out[s][h][:] = sum_t weights[s][h][t] * D(V)[s][h / (n_q_heads / n_kv_heads)][t][:]
+ * with D the dequantization of the values (no RoPE), summed in the codec
+ * frame (one inverse Walsh-Hadamard transform per query head).
+ *  pv       packed values (bits_v, scale_group, parity from cfg)
+ *  weights  device fp32 [S][n_q_heads][T] (e.g. softmax of the scores)
+ *  out      device fp32 [S][n_q_heads][d]
+ * n_q_heads must be a positive multiple of n_kv_heads.  The result is
+ * deterministic (fixed reduction order).  Errors as nq_quantize_kv. */
+int nq_attend_packed_values(const nq_config* cfg, const nq_packed* pv,
+                            int64_t n_slabs, int32_t n_kv_heads,
+                            int32_t n_q_heads, int64_t n_tokens,
+                            const float* weights, float* out, void* stream);
+
 /* Test hook: the nearest-codeword decoder alone ([Walk] "The Conway-Sloane
  * Nearest-Point Algorithm") on caller-given groups y (lattice units).
  *  y          device fp32 [n_groups][8]

@@ -44,7 +44,8 @@ Packed planes, row-major over [S][H][T] vectors:
 
 Parity status: pinned (scale range, zero vector, pack/unpack round trip,
 plane sizes, strict parity of every group, lattice-point round trips,
-score = dot with an independent dequantization) -- tests/test_oracle_codec.py.
+score = dot with an independent dequantization, attend = one-hot rows, the
+codec-frame form and linearity) -- tests/test_oracle_codec.py.
 """
 
 from __future__ import annotations
@@ -56,7 +57,7 @@ import numpy as np
 
 from . import lattice, transform
 
-__all__ = ["Codec", "quantize", "dequantize", "score", "pack_codes",
+__all__ = ["Codec", "quantize", "dequantize", "score", "attend", "pack_codes",
            "unpack_codes", "pack_cosets", "unpack_cosets", "fp16_kv_bytes"]
 
 
@@ -206,4 +207,23 @@ def score(q, codes, cosets, scales, codec: Codec) -> np.ndarray:
     out = np.empty((S, Hq, k.shape[2]))
     for h in range(Hq):
         out[:, h, :] = np.einsum("sd,std->st", q[:, h, :], k[:, h // grp])
+    return out
+
+
+def attend(weights, codes, cosets, scales, codec: Codec) -> np.ndarray:
+    """out[s][h] = sum_t weights[s][h][t] * D(V)[s][h // (Hq/H)][t]   (fp64).
+
+    The value half of decode attention on the packed cache (the packed form
+    is kept on the device and unpacked on the fly: NexusQuant blog, E8
+    walkthrough post, "What Makes This Hard in Practice", item 3; scores from
+    the same cache: Nedelkoski et al., Abstract).  Values carry no RoPE.
+    weights: [S, Hq, T]; planes: [S, H, T, .] -> [S, Hq, d]."""
+    w = np.asarray(weights, dtype=np.float64)
+    v = dequantize(codes, cosets, scales, codec, is_key=False)    # [S,H,T,d]
+    S, Hq, _ = w.shape
+    H = v.shape[1]
+    grp = Hq // H
+    out = np.empty((S, Hq, v.shape[-1]))
+    for h in range(Hq):
+        out[:, h, :] = np.einsum("st,std->sd", w[:, h, :], v[:, h // grp])
     return out

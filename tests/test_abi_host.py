@@ -81,6 +81,11 @@ def test_invalid_arguments_rejected_before_launch():
     sc = lib.nq_score_packed_keys
     assert sc(ctypes.byref(c), ctypes.byref(pk), 1, 3, 4, 8, 0x10000, 0x20000, None, 0, None) == -1
     assert sc(ctypes.byref(c), ctypes.byref(pk), 1, 2, 4, 8, 0x10000, 0x20008, None, 0, None) == -1
+    at = lib.nq_attend_packed_values
+    assert at(ctypes.byref(c), ctypes.byref(pk), 1, 3, 4, 8, 0x10000, 0x20000, None) == -1
+    assert at(ctypes.byref(c), ctypes.byref(pk), 1, 2, 4, 8, 0x10004, 0x20000, None) == -1
+    assert at(ctypes.byref(c), None, 1, 2, 4, 8, 0x10000, 0x20000, None) == -1
+    assert at(ctypes.byref(c), ctypes.byref(pk), 0, 2, 4, 8, 0x10000, 0x20000, None) == -1
     dd = lib.nq_e8_decode_debug
     assert dd(0x1000, 10, 4, 0, 0x2000, 0x3000, None) == -2
     assert dd(0x1000, 0, 2, 0, 0x2000, 0x3000, None) == -1

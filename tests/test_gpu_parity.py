@@ -210,3 +210,63 @@ def test_qwen_decode_scores_sampled():
     ref = (kd * qs).sum(-1)
     got = scores[st, hqt, tt].cpu().numpy()
     check_scores(got, ref, np.linalg.norm(qs, axis=-1), np.linalg.norm(kd, axis=-1), "qwen")
+
+
+def _check_attend(out, w, planes, codec, label):
+    """|out - ref| <= 1e-3 * sum_t |w_t| |v^_t| per (slab, query head)."""
+    ref = oc.attend(w, *planes, codec)
+    vd = oc.dequantize(*planes, codec)                                   # [S,H,T,d]
+    grp = w.shape[1] // vd.shape[1]
+    vn = np.repeat(np.linalg.norm(vd, axis=-1), grp, axis=1)             # [S,Hq,T]
+    lim = 1e-3 * (np.abs(w) * vn).sum(-1) + 1e-9
+    err = np.linalg.norm(out - ref, axis=-1)
+    assert np.all(err <= lim), f"{label}: worst {np.max(err / lim)}"
+
+
+@pytest.mark.parametrize("cfg,grp,signed", [
+    (nq.Config(128, 2, 2, 0, R_, F16, 5e5), 4, False),
+    (nq.Config(96, 2, 3, 32, S_, F16, 1e4), 3, False),
+    (nq.Config(64, 2, 2, 0, R_, F32, 0.0), 12, True),
+    (nq.Config(256, 2, 2, 64, S_, F16, 0.0), 2, False),
+    (nq.Config(8, 2, 3, 8, R_, F32, 0.0), 1, True),
+    (nq.Config(128, 3, 3, 64, R_, F16, 1e6), 5, False),
+])
+def test_attend_parity(cfg, grp, signed):
+    S, H, T = 2, 2, 1501
+    log(f"[attend] d={cfg.head_dim} bits_v={cfg.bits_v} G={cfg.scale_group} grp={grp}")
+    _, v = _inputs(cfg, S, H, T, 6)
+    _, pv = nq.quantize_kv(cfg, None, v)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11)
+    x = torch.randn((S, H * grp, T), generator=g, device=DEV)
+    w = (x if signed else torch.softmax(x * 3, dim=-1)).contiguous()
+    out = nq.attend_packed_values(cfg, pv, w, S, H, T)
+    torch.cuda.synchronize()
+    _check_attend(out.cpu().numpy(), w.cpu().numpy().astype(np.float64), to_np(pv),
+                  oracle_codec(cfg, True), "attend")
+
+
+def test_attend_llama_full_sampled():
+    """Llama-3.1-8B 32K values, 32 query heads (GQA 4), softmax weights;
+    every output of 4 sampled (slab, KV head) pairs checked against the
+    oracle."""
+    w_ = workloads.LLAMA
+    cfg = nq.Config(w_.d, w_.bits_k, w_.bits_v, w_.G, R_, F16, w_.theta)
+    _, v = synth.workload_inputs(w_, seed=0, device=DEV)
+    _, pv = nq.quantize_kv(cfg, None, v)
+    del v
+    Hq = 32
+    g = torch.Generator(device=DEV)
+    g.manual_seed(12)
+    w = torch.softmax(torch.randn((w_.S, Hq, w_.T), generator=g, device=DEV) * 4, dim=-1)
+    out = nq.attend_packed_values(cfg, pv, w.contiguous(), w_.S, w_.H, w_.T)
+    torch.cuda.synchronize()
+    log("[attend-full] computed")
+    rng = np.random.default_rng(3)
+    codec = oracle_codec(cfg, True)
+    for _ in range(4):
+        s, h = int(rng.integers(0, w_.S)), int(rng.integers(0, w_.H))
+        planes = [pl[s:s + 1, h:h + 1].cpu().numpy() for pl in (pv.codes, pv.cosets, pv.scales)]
+        ws = w[s:s + 1, 4 * h:4 * h + 4].cpu().numpy().astype(np.float64)
+        _check_attend(out[s:s + 1, 4 * h:4 * h + 4].cpu().numpy(), ws, planes, codec,
+                      f"attend-full s={s} h={h}")

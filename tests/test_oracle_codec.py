@@ -144,3 +144,34 @@ def test_score_equals_rotated_query_form():
     for h in range(Hq):
         ref = np.einsum("sd,std->st", qt[:, h], sc[:, h // 3] * p[:, h // 3])
         np.testing.assert_allclose(s[:, h], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_attend_pins():
+    """attend(): one-hot weights give dequantized rows; the sum equals the
+    codec-frame form (H sum_t w_t s_t p_t / sqrt(n))[:d] computed here
+    independently; linear in the weights."""
+    cfg = oc.Codec(96, 2, 32, strict=True)
+    S, H, Hq, T = 2, 2, 4, 37
+    v = _x((S, H, T, 96), 9, outliers=False)
+    pv = oc.quantize(v, cfg)
+    planes = (pv["codes"], pv["cosets"], pv["scales"])
+    vd = oc.dequantize(*planes, cfg)
+    rng = np.random.default_rng(10)
+    w = rng.uniform(0, 1, size=(S, Hq, T))
+    out = oc.attend(w, *planes, cfg)
+    # one-hot weights
+    onehot = np.zeros((S, Hq, T))
+    onehot[:, :, 5] = 1.0
+    np.testing.assert_allclose(oc.attend(onehot, *planes, cfg),
+                               np.repeat(vd[:, :, 5, :], Hq // H, axis=1), atol=1e-12)
+    # codec-frame identity
+    p = lattice.codeword_points(pv["idx"].reshape(-1, 8), pv["c"].reshape(-1), cfg.L).reshape(S, H, T, 128)
+    sc = np.repeat(pv["scales"].astype(np.float64), 32, -1)
+    for h in range(Hq):
+        z = np.einsum("st,stj->sj", w[:, h], sc[:, h // 2] * p[:, h // 2])
+        ref = transform.fwht_f64(z)[:, :96] / math.sqrt(128)
+        np.testing.assert_allclose(out[:, h], ref, rtol=1e-12, atol=1e-12)
+    # linearity
+    w2 = rng.normal(size=w.shape)
+    np.testing.assert_allclose(oc.attend(2 * w - 3 * w2, *planes, cfg),
+                               2 * out - 3 * oc.attend(w2, *planes, cfg), atol=1e-10)
