@@ -428,6 +428,37 @@ __device__ __forceinline__ uint32_t spread8(uint32_t x) {
   return x;
 }
 
+// fl(1/a): the hardware reciprocal estimate refined by one Newton step whose
+// residual 1 - a*r0 is formed by a fused multiply-add.  On gfx950 this equals
+// the correctly rounded quotient 1/a for every normal a below 2^126, i.e.
+// wherever 1/a is normal (compared against IEEE division for every fp32
+// mantissa of every such binade); the callers keep the true division above.
+__device__ __forceinline__ float rcp_rn(float a) {
+  const float r0 = __builtin_amdgcn_rcpf(a);
+  const float e = __builtin_fmaf(-a, r0, 1.0f);
+  return __builtin_fmaf(e, r0, r0);
+}
+
+// Coset words from a wave-wide ballot: bit VL*row + l of `mask` is the coset
+// bit of lane l of that row; move it to bit VL*row + lane_group(l), i.e.
+// reverse the nibbles at odd nibble positions (l ^ 3 where bit 2 of l is
+// set), then for VL = 16 swap nibbles 2 and 3 of each 16-bit row word
+// (l ^ 4 where bit 3 is set).  Runs on the scalar unit.
+template <int VL>
+__device__ __forceinline__ uint64_t coset_rows(uint64_t x) {
+  if (VL >= 8) {
+    const uint64_t odd = x & 0xF0F0F0F0F0F0F0F0ull;
+    x = (x & 0x0F0F0F0F0F0F0F0Full) | ((odd & 0x1010101010101010ull) << 3) |
+        ((odd & 0x8080808080808080ull) >> 3) | ((odd & 0x2020202020202020ull) << 1) |
+        ((odd & 0x4040404040404040ull) >> 1);
+  }
+  if (VL == 16) {
+    x = (x & 0x00FF00FF00FF00FFull) | ((x & 0x0F000F000F000F00ull) << 4) |
+        ((x & 0xF000F000F000F000ull) >> 4);
+  }
+  return x;
+}
+
 // (x << n) | (the top n bits of w): v_alignbit_b32
 __device__ __forceinline__ uint32_t shift_in(uint32_t x, float w, int n) {
   return __builtin_amdgcn_alignbit(x, __float_as_uint(w), (uint32_t)(32 - n));
@@ -461,9 +492,11 @@ __device__ __forceinline__ int64_t xcd_wave_id() {
 // the lowest index win ties.  Code word: 2-bit idx_k = p_k + 2 - c/2 at bits
 // [2k, 2k+2): integer coset bit0 = B, bit1 = ~(B & S); half coset
 // bit0 = E ^ S, bit1 = ~S.
+// `cosets` receives the wave-wide ballot of the coset bit (every lane of the
+// wave must be active).
 template <bool STRICT>
 __device__ __forceinline__ void e8_decode2(const float g[8], uint32_t& code,
-                                           int& coset) {
+                                           uint64_t& cosets) {
   uint32_t X = 0, Bn = 0, f0 = 1u << 14, f1 = 0;
   float acc = 0.f, best0, best1 = -INFINITY;
 #pragma unroll
@@ -495,6 +528,7 @@ __device__ __forceinline__ void e8_decode2(const float g[8], uint32_t& code,
   }
   const float rhs = odd0 ? 4.f * best0 : 0.f;
   const int c = lhs < rhs ? 1 : 0;
+  cosets = __ballot(lhs < rhs);
   const uint32_t Bsp = spread8(~Bn);
   uint32_t w;
   if (c == 0) {
@@ -506,7 +540,6 @@ __device__ __forceinline__ void e8_decode2(const float g[8], uint32_t& code,
     w = ((x ^ (x >> 1)) & 0x5555u) | (~x & 0xaaaau);
   }
   code = w;
-  coset = c;
 }
 
 // ROPE: 0 none, 1 partner through DPP (d == n >= 16), 2 partner through
@@ -561,8 +594,14 @@ __global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
 #pragma unroll
   for (int k = 0; k < 4; ++k) coef[k] = ((m >> k) & 1) ? -1.f : 1.f;
   const bool neg_sigma = (__builtin_popcount(m) & 1) != 0;
-  const uint32_t my_cbit = 1u << m;
-  const bool scale_lane = (m % gl) == 0;
+  // decision scale 2r (2-bit decoder on 2y) or r, with the lane's sign
+  const float kr = (neg_sigma ? -a.half_L : a.half_L) * (BITS == 2 ? 2.f : 1.f);
+  const float kq = (neg_sigma ? -1.f : 1.f) * (BITS == 2 ? 2.f : 1.f);
+  const int row_shift = row * VL;
+  constexpr uint32_t kRowMask = VL >= 32 ? 0xffffffffu : (1u << VL) - 1u;
+  // Scale conversions are batched over gl iterations: lane m keeps the group
+  // maximum of iteration (m % gl) of the batch and converts it at the flush.
+  const int mg = m % gl;
 
   // per-lane byte offsets inside one (slab, head) plane (the host keeps
   // them below 2^31); the plane bases advance uniformly with sh
@@ -574,13 +613,24 @@ __global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
   const int64_t plane_c = a.T * a.code_bytes;
   const int64_t plane_s = a.T * a.coset_bytes;
   const int64_t plane_g = a.T * a.n_scales;
-  for (int64_t sh = sh0; sh < sh1; ++sh) {
+  const uint32_t off_gb = (off_g + (uint32_t)mg * (uint32_t)plane_g) * 2u;
+  float keep = 0.f;
+  // uniform plane bases in scalar registers, lane offsets in 32-bit vector
+  // registers (global_load/store with an SGPR base); the empty asm keeps the
+  // offsets from being folded into per-lane 64-bit pointers
+  const int n_it = (int)(sh1 - sh0);
+  const char* xb = static_cast<const char*>(a.x) + sh0 * plane_x;
+  uint8_t* cb = a.codes + sh0 * plane_c;
+  uint8_t* qb = a.cosets + sh0 * plane_s;
+  char* gb = reinterpret_cast<char*>(a.scales) + sh0 * plane_g * 2;
+  uint32_t ox = off_x, oc = off_c, os = off_s;
+  for (int it = 0; it < n_it; ++it, xb += plane_x, cb += plane_c, qb += plane_s) {
+    asm volatile("" : "+v"(ox), "+v"(oc), "+v"(os));
     float v[8];
-    const char* xb = static_cast<const char*>(a.x) + sh * plane_x;
     constexpr bool kFuse = ROPE == 0 && std::is_same<InT, __half>::value;
     if (!PAD || data_lane) {
-      if constexpr (kFuse) load8_h_stage1(xb + off_x, v);
-      else Io<InT>::load8(xb + off_x, 0, v);
+      if constexpr (kFuse) load8_h_stage1(xb + ox, v);
+      else Io<InT>::load8(xb + ox, 0, v);
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) v[k] = 0.f;
@@ -616,26 +666,32 @@ __global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
     if (VL > 8) stage_fmac<3>(v, coef[3]);
     float mx = abs_max8(v);
     mx = group_max<VL>(mx, gl);
-    const float amax = fmaxf(mx, a.eps);
-    const float r = __fdiv_rn(a.half_L, amax);
-    const float rsig = neg_sigma ? -r : r;
+    float amax;
+    asm("v_max_f32 %0, %1, %2" : "=v"(amax) : "s"(a.eps), "v"(mx));
+    // r = fl((L/2) / amax) = (L/2) fl(1/amax) (a power-of-two multiple);
+    // fp16 inputs keep amax below 2^25
+    float rs;
+    if (std::is_same<InT, __half>::value || amax < 0x1p126f)
+      rs = __fmul_rn(rcp_rn(amax), kr);
+    else
+      rs = __fmul_rn(__fdiv_rn(a.half_L, amax), kq);
     uint32_t code;
-    int c;
+    uint64_t cball;
+    float y[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) y[k] = __fmul_rn(v[k], rs);
     if (BITS == 2) {
-      float g[8];
-      const float r2 = rsig + rsig;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) g[k] = __fmul_rn(v[k], r2);
-      e8_decode2<STRICT>(g, code, c);
+      e8_decode2<STRICT>(y, code, cball);
     } else {
-      float y[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) y[k] = __fmul_rn(v[k], rsig);
+      int c;
       e8_decode<BITS, STRICT>(y, code, c);
+      cball = __ballot(c);
     }
-    const uint32_t cw = row_or<VL>(c ? my_cbit : 0u);
+    const uint64_t cmask = coset_rows<VL>(cball);
+    const int slot = it & (gl - 1);
+    if (mg == slot) keep = amax;
     if (tvalid) {
-      uint8_t* cp = a.codes + sh * plane_c + off_c;
+      uint8_t* cp = cb + oc;
       if (BITS == 2) {
         *reinterpret_cast<uint16_t*>(cp) = (uint16_t)code;
       } else {
@@ -644,12 +700,18 @@ __global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
         cp[2] = (uint8_t)(code >> 16);
       }
       if (m == 0) {
-        uint8_t* q = a.cosets + sh * plane_s + off_s;
+        const uint32_t cw = (uint32_t)(cmask >> row_shift) & kRowMask;
+        uint8_t* q = qb + os;
         if (VL > 8) *reinterpret_cast<uint16_t*>(q) = (uint16_t)cw;
         else q[0] = (uint8_t)cw;
       }
-      if (scale_lane)
-        a.scales[sh * plane_g + off_g] = f64_to_f16_rn((double)amax * a.sigma_k);
+    }
+    if (slot == gl - 1 || it == n_it - 1) {
+      if (tvalid && mg <= slot) {
+        char* sb = gb + (int64_t)(it - slot) * plane_g * 2;
+        *reinterpret_cast<uint16_t*>(sb + off_gb) =
+            f64_to_f16_rn((double)keep * a.sigma_k);
+      }
     }
   }
 }
