@@ -34,6 +34,16 @@ int check_config(const nq_config* c) {
     return NQ_ERR_INVALID_ARG;
   if (!(c->rope_theta >= 0.0) || !isfinite(c->rope_theta)) return NQ_ERR_INVALID_ARG;
   if (c->rope_theta > 0.0 && !(d == 8 || d % 16 == 0)) return NQ_ERR_UNSUPPORTED;
+  if (c->rope_scaling == NQ_ROPE_SCALING_LINEAR || c->rope_scaling == NQ_ROPE_SCALING_LLAMA3) {
+    if (!(c->rope_factor > 0.0) || !isfinite(c->rope_factor)) return NQ_ERR_INVALID_ARG;
+  } else if (c->rope_scaling != NQ_ROPE_SCALING_NONE) {
+    return NQ_ERR_INVALID_ARG;
+  }
+  if (c->rope_scaling == NQ_ROPE_SCALING_LLAMA3) {
+    if (!(c->rope_low_freq_factor > 0.0) || !isfinite(c->rope_high_freq_factor) ||
+        !(c->rope_high_freq_factor > c->rope_low_freq_factor) || c->rope_original_max <= 0)
+      return NQ_ERR_INVALID_ARG;
+  }
   const int n = next_pow2_min8(d);
   const int G = c->scale_group == 0 ? n : c->scale_group;
   if (G < 8 || G > n || (G % 8) != 0 || (n % G) != 0) return NQ_ERR_UNSUPPORTED;
@@ -99,6 +109,22 @@ nq::TensorArgs tensor_args(const nq_config* c, const Layout& l, int64_t S,
   return a;
 }
 
+// Frequency i of the rotary embedding, with the config's frequency scaling
+// (the formulas of nq_config, in fp64, in the order written there).
+double rope_freq(const nq_config* c, int i) {
+  const int d = c->head_dim;
+  const double w = pow(c->rope_theta, -(2.0 * i) / d);
+  if (c->rope_scaling == NQ_ROPE_SCALING_LINEAR) return w / c->rope_factor;
+  if (c->rope_scaling != NQ_ROPE_SCALING_LLAMA3) return w;
+  const double C = (double)c->rope_original_max;
+  const double lo = c->rope_low_freq_factor, hi = c->rope_high_freq_factor;
+  const double wavelen = 2.0 * M_PI / w;
+  if (wavelen < C / hi) return w;
+  if (wavelen > C / lo) return w / c->rope_factor;
+  const double a = (C / wavelen - lo) / (hi - lo);
+  return (1.0 - a) * w / c->rope_factor + a * w;
+}
+
 // Builds the cos/sin table in the workspace when keys need RoPE.
 int prepare_rope(const nq_config* c, int64_t T, const int32_t* positions,
                  void* ws, size_t ws_bytes, hipStream_t s, const float2** out) {
@@ -109,7 +135,7 @@ int prepare_rope(const nq_config* c, int64_t T, const int32_t* positions,
   if (!aligned16(ws)) return NQ_ERR_INVALID_ARG;
   nq::RopeFreqs f;
   const int d = c->head_dim;
-  for (int i = 0; i < d / 2; ++i) f.omega[i] = pow(c->rope_theta, -(2.0 * i) / d);
+  for (int i = 0; i < d / 2; ++i) f.omega[i] = rope_freq(c, i);
   float2* table = static_cast<float2*>(ws);
   if (nq::launch_rope_table(positions, T, d, f, table, s) != hipSuccess)
     return NQ_ERR_HIP;

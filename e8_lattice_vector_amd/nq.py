@@ -26,6 +26,7 @@ PARITY_RELAXED = 1
 DTYPE_F16 = 0
 DTYPE_F32 = 1
 PLANE_CODES, PLANE_COSETS, PLANE_SCALES = 0, 1, 2
+ROPE_SCALING_NONE, ROPE_SCALING_LINEAR, ROPE_SCALING_LLAMA3 = 0, 1, 2
 
 EXPORTED = ("nq_packed_bytes", "nq_workspace_bytes", "nq_status_string",
             "nq_quantize_kv", "nq_dequantize_kv", "nq_score_packed_keys",
@@ -36,7 +37,10 @@ class _Config(ctypes.Structure):
     _fields_ = [("head_dim", ctypes.c_int32), ("bits_k", ctypes.c_int32),
                 ("bits_v", ctypes.c_int32), ("scale_group", ctypes.c_int32),
                 ("parity", ctypes.c_int32), ("in_dtype", ctypes.c_int32),
-                ("rope_theta", ctypes.c_double)]
+                ("rope_theta", ctypes.c_double),
+                ("rope_scaling", ctypes.c_int32), ("rope_original_max", ctypes.c_int32),
+                ("rope_factor", ctypes.c_double), ("rope_low_freq_factor", ctypes.c_double),
+                ("rope_high_freq_factor", ctypes.c_double)]
 
 
 class _Packed(ctypes.Structure):
@@ -98,10 +102,37 @@ class Config:
     parity: int = PARITY_RELAXED
     in_dtype: int = DTYPE_F16
     rope_theta: float = 0.0
+    rope_scaling: int = ROPE_SCALING_NONE
+    rope_original_max: int = 0
+    rope_factor: float = 1.0
+    rope_low_freq_factor: float = 1.0
+    rope_high_freq_factor: float = 4.0
 
     def c(self) -> _Config:
         return _Config(self.head_dim, self.bits_k, self.bits_v, self.scale_group,
-                       self.parity, self.in_dtype, float(self.rope_theta))
+                       self.parity, self.in_dtype, float(self.rope_theta),
+                       self.rope_scaling, self.rope_original_max, float(self.rope_factor),
+                       float(self.rope_low_freq_factor), float(self.rope_high_freq_factor))
+
+    @staticmethod
+    def scaling_from_hf(rope_scaling) -> dict:
+        """Config fields for a model config's ``rope_scaling`` dict (None,
+        {"rope_type": "linear", "factor": f} or {"rope_type": "llama3",
+        "factor", "low_freq_factor", "high_freq_factor",
+        "original_max_position_embeddings"})."""
+        if not rope_scaling:
+            return {"rope_scaling": ROPE_SCALING_NONE}
+        kind = rope_scaling.get("rope_type", rope_scaling.get("type"))
+        if kind == "linear":
+            return {"rope_scaling": ROPE_SCALING_LINEAR,
+                    "rope_factor": float(rope_scaling["factor"])}
+        if kind == "llama3":
+            return {"rope_scaling": ROPE_SCALING_LLAMA3,
+                    "rope_factor": float(rope_scaling["factor"]),
+                    "rope_low_freq_factor": float(rope_scaling["low_freq_factor"]),
+                    "rope_high_freq_factor": float(rope_scaling["high_freq_factor"]),
+                    "rope_original_max": int(rope_scaling["original_max_position_embeddings"])}
+        raise ValueError(f"unsupported rope_scaling type {kind!r}")
 
     @property
     def n(self) -> int:

@@ -53,6 +53,7 @@ typedef enum {
 } nq_status;
 
 enum { NQ_PARITY_STRICT = 0, NQ_PARITY_RELAXED = 1 };
+enum { NQ_ROPE_SCALING_NONE = 0, NQ_ROPE_SCALING_LINEAR = 1, NQ_ROPE_SCALING_LLAMA3 = 2 };
 enum { NQ_DTYPE_F16 = 0, NQ_DTYPE_F32 = 1 };
 enum { NQ_PLANE_CODES = 0, NQ_PLANE_COSETS = 1, NQ_PLANE_SCALES = 2 };
 
@@ -74,6 +75,20 @@ enum { NQ_PLANE_CODES = 0, NQ_PLANE_COSETS = 1, NQ_PLANE_SCALES = 2 };
  *              theta^(-2i/d), pair (i, i + d/2)); it is removed before
  *              quantizing and re-applied on dequantize.  0: keys are
  *              quantized as given (the README's "fast" mode, no RoPE removal).
+ *
+ * RoPE frequency scaling ([RM] "API reference": rope_scaling, the model
+ * config's dict, for Llama-3.1 and similar; "Limitations": linear scaling and
+ * Llama-3.1 at long context).  Each frequency w_i = theta^(-2i/d) becomes:
+ *  NQ_ROPE_SCALING_NONE    w_i (the remaining fields are ignored)
+ *  NQ_ROPE_SCALING_LINEAR  w_i / rope_factor
+ *  NQ_ROPE_SCALING_LLAMA3  with wavelength l = 2 pi / w_i and the original
+ *      context C = rope_original_max: w_i where l < C / high_freq_factor;
+ *      w_i / rope_factor where l > C / low_freq_factor; between the two,
+ *      (1 - a) w_i / rope_factor + a w_i with
+ *      a = (C / l - low_freq_factor) / (high_freq_factor - low_freq_factor).
+ * Everything is evaluated in fp64 in that order on the host.  Requirements:
+ * rope_factor > 0; LLAMA3 also 0 < low_freq_factor < high_freq_factor and
+ * rope_original_max > 0; otherwise NQ_ERR_INVALID_ARG.
  */
 typedef struct {
   int32_t head_dim;
@@ -83,6 +98,11 @@ typedef struct {
   int32_t parity;
   int32_t in_dtype;
   double rope_theta;
+  int32_t rope_scaling;          /* NQ_ROPE_SCALING_*                       */
+  int32_t rope_original_max;     /* LLAMA3: original context length C       */
+  double rope_factor;            /* LINEAR, LLAMA3                          */
+  double rope_low_freq_factor;   /* LLAMA3                                  */
+  double rope_high_freq_factor;  /* LLAMA3                                  */
 } nq_config;
 
 /* Packed form of one KV tensor: three device planes, each row-major over the

@@ -68,6 +68,7 @@ class Codec:
     scale_group: int = 0      # 0 -> n (one scale per vector)
     strict: bool = False
     rope_theta: float = 0.0   # > 0: keys have RoPE removed before quantizing
+    rope_scaling: transform.RopeScaling | None = None   # frequency scaling
 
     @property
     def n(self) -> int:
@@ -113,7 +114,7 @@ def compute_y(x, codec: Codec, positions=None, is_key: bool = False):
     if is_key and codec.rope_theta > 0:
         T = x32.shape[-2]
         pos = np.arange(T) if positions is None else np.asarray(positions)
-        c32, s32 = transform.rope_table_f32(pos, codec.rope_theta, d)
+        c32, s32 = transform.rope_table_f32(pos, codec.rope_theta, d, codec.rope_scaling)
         x32 = transform.rope_inverse_f32(x32, c32, s32)
     n = codec.n
     v = np.zeros(x32.shape[:-1] + (n,), dtype=np.float32)
@@ -191,7 +192,7 @@ def dequantize(codes, cosets, scales, codec: Codec, positions=None,
     if is_key and apply_rope and codec.rope_theta > 0:
         T = x.shape[-2]
         pos = np.arange(T) if positions is None else np.asarray(positions)
-        x = transform.rope_forward_f64(x, pos, codec.rope_theta)
+        x = transform.rope_forward_f64(x, pos, codec.rope_theta, codec.rope_scaling)
     return x
 
 

@@ -13,6 +13,15 @@ Sources
   H / sqrt(n).
 * RoPE frequencies omega_i = theta^(-2i/d), the form HF models use with
   ``rope_theta`` from the config (README "API reference", ``rope_base``).
+* Frequency scaling: README "API reference" takes the model config's
+  ``rope_scaling`` dict ("Pass model.config.rope_scaling for Llama-3.1 and
+  similar"); README "Limitations" names linear scaling and Llama-3.1 beyond
+  its original context.  The pages print no formula; we take the published
+  definitions of the two HF types that phrase points at: "linear" divides
+  every frequency by the factor; "llama3" keeps the high-frequency band
+  (wavelength below C / high_freq_factor), divides the low-frequency band
+  (wavelength above C / low_freq_factor) by the factor and interpolates
+  linearly in C / wavelength between them (C = original context length).
 
 fp32 functions (``rope_table_f32``, ``rope_inverse_f32``, ``fwht_f32``) define
 the value y on which the lattice decision is taken: every operation is one
@@ -22,16 +31,22 @@ floating-point outputs (dequantized vectors, scores).
 
 Parity status: pinned (H H^T = nI, fast transform equals the dense product,
 norm preservation, inverse-after-forward RoPE is the identity, position 0 is
-the identity) -- see tests/test_oracle_transform.py.
+the identity; scaling: factor 1 is the identity, linear scaling equals
+unscaled RoPE at position p / factor, llama3 frequencies lie between w/f and
+w, fall monotonically, keep / divide the outer bands and are continuous at
+the band edges) -- see tests/test_oracle_transform.py.
 """
 
 from __future__ import annotations
 
 import math
+from dataclasses import dataclass
 
 import numpy as np
 
 __all__ = [
+    "RopeScaling",
+    "scale_freqs",
     "next_pow2",
     "rope_freqs",
     "rope_angles",
@@ -52,21 +67,61 @@ def next_pow2(d: int) -> int:
     return n
 
 
-def rope_freqs(theta: float, d: int) -> np.ndarray:
-    """omega_i = theta ** (-(2 i) / d), i in [0, d/2), each by C pow()."""
-    return np.array([math.pow(theta, -(2.0 * i) / d) for i in range(d // 2)],
-                    dtype=np.float64)
+@dataclass(frozen=True)
+class RopeScaling:
+    """A model config's rope_scaling: kind "linear" or "llama3"."""
+    kind: str
+    factor: float
+    low_freq_factor: float = 1.0
+    high_freq_factor: float = 4.0
+    original_max: int = 8192
 
 
-def rope_angles(positions, theta: float, d: int) -> np.ndarray:
+def scale_freqs(omega, scaling: RopeScaling | None) -> np.ndarray:
+    """Scaled frequencies, one fp64 operation at a time in the written order.
+
+    linear: w / f.  llama3, with wavelength l = 2 pi / w and C the original
+    context: w if l < C / high; w / f if l > C / low; otherwise
+    (1 - a) w / f + a w with a = (C / l - low) / (high - low)."""
+    omega = np.asarray(omega, dtype=np.float64)
+    if scaling is None:
+        return omega.copy()
+    f = float(scaling.factor)
+    if scaling.kind == "linear":
+        return np.array([w / f for w in omega.tolist()])
+    assert scaling.kind == "llama3", scaling.kind
+    C = float(scaling.original_max)
+    lo, hi = float(scaling.low_freq_factor), float(scaling.high_freq_factor)
+    out = []
+    for w in omega.tolist():
+        wavelen = 2.0 * math.pi / w
+        if wavelen < C / hi:
+            out.append(w)
+        elif wavelen > C / lo:
+            out.append(w / f)
+        else:
+            a = (C / wavelen - lo) / (hi - lo)
+            out.append((1.0 - a) * w / f + a * w)
+    return np.array(out, dtype=np.float64)
+
+
+def rope_freqs(theta: float, d: int, scaling: RopeScaling | None = None) -> np.ndarray:
+    """omega_i = theta ** (-(2 i) / d), i in [0, d/2), each by C pow(), then
+    the frequency scaling."""
+    w = np.array([math.pow(theta, -(2.0 * i) / d) for i in range(d // 2)],
+                 dtype=np.float64)
+    return scale_freqs(w, scaling)
+
+
+def rope_angles(positions, theta: float, d: int, scaling=None) -> np.ndarray:
     """[T, d/2] fp64 angles position * omega_i (one rounded product each)."""
     pos = np.asarray(positions, dtype=np.float64).reshape(-1, 1)
-    return pos * rope_freqs(theta, d)[None, :]
+    return pos * rope_freqs(theta, d, scaling)[None, :]
 
 
-def rope_table_f32(positions, theta: float, d: int):
+def rope_table_f32(positions, theta: float, d: int, scaling=None):
     """cos and sin of the fp64 angles, each rounded once to fp32."""
-    a = rope_angles(positions, theta, d)
+    a = rope_angles(positions, theta, d, scaling)
     return np.cos(a).astype(np.float32), np.sin(a).astype(np.float32)
 
 
@@ -86,22 +141,22 @@ def rope_inverse_f32(x32: np.ndarray, cos32: np.ndarray, sin32: np.ndarray):
     return out
 
 
-def rope_forward_f64(x: np.ndarray, positions, theta: float):
+def rope_forward_f64(x: np.ndarray, positions, theta: float, scaling=None):
     """Apply split-half RoPE in fp64: y_i = x_i c - x_{i+h} s,
     y_{i+h} = x_{i+h} c + x_i s."""
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
-    a = rope_angles(positions, theta, d)
+    a = rope_angles(positions, theta, d, scaling)
     c, s = np.cos(a), np.sin(a)
     h = d // 2
     lo, hi = x[..., :h], x[..., h:]
     return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1)
 
 
-def rope_inverse_f64(x: np.ndarray, positions, theta: float):
+def rope_inverse_f64(x: np.ndarray, positions, theta: float, scaling=None):
     x = np.asarray(x, dtype=np.float64)
     d = x.shape[-1]
-    a = rope_angles(positions, theta, d)
+    a = rope_angles(positions, theta, d, scaling)
     c, s = np.cos(a), np.sin(a)
     h = d // 2
     lo, hi = x[..., :h], x[..., h:]

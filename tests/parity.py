@@ -13,16 +13,27 @@ import math
 import numpy as np
 
 from oracle import codec as oc
-from oracle import lattice
+from oracle import lattice, transform
 
 REGRET_TOL = 1e-6
 EXEMPT_FRAC = 1e-6
 
 
+def oracle_scaling(cfg):
+    """The oracle's RopeScaling for an nq.Config (None when unscaled)."""
+    if cfg.rope_scaling == 1:
+        return transform.RopeScaling("linear", cfg.rope_factor)
+    if cfg.rope_scaling == 2:
+        return transform.RopeScaling("llama3", cfg.rope_factor, cfg.rope_low_freq_factor,
+                                     cfg.rope_high_freq_factor, cfg.rope_original_max)
+    return None
+
+
 def oracle_codec(cfg, is_value: bool) -> oc.Codec:
     return oc.Codec(cfg.head_dim, cfg.bits_v if is_value else cfg.bits_k,
                     cfg.scale_group, cfg.parity == 0,
-                    0.0 if is_value else cfg.rope_theta)
+                    0.0 if is_value else cfg.rope_theta,
+                    None if is_value else oracle_scaling(cfg))
 
 
 def to_np(packed):

@@ -92,3 +92,37 @@ def test_invalid_arguments_rejected_before_launch():
     assert dd(0x1000, 10, 2, 5, 0x2000, 0x3000, None) == -1
     for s in (0, -1, -2, -3, -4, 9):
         assert isinstance(nq.status_string(s), str)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(rope_scaling=3),
+    dict(rope_scaling=-1),
+    dict(rope_scaling=nq.ROPE_SCALING_LINEAR, rope_factor=0.0),
+    dict(rope_scaling=nq.ROPE_SCALING_LINEAR, rope_factor=float("inf")),
+    dict(rope_scaling=nq.ROPE_SCALING_LLAMA3, rope_factor=8.0, rope_original_max=0),
+    dict(rope_scaling=nq.ROPE_SCALING_LLAMA3, rope_factor=8.0, rope_original_max=8192,
+         rope_low_freq_factor=4.0, rope_high_freq_factor=1.0),
+    dict(rope_scaling=nq.ROPE_SCALING_LLAMA3, rope_factor=8.0, rope_original_max=8192,
+         rope_low_freq_factor=0.0),
+])
+def test_invalid_rope_scaling_rejected(kw):
+    c = nq.Config(128, 2, 2, 0, nq.PARITY_RELAXED, nq.DTYPE_F16, 5e5, **kw)
+    assert nq.packed_bytes(c, 0, 1, 0) == 0
+    pk = nq._Packed(0x1000, 0x2000, 0x3000)
+    cc = c.c()
+    st = nq.load().nq_quantize_kv(ctypes.byref(cc), 0x10000, None, 1, 1, 4, None,
+                                  ctypes.byref(pk), None, 0x8000, 1 << 20, None)
+    assert st == nq.NQ_ERR_INVALID_ARG
+
+
+def test_rope_scaling_from_hf_dict():
+    f = nq.Config.scaling_from_hf({"rope_type": "llama3", "factor": 8.0, "low_freq_factor": 1.0,
+                                   "high_freq_factor": 4.0,
+                                   "original_max_position_embeddings": 8192})
+    c = nq.Config(128, 2, 2, 0, 1, 0, 5e5, **f)
+    assert (c.rope_scaling, c.rope_original_max, c.rope_factor) == (nq.ROPE_SCALING_LLAMA3, 8192, 8.0)
+    assert nq.packed_bytes(c, 0, 1, 0) == 32
+    assert nq.Config.scaling_from_hf(None) == {"rope_scaling": nq.ROPE_SCALING_NONE}
+    assert nq.Config.scaling_from_hf({"type": "linear", "factor": 2.0})["rope_factor"] == 2.0
+    with pytest.raises(ValueError):
+        nq.Config.scaling_from_hf({"rope_type": "yarn", "factor": 4.0})

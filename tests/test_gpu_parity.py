@@ -12,9 +12,9 @@ import torch
 
 from e8_lattice_vector_amd import nq, synth, workloads
 from oracle import codec as oc
-from oracle import lattice
+from oracle import lattice, transform
 
-from parity import check_codes, check_dequant, check_scores, oracle_codec, to_np
+from parity import check_codes, check_dequant, check_scores, oracle_codec, oracle_scaling, to_np
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -41,12 +41,23 @@ CASES = [
     ("d80-g16-strict", nq.Config(80, 2, 2, 16, S_, F16, 1e4), 1, 2, 95, False),
     ("d16-g8", nq.Config(16, 2, 3, 8, S_, F16, 0.0), 3, 1, 50, False),
     ("single-token", nq.Config(128, 2, 2, 0, S_, F16, 5e5), 1, 1, 1, True),
+    # Llama-3.1 frequency scaling (factor 8, bands 1 / 4, 8192 original
+    # context) at positions up to 65535; linear scaling by 4
+    ("llama31-rope-scaled", nq.Config(128, 2, 2, 0, R_, F16, 5e5, nq.ROPE_SCALING_LLAMA3,
+                                      8192, 8.0, 1.0, 4.0), 2, 2, 700, True),
+    ("linear-rope-scaled", nq.Config(64, 3, 2, 32, S_, F16, 1e4, nq.ROPE_SCALING_LINEAR,
+                                     0, 4.0), 1, 3, 211, True),
 ]
 
 
-def _inputs(cfg, S, H, T, seed, scale=1.0):
+def _inputs(cfg, S, H, T, seed, scale=1.0, pos=None):
+    """K carries RoPE with the config's (scaled) frequencies at `pos`."""
     dt = cfg.torch_dtype
-    k = synth.kv("k", S, H, T, cfg.head_dim, cfg.rope_theta, seed, DEV, torch.float32)
+    omega = None
+    if cfg.rope_theta > 0 and cfg.rope_scaling:
+        omega = transform.rope_freqs(cfg.rope_theta, cfg.head_dim, oracle_scaling(cfg))
+    k = synth.kv("k", S, H, T, cfg.head_dim, cfg.rope_theta, seed, DEV, torch.float32,
+                 omega=omega, positions=pos)
     v = synth.kv("v", S, H, T, cfg.head_dim, 0.0, seed, DEV, torch.float32)
     return (k * scale).to(dt).contiguous(), (v * scale).to(dt).contiguous()
 
@@ -61,8 +72,8 @@ def _positions(T, explicit):
 def _run_case(name, cfg, S, H, T, explicit, seed=0, scale=1.0):
     log(f"[case] {name} S={S} H={H} T={T} d={cfg.head_dim} bits={cfg.bits_k}/{cfg.bits_v} "
         f"G={cfg.scale_group} parity={cfg.parity} scale={scale}")
-    k, v = _inputs(cfg, S, H, T, seed, scale)
     pos_t, pos = _positions(T, explicit)
+    k, v = _inputs(cfg, S, H, T, seed, scale, pos)
     pk, pv = nq.quantize_kv(cfg, k, v, positions=pos_t)
     kd, vd = nq.dequantize_kv(cfg, pk, pv, S, H, T, positions=pos_t)
     torch.cuda.synchronize()

@@ -73,3 +73,61 @@ def test_rope_roundtrip_and_invariants(d, theta):
     assert np.max(np.abs(got - ref)) < 4 * 2.0 ** -24 * np.abs(y32).max() * 2
     c0, s0 = transform.rope_table_f32([0], theta, d)
     assert np.all(c0 == 1) and np.all(s0 == 0)
+
+
+LLAMA31 = transform.RopeScaling("llama3", 8.0, 1.0, 4.0, 8192)
+
+
+def test_rope_scaling_factor_one_is_identity():
+    w = transform.rope_freqs(5e5, 128)
+    assert np.array_equal(transform.rope_freqs(5e5, 128, transform.RopeScaling("linear", 1.0)), w)
+    one = transform.RopeScaling("llama3", 1.0, 1.0, 4.0, 8192)
+    np.testing.assert_allclose(transform.rope_freqs(5e5, 128, one), w, rtol=2e-16)
+
+
+def test_linear_scaling_is_position_division():
+    """RoPE with linear factor f at position p equals unscaled RoPE at p / f."""
+    rng = np.random.default_rng(1)
+    x = rng.normal(size=(3, 40, 64))
+    pos = np.arange(40) * 4 + 8000
+    lin = transform.RopeScaling("linear", 4.0)
+    a = transform.rope_forward_f64(x, pos, 1e4, lin)
+    b = transform.rope_forward_f64(x, pos // 4, 1e4)
+    np.testing.assert_allclose(a, b, atol=1e-9)
+    np.testing.assert_allclose(transform.rope_inverse_f64(a, pos, 1e4, lin), x, atol=1e-12)
+
+
+def test_llama3_scaling_bands():
+    """Llama-3.1-8B: theta 5e5, d 128, factor 8, low 1, high 4, C 8192.
+    By hand: w_i > 2 pi / 2048 (kept) for i <= 28, w_i < 2 pi / 8192
+    (divided by 8) for i >= 35, i = 29..34 in between."""
+    w = transform.rope_freqs(5e5, 128)
+    ws = transform.rope_freqs(5e5, 128, LLAMA31)
+    assert np.array_equal(ws[:29], w[:29])
+    assert np.array_equal(ws[35:], w[35:] / 8.0)
+    mid = ws[29:35] / w[29:35]
+    assert np.all((mid > 1 / 8) & (mid < 1))
+    # between w / f and w, and falling with i like the unscaled frequencies
+    assert np.all(ws <= w) and np.all(ws >= w / 8)
+    assert np.all(np.diff(ws) < 0)
+    # the ratio w'/w falls monotonically across the middle band
+    assert np.all(np.diff(mid) < 0)
+
+
+def test_llama3_scaling_continuous_at_band_edges():
+    """At wavelength C / high the scaled frequency is w itself, at C / low it
+    is w / f, approached from either side."""
+    s = LLAMA31
+    w_hi = 2 * math.pi * s.high_freq_factor / s.original_max   # edge of the kept band
+    w_lo = 2 * math.pi * s.low_freq_factor / s.original_max    # edge of the divided band
+    eps = 1e-9
+    out = transform.scale_freqs([w_hi * (1 + eps), w_hi * (1 - eps),
+                                 w_lo * (1 + eps), w_lo * (1 - eps)], s)
+    np.testing.assert_allclose(out[:2], w_hi, rtol=1e-7)
+    np.testing.assert_allclose(out[2:], w_lo / s.factor, rtol=1e-7)
+    # scaling then inverting the rotation is the identity
+    rng = np.random.default_rng(2)
+    x = rng.normal(size=(2, 30, 128))
+    pos = np.arange(30) + 60000
+    y = transform.rope_forward_f64(x, pos, 5e5, s)
+    np.testing.assert_allclose(transform.rope_inverse_f64(y, pos, 5e5, s), x, atol=1e-12)
