@@ -69,13 +69,42 @@ size_t rope_bytes(const nq_config* c, int64_t T) {
   return (b + 255) & ~(size_t)255;
 }
 
-int check_packed(const nq_packed* p) {
+constexpr int64_t kMaxTokens = (int64_t)1 << 40;
+
+// Pointers, alignment and the token window [token_offset, token_offset + T)
+// of a call inside planes of token_capacity tokens per (slab, head).
+int check_packed(const nq_packed* p, int64_t T) {
   if (p == nullptr || p->codes == nullptr || p->cosets == nullptr ||
       p->scales == nullptr)
     return NQ_ERR_INVALID_ARG;
   if (!aligned16(p->codes) || !aligned16(p->cosets) || !aligned16(p->scales))
     return NQ_ERR_INVALID_ARG;
+  if (p->token_offset < 0 || p->token_offset > kMaxTokens || p->token_capacity < 0 ||
+      p->token_capacity > kMaxTokens)
+    return NQ_ERR_INVALID_ARG;
+  if (p->token_capacity != 0 && p->token_offset + T > p->token_capacity)
+    return NQ_ERR_INVALID_ARG;
   return NQ_OK;
+}
+
+// The call's window: plane token stride and plane bases advanced to the
+// window's first token (the same shift as starting at a later vector, so the
+// kernels' alignment assumptions still hold).
+struct PackedView {
+  uint8_t* codes;
+  uint8_t* cosets;
+  uint16_t* scales;
+  int64_t pT, t0;
+};
+
+PackedView packed_view(const nq_packed* p, const Layout& l, int64_t T) {
+  PackedView v;
+  v.t0 = p->token_offset;
+  v.pT = p->token_capacity != 0 ? p->token_capacity : p->token_offset + T;
+  v.codes = static_cast<uint8_t*>(p->codes) + v.t0 * l.code_bytes;
+  v.cosets = static_cast<uint8_t*>(p->cosets) + v.t0 * l.coset_bytes;
+  v.scales = static_cast<uint16_t*>(p->scales) + v.t0 * l.n_scales;
+  return v;
 }
 
 int check_shape(int64_t S, int32_t H, int64_t T) {
@@ -89,11 +118,13 @@ nq::TensorArgs tensor_args(const nq_config* c, const Layout& l, int64_t S,
                            int32_t H, int64_t T, const nq_packed* p) {
   nq::TensorArgs a;
   memset(&a, 0, sizeof(a));
-  a.codes = static_cast<uint8_t*>(p->codes);
-  a.cosets = static_cast<uint8_t*>(p->cosets);
-  a.scales = static_cast<uint16_t*>(p->scales);
+  const PackedView pv = packed_view(p, l, T);
+  a.codes = pv.codes;
+  a.cosets = pv.cosets;
+  a.scales = pv.scales;
   a.n_vec = S * (int64_t)H * T;
   a.T = T;
+  a.pT = pv.pT;
   a.d = l.d;
   a.n = l.n;
   a.G = l.G;
@@ -126,7 +157,7 @@ double rope_freq(const nq_config* c, int i) {
 }
 
 // Builds the cos/sin table in the workspace when keys need RoPE.
-int prepare_rope(const nq_config* c, int64_t T, const int32_t* positions,
+int prepare_rope(const nq_config* c, int64_t T, const int32_t* positions, int64_t pos0,
                  void* ws, size_t ws_bytes, hipStream_t s, const float2** out) {
   *out = nullptr;
   const size_t need = rope_bytes(c, T);
@@ -137,7 +168,7 @@ int prepare_rope(const nq_config* c, int64_t T, const int32_t* positions,
   const int d = c->head_dim;
   for (int i = 0; i < d / 2; ++i) f.omega[i] = rope_freq(c, i);
   float2* table = static_cast<float2*>(ws);
-  if (nq::launch_rope_table(positions, T, d, f, table, s) != hipSuccess)
+  if (nq::launch_rope_table(positions, pos0, T, d, f, table, s) != hipSuccess)
     return NQ_ERR_HIP;
   *out = table;
   return NQ_OK;
@@ -183,15 +214,15 @@ int nq_quantize_kv(const nq_config* cfg, const void* k, const void* v,
   if (st != NQ_OK) return st;
   if ((st = check_shape(S, H, T)) != NQ_OK) return st;
   if (k == nullptr && v == nullptr) return NQ_ERR_INVALID_ARG;
-  if (k != nullptr && (!aligned16(k) || (st = check_packed(pk)) != NQ_OK))
+  if (k != nullptr && (!aligned16(k) || (st = check_packed(pk, T)) != NQ_OK))
     return st != NQ_OK ? st : NQ_ERR_INVALID_ARG;
-  if (v != nullptr && (!aligned16(v) || (st = check_packed(pv)) != NQ_OK))
+  if (v != nullptr && (!aligned16(v) || (st = check_packed(pv, T)) != NQ_OK))
     return st != NQ_OK ? st : NQ_ERR_INVALID_ARG;
   if (positions != nullptr && !aligned16(positions)) return NQ_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float2* rope = nullptr;
   if (k != nullptr) {
-    if ((st = prepare_rope(cfg, T, positions, ws, ws_bytes, s, &rope)) != NQ_OK)
+    if ((st = prepare_rope(cfg, T, positions, pk->token_offset, ws, ws_bytes, s, &rope)) != NQ_OK)
       return st;
     nq::TensorArgs a = tensor_args(cfg, layout(cfg, 0), S, H, T, pk);
     a.x = k;
@@ -214,15 +245,15 @@ int nq_dequantize_kv(const nq_config* cfg, const nq_packed* pk,
   if (st != NQ_OK) return st;
   if ((st = check_shape(S, H, T)) != NQ_OK) return st;
   if (k_out == nullptr && v_out == nullptr) return NQ_ERR_INVALID_ARG;
-  if (k_out != nullptr && (!aligned16(k_out) || (st = check_packed(pk)) != NQ_OK))
+  if (k_out != nullptr && (!aligned16(k_out) || (st = check_packed(pk, T)) != NQ_OK))
     return st != NQ_OK ? st : NQ_ERR_INVALID_ARG;
-  if (v_out != nullptr && (!aligned16(v_out) || (st = check_packed(pv)) != NQ_OK))
+  if (v_out != nullptr && (!aligned16(v_out) || (st = check_packed(pv, T)) != NQ_OK))
     return st != NQ_OK ? st : NQ_ERR_INVALID_ARG;
   if (positions != nullptr && !aligned16(positions)) return NQ_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (k_out != nullptr) {
     const float2* rope = nullptr;
-    if ((st = prepare_rope(cfg, T, positions, ws, ws_bytes, s, &rope)) != NQ_OK)
+    if ((st = prepare_rope(cfg, T, positions, pk->token_offset, ws, ws_bytes, s, &rope)) != NQ_OK)
       return st;
     nq::TensorArgs a = tensor_args(cfg, layout(cfg, 0), S, H, T, pk);
     a.y = k_out;
@@ -248,20 +279,22 @@ int nq_score_packed_keys(const nq_config* cfg, const nq_packed* pk, int64_t S,
   if ((st = check_shape(S, H, T)) != NQ_OK) return st;
   if (Hq <= 0 || Hq % H != 0) return NQ_ERR_INVALID_ARG;
   if (S > 65535 || H > 65535) return NQ_ERR_UNSUPPORTED;
-  if ((st = check_packed(pk)) != NQ_OK) return st;
+  if ((st = check_packed(pk, T)) != NQ_OK) return st;
   if (q == nullptr || scores == nullptr || !aligned16(q) || !aligned16(scores))
     return NQ_ERR_INVALID_ARG;
   const Layout l = layout(cfg, 0);
   if ((size_t)(Hq / H) * l.n * sizeof(float) > 64 * 1024) return NQ_ERR_UNSUPPORTED;
   nq::ScoreArgs a;
   memset(&a, 0, sizeof(a));
-  a.codes = static_cast<const uint8_t*>(pk->codes);
-  a.cosets = static_cast<const uint8_t*>(pk->cosets);
-  a.scales = static_cast<const uint16_t*>(pk->scales);
+  const PackedView pv = packed_view(pk, l, T);
+  a.codes = pv.codes;
+  a.cosets = pv.cosets;
+  a.scales = pv.scales;
   a.q = q;
   a.out = scores;
   a.S = S;
   a.T = T;
+  a.pT = pv.pT;
   a.H = H;
   a.Hq = Hq;
   a.d = l.d;
@@ -286,19 +319,21 @@ int nq_attend_packed_values(const nq_config* cfg, const nq_packed* pv,
   if ((st = check_shape(S, H, T)) != NQ_OK) return st;
   if (Hq <= 0 || Hq % H != 0) return NQ_ERR_INVALID_ARG;
   if (S > 65535 || (int64_t)H * ((Hq / H + 3) / 4 + 1) > 65535) return NQ_ERR_UNSUPPORTED;
-  if ((st = check_packed(pv)) != NQ_OK) return st;
+  if ((st = check_packed(pv, T)) != NQ_OK) return st;
   if (weights == nullptr || out == nullptr || !aligned16(weights) || !aligned16(out))
     return NQ_ERR_INVALID_ARG;
   const Layout l = layout(cfg, 1);
   nq::AttendArgs a;
   memset(&a, 0, sizeof(a));
-  a.codes = static_cast<const uint8_t*>(pv->codes);
-  a.cosets = static_cast<const uint8_t*>(pv->cosets);
-  a.scales = static_cast<const uint16_t*>(pv->scales);
+  const PackedView view = packed_view(pv, l, T);
+  a.codes = view.codes;
+  a.cosets = view.cosets;
+  a.scales = view.scales;
   a.w = weights;
   a.out = out;
   a.S = S;
   a.T = T;
+  a.pT = view.pT;
   a.H = H;
   a.Hq = Hq;
   a.d = l.d;

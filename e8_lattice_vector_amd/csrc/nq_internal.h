@@ -16,7 +16,9 @@ struct TensorArgs {
   uint16_t* scales;     // fp16 bits
   const float2* rope;   // [T][d/2] (cos, sin), or nullptr: no RoPE step
   int64_t n_vec;        // S * H * T
-  int64_t T;
+  int64_t T;            // tokens of this call (dense x / y planes hold T)
+  int64_t pT;           // token stride of the packed planes (>= T); the plane
+                        // bases already point at the call's first token
   int d, n, G, bits, strict, code_bytes, coset_bytes, n_scales;
   float eps;            // fp32(1e-8 * sqrt(n)): floor of the group maximum of |H v|
   float half_L;         // L / 2
@@ -31,6 +33,7 @@ struct ScoreArgs {
   const void* q;        // [S][Hq][d]
   float* out;           // [S][Hq][T]
   int64_t S, T;
+  int64_t pT;           // token stride of the packed planes (>= T)
   int H, Hq, d, n, G, bits, code_bytes, coset_bytes, n_scales;
   float half_L;
   float inv_sqrt_n;
@@ -43,6 +46,7 @@ struct AttendArgs {
   const float* w;       // [S][Hq][T]
   float* out;           // [S][Hq][d]
   int64_t S, T;
+  int64_t pT;           // token stride of the packed planes (>= T)
   int H, Hq, d, n, G, bits, code_bytes, coset_bytes, n_scales;
   float half_L;
   float inv_sqrt_n;
@@ -53,8 +57,9 @@ struct RopeFreqs {
   double omega[kMaxHalfDim];  // theta^(-2i/d), computed on the host
 };
 
-hipError_t launch_rope_table(const int32_t* positions, int64_t T, int d,
-                             const RopeFreqs& f, float2* table,
+// positions[t], or pos0 + t when positions is null
+hipError_t launch_rope_table(const int32_t* positions, int64_t pos0, int64_t T,
+                             int d, const RopeFreqs& f, float2* table,
                              hipStream_t stream);
 hipError_t launch_quantize(const TensorArgs& a, int in_dtype, hipStream_t s);
 hipError_t launch_dequantize(const TensorArgs& a, int out_dtype, hipStream_t s);

@@ -610,9 +610,9 @@ __global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
   const uint32_t off_s = (uint32_t)(tc * a.coset_bytes);
   const uint32_t off_g = (uint32_t)(tc * a.n_scales) + (uint32_t)(m / gl);
   const int64_t plane_x = a.T * a.d * (int64_t)sizeof(InT);
-  const int64_t plane_c = a.T * a.code_bytes;
-  const int64_t plane_s = a.T * a.coset_bytes;
-  const int64_t plane_g = a.T * a.n_scales;
+  const int64_t plane_c = a.pT * a.code_bytes;
+  const int64_t plane_s = a.pT * a.coset_bytes;
+  const int64_t plane_g = a.pT * a.n_scales;
   const uint32_t off_gb = (off_g + (uint32_t)mg * (uint32_t)plane_g) * 2u;
   float keep = 0.f;
   // uniform plane bases in scalar registers, lane offsets in 32-bit vector
@@ -732,10 +732,9 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(TensorArgs a) {
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = 0.f;
   }
-  if (a.rope != nullptr) {
-    const int64_t t = vv % a.T;
-    rope_lane<true>(v, m, a.d, a.rope + t * (a.d >> 1));
-  }
+  const int64_t t = vv % a.T;
+  const int64_t pvec = (vv - t) / a.T * a.pT + t;   // index in the packed planes
+  if (a.rope != nullptr) rope_lane<true>(v, m, a.d, a.rope + t * (a.d >> 1));
   fwht_lane(v);
   fwht_cross<VL>(v, m);
   float mx = 0.f;
@@ -753,7 +752,7 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(TensorArgs a) {
   e8_decode<BITS, STRICT>(y, code, c);
   const uint64_t bal = __ballot(c);
   if (!live) return;
-  uint8_t* cp = a.codes + vec * a.code_bytes + m * BITS;
+  uint8_t* cp = a.codes + pvec * a.code_bytes + m * BITS;
   if (BITS == 2) {
     *reinterpret_cast<uint16_t*>(cp) = (uint16_t)code;
   } else {
@@ -765,11 +764,11 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(TensorArgs a) {
     const int lane = threadIdx.x & 63;
     const uint32_t bits = (uint32_t)(bal >> lane) &
                           (VL >= 32 ? 0xffffffffu : ((1u << VL) - 1u));
-    uint8_t* q = a.cosets + vec * a.coset_bytes;
+    uint8_t* q = a.cosets + pvec * a.coset_bytes;
     for (int b = 0; b < a.coset_bytes; ++b) q[b] = (uint8_t)(bits >> (8 * b));
   }
   if (m % gl == 0) {
-    a.scales[vec * a.n_scales + m / gl] = f64_to_f16_rn((double)amax * a.sigma_k);
+    a.scales[pvec * a.n_scales + m / gl] = f64_to_f16_rn((double)amax * a.sigma_k);
   }
 }
 
@@ -876,15 +875,15 @@ __global__ __launch_bounds__(kBlock) void dequantize_fast_kernel(TensorArgs a,
     }
     cbyte = a.cosets[vec * a.coset_bytes + (m >> 3)];
     sbits = a.scales[vec * a.n_scales + m / gl];
-  };
+  };  // `vec` indexes the packed planes (token stride pT)
   uint32_t code_n, cbyte_n;
   uint16_t sbits_n;
-  load_meta(sh0 * a.T + tc, code_n, cbyte_n, sbits_n);
+  load_meta(sh0 * a.pT + tc, code_n, cbyte_n, sbits_n);
   for (int64_t sh = sh0; sh < sh1; ++sh) {
     const int64_t vec = sh * a.T + tc;
     const uint32_t code = code_n, cbyte = cbyte_n;
     const uint16_t sbits = sbits_n;
-    if (sh + 1 < sh1) load_meta(vec + a.T, code_n, cbyte_n, sbits_n);
+    if (sh + 1 < sh1) load_meta((sh + 1) * a.pT + tc, code_n, cbyte_n, sbits_n);
     const int c = (int)((cbyte >> (m & 7)) & 1u);
     const float sc = h2f(sbits) * a.inv_sqrt_n;
     const float off = (0.5f * (float)c - a.half_L) * sc;
@@ -931,16 +930,18 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(TensorArgs a) {
   const int64_t vec = (int64_t)blockIdx.x * VPB + threadIdx.x / VL;
   const bool live = vec < a.n_vec;
   const int64_t vv = live ? vec : 0;
-  const uint8_t* cp = a.codes + vv * a.code_bytes + m * BITS;
+  const int64_t t = vv % a.T;
+  const int64_t pvec = (vv - t) / a.T * a.pT + t;   // index in the packed planes
+  const uint8_t* cp = a.codes + pvec * a.code_bytes + m * BITS;
   uint32_t code;
   if (BITS == 2) {
     code = *reinterpret_cast<const uint16_t*>(cp);
   } else {
     code = (uint32_t)cp[0] | ((uint32_t)cp[1] << 8) | ((uint32_t)cp[2] << 16);
   }
-  const int c = (a.cosets[vv * a.coset_bytes + (m >> 3)] >> (m & 7)) & 1;
+  const int c = (a.cosets[pvec * a.coset_bytes + (m >> 3)] >> (m & 7)) & 1;
   const int gl = a.G >> 3;
-  const float s = h2f(a.scales[vv * a.n_scales + m / gl]) * a.inv_sqrt_n;
+  const float s = h2f(a.scales[pvec * a.n_scales + m / gl]) * a.inv_sqrt_n;
   const float off = 0.5f * (float)c - a.half_L;
   float v[8];
 #pragma unroll
@@ -950,10 +951,7 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(TensorArgs a) {
   }
   fwht_lane(v);
   fwht_cross<VL>(v, m);
-  if (a.rope != nullptr) {
-    const int64_t t = vv % a.T;
-    rope_lane<false>(v, m, a.d, a.rope + t * (a.d >> 1));
-  }
+  if (a.rope != nullptr) rope_lane<false>(v, m, a.d, a.rope + t * (a.d >> 1));
   const int j0 = 8 * m;
   if (live && j0 < a.d) Io<OutT>::store8(a.y, vec * a.d + j0, v);
 }
@@ -991,7 +989,7 @@ __global__ __launch_bounds__(kBlock) void score_kernel(ScoreArgs a) {
   const int gl = a.G >> 3;
   for (int64_t t = (int64_t)blockIdx.x * kScoreKeys + threadIdx.x; t < t_end;
        t += blockDim.x) {
-    const int64_t vec = (s * a.H + h) * a.T + t;
+    const int64_t vec = (s * a.H + h) * a.pT + t;   // packed planes: token stride pT
     uint8_t cb[CB];
     const uint8_t* cp = a.codes + vec * a.code_bytes;
 #pragma unroll
@@ -1136,7 +1134,7 @@ __global__ __launch_bounds__(kLutBlock) void score_lut_kernel(ScoreArgs a,
   const int ns = NG / gl;                  // scale groups per key
   const int64_t t0 = (int64_t)blockIdx.x * chunk;
   const int64_t t1 = min(a.T, t0 + chunk);
-  const int64_t base = (s * a.H + h) * a.T;
+  const int64_t base = (s * a.H + h) * a.pT;   // packed planes: token stride pT
   for (int64_t t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
     const int64_t vec = base + t;
     uint32_t cw[CB / 4 + 1];
@@ -1224,7 +1222,7 @@ __global__ __launch_bounds__(kAttBlock) void attend_kernel(AttendArgs a, int n_p
 #pragma unroll
     for (int k = 0; k < 8; ++k) acc[g][k] = 0.f;
   }
-  const int64_t base = (s * a.H + h) * a.T;
+  const int64_t base = (s * a.H + h) * a.pT;   // packed planes: token stride pT
   const float* wrow = a.w + (s * a.Hq + hq0) * a.T;
   const int64_t stride = (int64_t)nw * KPW;
   // U keys per row per step, all loads issued before any use so that U
@@ -1331,12 +1329,12 @@ __global__ __launch_bounds__(kBlock) void decode_debug_kernel(
 }
 
 __global__ __launch_bounds__(kBlock) void rope_table_kernel(
-    const int32_t* pos, int64_t T, int h, RopeFreqs f, float2* table) {
+    const int32_t* pos, int64_t pos0, int64_t T, int h, RopeFreqs f, float2* table) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= T * h) return;
   const int64_t t = i / h;
   const int k = (int)(i % h);
-  const double p = pos ? (double)pos[t] : (double)t;
+  const double p = pos ? (double)pos[t] : (double)(pos0 + t);
   const double ang = p * f.omega[k];
   double sn, cs;
   sincos(ang, &sn, &cs);
@@ -1380,7 +1378,8 @@ hipError_t quantize_fast_rope(const TensorArgs& a, hipStream_t s) {
 template <int N, int BITS, typename T>
 hipError_t quantize_n(const TensorArgs& a, hipStream_t s) {
   if constexpr (N <= 128) {
-    if (a.T * a.d * (int64_t)sizeof(T) < ((int64_t)1 << 31))
+    // per-lane byte offsets are 32-bit, in the dense planes and the packed ones
+    if (max(a.T, a.pT) * a.d * (int64_t)sizeof(T) < ((int64_t)1 << 31))
       return a.strict ? quantize_fast_rope<N, BITS, true, T>(a, s)
                       : quantize_fast_rope<N, BITS, false, T>(a, s);
   }
@@ -1559,14 +1558,14 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
 namespace {
 }  // namespace
 
-hipError_t launch_rope_table(const int32_t* positions, int64_t T, int d,
-                             const RopeFreqs& f, float2* table,
+hipError_t launch_rope_table(const int32_t* positions, int64_t pos0, int64_t T,
+                             int d, const RopeFreqs& f, float2* table,
                              hipStream_t stream) {
   const int h = d / 2;
   const int64_t total = T * h;
   const int64_t blocks = (total + kBlock - 1) / kBlock;
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(kBlock), 0,
-                     stream, positions, T, h, f, table);
+                     stream, positions, pos0, T, h, f, table);
   return hipGetLastError();
 }
 

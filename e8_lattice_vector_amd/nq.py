@@ -45,7 +45,8 @@ class _Config(ctypes.Structure):
 
 class _Packed(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("cosets", ctypes.c_void_p),
-                ("scales", ctypes.c_void_p)]
+                ("scales", ctypes.c_void_p), ("token_capacity", ctypes.c_int64),
+                ("token_offset", ctypes.c_int64)]
 
 
 class NQError(RuntimeError):
@@ -148,13 +149,19 @@ class Config:
 
 @dataclass
 class Packed:
+    """Three planes shaped [S][H][capacity][bytes]; a call covers the token
+    window [token_offset, token_offset + T) of every (slab, head) plane."""
     codes: torch.Tensor
     cosets: torch.Tensor
     scales: torch.Tensor
 
-    def c(self) -> _Packed:
+    @property
+    def capacity(self) -> int:
+        return self.codes.shape[2]
+
+    def c(self, token_offset: int = 0) -> _Packed:
         return _Packed(self.codes.data_ptr(), self.cosets.data_ptr(),
-                       self.scales.data_ptr())
+                       self.scales.data_ptr(), self.capacity, int(token_offset))
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in (self.codes, self.cosets, self.scales))
@@ -205,8 +212,9 @@ def alloc_workspace(cfg: Config, T: int, device):
 
 
 def quantize_kv(cfg: Config, k, v, positions=None, pk: Packed | None = None,
-                pv: Packed | None = None, workspace=None, stream=None):
-    """Quantize + pack K and/or V ([S][H][T][d] device tensors)."""
+                pv: Packed | None = None, workspace=None, stream=None, token_offset: int = 0):
+    """Quantize + pack K and/or V ([S][H][T][d] device tensors) into tokens
+    [token_offset, token_offset + T) of the packed planes."""
     ref = k if k is not None else v
     S, H, T, d = ref.shape
     if d != cfg.head_dim:
@@ -216,16 +224,16 @@ def quantize_kv(cfg: Config, k, v, positions=None, pk: Packed | None = None,
                               or tuple(t.shape) != (S, H, T, d)):
             raise NQError(NQ_ERR_INVALID_ARG, "quantize_kv tensor")
     if k is not None and pk is None:
-        pk = alloc_packed(cfg, False, S, H, T, k.device)
+        pk = alloc_packed(cfg, False, S, H, token_offset + T, k.device)
     if v is not None and pv is None:
-        pv = alloc_packed(cfg, True, S, H, T, v.device)
+        pv = alloc_packed(cfg, True, S, H, token_offset + T, v.device)
     if workspace is None and k is not None:
         workspace = alloc_workspace(cfg, T, ref.device)
     if positions is not None and (positions.dtype != torch.int32 or positions.numel() != T):
         raise NQError(NQ_ERR_INVALID_ARG, "quantize_kv positions")
     cc = cfg.c()
-    ck = pk.c() if pk is not None else None
-    cv = pv.c() if pv is not None else None
+    ck = pk.c(token_offset) if k is not None else None
+    cv = pv.c(token_offset) if v is not None else None
     st = load().nq_quantize_kv(
         ctypes.byref(cc), _ptr(k), _ptr(v), S, H, T, _ptr(positions),
         ctypes.byref(ck) if ck is not None else None,
@@ -237,7 +245,8 @@ def quantize_kv(cfg: Config, k, v, positions=None, pk: Packed | None = None,
 
 def dequantize_kv(cfg: Config, pk: Packed | None, pv: Packed | None, S: int, H: int,
                   T: int, positions=None, k_out=None, v_out=None, workspace=None,
-                  stream=None):
+                  stream=None, token_offset: int = 0):
+    """Dequantize tokens [token_offset, token_offset + T) -> [S][H][T][d]."""
     dev = (pk if pk is not None else pv).codes.device
     shape = (S, H, T, cfg.head_dim)
     if pk is not None and k_out is None:
@@ -247,8 +256,8 @@ def dequantize_kv(cfg: Config, pk: Packed | None, pv: Packed | None, S: int, H: 
     if workspace is None and pk is not None:
         workspace = alloc_workspace(cfg, T, dev)
     cc = cfg.c()
-    ck = pk.c() if pk is not None else None
-    cv = pv.c() if pv is not None else None
+    ck = pk.c(token_offset) if pk is not None else None
+    cv = pv.c(token_offset) if pv is not None else None
     st = load().nq_dequantize_kv(
         ctypes.byref(cc), ctypes.byref(ck) if ck is not None else None,
         ctypes.byref(cv) if cv is not None else None, S, H, T, _ptr(positions),
@@ -259,15 +268,16 @@ def dequantize_kv(cfg: Config, pk: Packed | None, pv: Packed | None, S: int, H: 
 
 
 def score_packed_keys(cfg: Config, pk: Packed, q, S: int, H: int, T: int,
-                      scores=None, stream=None):
-    """q: [S][Hq][d] device tensor -> fp32 scores [S][Hq][T]."""
+                      scores=None, stream=None, token_offset: int = 0):
+    """q: [S][Hq][d] device tensor -> fp32 scores [S][Hq][T] against keys
+    [token_offset, token_offset + T)."""
     Hq = q.shape[1]
     if q.dtype != cfg.torch_dtype or not q.is_contiguous() or q.shape != (S, Hq, cfg.head_dim):
         raise NQError(NQ_ERR_INVALID_ARG, "score_packed_keys q")
     if scores is None:
         scores = torch.empty((S, Hq, T), dtype=torch.float32, device=q.device)
     cc = cfg.c()
-    ck = pk.c()
+    ck = pk.c(token_offset)
     st = load().nq_score_packed_keys(ctypes.byref(cc), ctypes.byref(ck), S, H, Hq, T,
                                      q.data_ptr(), scores.data_ptr(), None, 0,
                                      _stream(stream))
@@ -276,8 +286,9 @@ def score_packed_keys(cfg: Config, pk: Packed, q, S: int, H: int, T: int,
 
 
 def attend_packed_values(cfg: Config, pv: Packed, weights, S: int, H: int, T: int,
-                         out=None, stream=None):
-    """weights: fp32 [S][Hq][T] device tensor -> fp32 [S][Hq][d] sum_t w_t * V_t."""
+                         out=None, stream=None, token_offset: int = 0):
+    """weights: fp32 [S][Hq][T] device tensor -> fp32 [S][Hq][d] sum_t w_t * V_t
+    over values [token_offset, token_offset + T)."""
     Hq = weights.shape[1]
     if (weights.dtype != torch.float32 or not weights.is_contiguous()
             or tuple(weights.shape) != (S, Hq, T)):
@@ -285,7 +296,7 @@ def attend_packed_values(cfg: Config, pv: Packed, weights, S: int, H: int, T: in
     if out is None:
         out = torch.empty((S, Hq, cfg.head_dim), dtype=torch.float32, device=weights.device)
     cc = cfg.c()
-    cv = pv.c()
+    cv = pv.c(token_offset)
     st = load().nq_attend_packed_values(ctypes.byref(cc), ctypes.byref(cv), S, H, Hq, T,
                                         weights.data_ptr(), out.data_ptr(), _stream(stream))
     _check(st, "nq_attend_packed_values")

@@ -105,20 +105,31 @@ typedef struct {
   double rope_high_freq_factor;  /* LLAMA3                                  */
 } nq_config;
 
-/* Packed form of one KV tensor: three device planes, each row-major over the
- * S*H*T vectors ([Walk] "Bit Rate Accounting": b bits per coordinate plus a
- * 16-bit scale; one coset bit per 8-group is added so both cosets fit):
+/* Packed form of one KV tensor: three device planes, each row-major over
+ * [S][H][token_capacity] vectors ([Walk] "Bit Rate Accounting": b bits per
+ * coordinate plus a 16-bit scale; one coset bit per 8-group is added so both
+ * cosets fit):
  *   codes  : n*b/8 bytes per vector; coordinate j at bits [j*b, j*b+b) of the
  *            vector's little-endian bit stream, value idx = p - c/2 + L/2
  *   cosets : ceil(n/64) bytes per vector; bit m = 1 when 8-group m lies on
  *            the half-integer coset
  *   scales : n/G fp16 per vector, sigma = max|z| / (L/2) over the group, z the
  *            orthonormally rotated vector
- * The three pointers must be 16-byte aligned; sizes from nq_packed_bytes. */
+ * The three pointers must be 16-byte aligned; sizes from nq_packed_bytes for
+ * S * H * token_capacity vectors.
+ *
+ * Token window (decode-time append, [RM] "HuggingFace ecosystem": the cache
+ * keeps growing during decode): a call on n_tokens tokens touches tokens
+ * [token_offset, token_offset + n_tokens) of every (slab, head) plane.
+ * token_capacity = 0 means token_offset + n_tokens; otherwise the window must
+ * fit (NQ_ERR_INVALID_ARG).  Both 0 is a dense cache of exactly n_tokens.
+ * With positions == NULL, keys take RoPE positions token_offset + t. */
 typedef struct {
   void* codes;
   void* cosets;
   void* scales;
+  int64_t token_capacity;  /* tokens per (slab, head) plane, or 0          */
+  int64_t token_offset;    /* first token of the call inside each plane    */
 } nq_packed;
 
 /* Host.  Bytes of one plane for n_vectors vectors of keys (is_value = 0) or
@@ -142,7 +153,7 @@ const char* nq_status_string(int status);
  *  k, v        device [S][H][T][d] inputs; either may be NULL (then the
  *              matching packed planes are not touched)
  *  positions   device int32 [T] token positions for RoPE, or NULL for
- *              0..T-1; values must be >= 0
+ *              token_offset + (0..T-1); values must be >= 0
  *  pk, pv      host structs holding device plane pointers (outputs)
  *  workspace   device scratch of nq_workspace_bytes(cfg, T) bytes
  * Errors: NQ_ERR_INVALID_ARG (sizes <= 0, null config, misalignment),

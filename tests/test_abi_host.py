@@ -126,3 +126,23 @@ def test_rope_scaling_from_hf_dict():
     assert nq.Config.scaling_from_hf({"type": "linear", "factor": 2.0})["rope_factor"] == 2.0
     with pytest.raises(ValueError):
         nq.Config.scaling_from_hf({"rope_type": "yarn", "factor": 4.0})
+
+
+def test_token_window_checked_before_launch():
+    lib = nq.load()
+    c = nq.Config(128, 2, 2, 0, nq.PARITY_RELAXED, nq.DTYPE_F16, 0.0).c()
+    q = lambda pk: lib.nq_quantize_kv(ctypes.byref(c), 0x10000, None, 1, 1, 4, None,  # noqa: E731
+                                      ctypes.byref(pk), None, None, 0, None)
+    # window past the capacity, negative offset or capacity
+    assert q(nq._Packed(0x1000, 0x2000, 0x3000, 10, 7)) == nq.NQ_ERR_INVALID_ARG
+    assert q(nq._Packed(0x1000, 0x2000, 0x3000, 0, -1)) == nq.NQ_ERR_INVALID_ARG
+    assert q(nq._Packed(0x1000, 0x2000, 0x3000, -5, 0)) == nq.NQ_ERR_INVALID_ARG
+    assert q(nq._Packed(0x1000, 0x2000, 0x3000, 3, 0)) == nq.NQ_ERR_INVALID_ARG
+    # the same checks guard the reading entry points
+    pk = nq._Packed(0x1000, 0x2000, 0x3000, 10, 7)
+    assert lib.nq_dequantize_kv(ctypes.byref(c), ctypes.byref(pk), None, 1, 1, 4, None,
+                                0x10000, None, None, 0, None) == nq.NQ_ERR_INVALID_ARG
+    assert lib.nq_score_packed_keys(ctypes.byref(c), ctypes.byref(pk), 1, 1, 2, 4, 0x10000,
+                                    0x20000, None, 0, None) == nq.NQ_ERR_INVALID_ARG
+    assert lib.nq_attend_packed_values(ctypes.byref(c), ctypes.byref(pk), 1, 1, 2, 4, 0x10000,
+                                       0x20000, None) == nq.NQ_ERR_INVALID_ARG
