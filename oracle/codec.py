@@ -17,6 +17,13 @@ Sources
   "Results" (scale_bpe = 16/128 at G = 128).
 * Same post, "What Makes This Hard in Practice" item 3: the compressed form
   has to stay on the device and be unpacked on the fly -> dequantize.
+* Compact strict packing (our reading of "Bit Rate Accounting", which counts
+  exactly b bits per coordinate, together with "The Relaxed Parity
+  Discovery", where strict E8 keeps an even coordinate sum on both cosets):
+  a strict codeword has an even index sum (sum idx = sum p + 4L - 4c), so
+  the low bit of idx_7 equals the parity of the low bits of idx_0..idx_6 and
+  need not be stored; that bit position carries the coset bit instead.  A
+  group then takes exactly 8b bits and there is no coset plane.
 * Nedelkoski et al., "E8 Lattice Key Quantization for Low-Bit KV-Cache
   Compression", Abstract and Table 3: attention scores computed from the
   packed keys without dequantizing them.  The oracle scores by
@@ -45,7 +52,9 @@ Packed planes, row-major over [S][H][T] vectors:
 Parity status: pinned (scale range, zero vector, pack/unpack round trip,
 plane sizes, strict parity of every group, lattice-point round trips,
 score = dot with an independent dequantization, attend = one-hot rows, the
-codec-frame form and linearity) -- tests/test_oracle_codec.py.
+codec-frame form and linearity; compact packing: a bijection on all 36,049
+strict 2-bit codewords, exactly 8b bits per group, same reconstruction as
+the standard planes) -- tests/test_oracle_codec.py.
 """
 
 from __future__ import annotations
@@ -58,7 +67,8 @@ import numpy as np
 from . import lattice, transform
 
 __all__ = ["Codec", "quantize", "dequantize", "score", "attend", "pack_codes",
-           "unpack_codes", "pack_cosets", "unpack_cosets", "fp16_kv_bytes"]
+           "unpack_codes", "pack_cosets", "unpack_cosets", "fold_cosets",
+           "unfold_cosets", "fp16_kv_bytes"]
 
 
 @dataclass(frozen=True)
@@ -69,6 +79,11 @@ class Codec:
     strict: bool = False
     rope_theta: float = 0.0   # > 0: keys have RoPE removed before quantizing
     rope_scaling: transform.RopeScaling | None = None   # frequency scaling
+    compact: bool = False     # strict only: coset bit in idx_7's low bit
+
+    def __post_init__(self):
+        if self.compact and not self.strict:
+            raise ValueError("compact packing needs strict parity")
 
     @property
     def n(self) -> int:
@@ -88,7 +103,7 @@ class Codec:
 
     @property
     def coset_bytes(self) -> int:
-        return (self.n // 8 + 7) // 8
+        return 0 if self.compact else (self.n // 8 + 7) // 8
 
     @property
     def n_scales(self) -> int:
@@ -152,6 +167,8 @@ def unpack_codes(codes, bits: int, n: int) -> np.ndarray:
 
 def pack_cosets(c, nbytes: int) -> np.ndarray:
     c = np.asarray(c, dtype=np.uint8)
+    if nbytes == 0:                       # compact packing: no coset plane
+        return np.zeros(c.shape[:-1] + (0,), np.uint8)
     pad = nbytes * 8 - c.shape[-1]
     if pad:
         c = np.concatenate([c, np.zeros(c.shape[:-1] + (pad,), np.uint8)], -1)
@@ -163,16 +180,35 @@ def unpack_cosets(cs, groups: int) -> np.ndarray:
                          bitorder="little")[..., :groups]
 
 
+def fold_cosets(idx, c) -> np.ndarray:
+    """Compact form of strict codewords: idx [.., 8] with an even sum, c [..]
+    -> idx with the low bit of idx_7 replaced by c."""
+    idx = np.array(idx, dtype=np.uint8, copy=True)
+    idx[..., 7] = (idx[..., 7] & 0xFE) | (np.asarray(c, dtype=np.uint8) & 1)
+    return idx
+
+
+def unfold_cosets(idx_c):
+    """Inverse of fold_cosets: c is the stored bit; the low bit of idx_7 is
+    the parity of idx_0 .. idx_6 (the index sum is even)."""
+    idx = np.array(idx_c, dtype=np.uint8, copy=True)
+    c = (idx[..., 7] & 1).astype(np.uint8)
+    low = (idx[..., :7].astype(np.int64).sum(-1) & 1).astype(np.uint8)
+    idx[..., 7] = (idx[..., 7] & 0xFE) | low
+    return idx, c
+
+
 def quantize(x, codec: Codec, positions=None, is_key: bool = False):
     """Quantize vectors x [.., d] -> dict of planes plus the decision data."""
     y, a = compute_y(x, codec, positions, is_key)
     lead = y.shape[:-1]
     idx, c, _ = lattice.decode(y.reshape(-1, 8), codec.L, codec.strict)
     ng = codec.n // 8
+    stored = fold_cosets(idx, c) if codec.compact else idx
     idx = idx.reshape(lead + (codec.n,))
     c = c.reshape(lead + (ng,))
     return {
-        "codes": pack_codes(idx, codec.bits),
+        "codes": pack_codes(stored.reshape(lead + (codec.n,)), codec.bits),
         "cosets": pack_cosets(c, codec.coset_bytes),
         "scales": scales_from_maxima(a, codec),
         "idx": idx, "c": c, "y": y, "a": a,
@@ -183,8 +219,14 @@ def dequantize(codes, cosets, scales, codec: Codec, positions=None,
                is_key: bool = False, apply_rope: bool = True) -> np.ndarray:
     """fp64 reconstruction [.., d] of packed vectors."""
     n, d, G = codec.n, codec.head_dim, codec.G
-    idx = unpack_codes(codes, codec.bits, n).astype(np.float64)
-    c = unpack_cosets(cosets, n // 8).astype(np.float64)
+    if codec.compact:
+        u = unpack_codes(codes, codec.bits, n)
+        idx8, c8 = unfold_cosets(u.reshape(u.shape[:-1] + (n // 8, 8)))
+        idx = idx8.reshape(u.shape).astype(np.float64)
+        c = c8.astype(np.float64)
+    else:
+        idx = unpack_codes(codes, codec.bits, n).astype(np.float64)
+        c = unpack_cosets(cosets, n // 8).astype(np.float64)
     p = idx - codec.L / 2 + 0.5 * np.repeat(c, 8, axis=-1)
     s = np.repeat(np.asarray(scales, np.float16).astype(np.float64), G, axis=-1)
     z = s * p

@@ -175,3 +175,48 @@ def test_attend_pins():
     w2 = rng.normal(size=w.shape)
     np.testing.assert_allclose(oc.attend(2 * w - 3 * w2, *planes, cfg),
                                2 * out - 3 * oc.attend(w2, *planes, cfg), atol=1e-10)
+
+
+def test_compact_packing_is_a_bijection_on_strict_codewords():
+    """Every strict 2-bit cube codeword (36,049) survives fold -> pack ->
+    unpack -> unfold; the packed group is exactly 16 bits."""
+    P = lattice.enumerate_cube_codebook(4, True)
+    assert len(P) == 36049
+    c = (np.abs(P[:, 0] - np.round(P[:, 0])) > 0.25).astype(np.uint8)   # half-integer coset
+    idx = (P + 2 - c[:, None] / 2).astype(np.uint8)
+    assert np.all(idx.astype(int).sum(-1) % 2 == 0)
+    packed = oc.pack_codes(oc.fold_cosets(idx, c), 2)
+    assert packed.shape == (len(P), 2)
+    i2, c2 = oc.unfold_cosets(oc.unpack_codes(packed, 2, 8))
+    assert np.array_equal(i2, idx) and np.array_equal(c2, c)
+    # 36,049 distinct codewords -> 36,049 distinct 16-bit words
+    assert len(np.unique(packed.view(np.uint16))) == len(P)
+
+
+def test_compact_needs_strict_parity():
+    with pytest.raises(ValueError):
+        oc.Codec(128, 2, 0, strict=False, compact=True)
+    # a relaxed half-integer codeword with an odd index sum does not survive
+    idx = np.array([[3, 2, 2, 2, 2, 2, 2, 2]], np.uint8)   # p = (1.5, .5, ..., .5), c = 1
+    i2, c2 = oc.unfold_cosets(oc.fold_cosets(idx, [1]))
+    assert not np.array_equal(i2, idx)
+
+
+@pytest.mark.parametrize("bits,G,d", [(2, 0, 128), (3, 64, 128), (2, 32, 96), (3, 8, 8)])
+def test_compact_same_reconstruction_as_standard(bits, G, d):
+    std = oc.Codec(d, bits, G, strict=True)
+    cmp_ = oc.Codec(d, bits, G, strict=True, compact=True)
+    assert cmp_.coset_bytes == 0 and cmp_.code_bytes == std.code_bytes
+    assert cmp_.vector_bytes * 8 == cmp_.n * bits + 16 * cmp_.n_scales
+    x = _x((2, 2, 33, d), 21)
+    a, b = oc.quantize(x, std), oc.quantize(x, cmp_)
+    assert np.array_equal(a["idx"], b["idx"]) and np.array_equal(a["c"], b["c"])
+    assert b["cosets"].shape[-1] == 0
+    # the two packings differ exactly in the low bit of idx_7 of each group
+    ua = oc.unpack_codes(a["codes"], bits, cmp_.n).reshape(-1, 8)
+    ub = oc.unpack_codes(b["codes"], bits, cmp_.n).reshape(-1, 8)
+    assert np.array_equal(ua[:, :7], ub[:, :7]) and np.array_equal(ua[:, 7] >> 1, ub[:, 7] >> 1)
+    assert np.array_equal(ub[:, 7] & 1, a["c"].reshape(-1))
+    ra = oc.dequantize(a["codes"], a["cosets"], a["scales"], std)
+    rb = oc.dequantize(b["codes"], b["cosets"], b["scales"], cmp_)
+    assert np.array_equal(ra, rb)
