@@ -10,7 +10,7 @@
 namespace {
 
 struct Layout {
-  int d, n, G, bits, L, code_bytes, coset_bytes, n_scales;
+  int d, n, G, bits, L, code_bytes, coset_bytes, n_scales, compact;
 };
 
 int next_pow2_min8(int d) {
@@ -39,6 +39,10 @@ int check_config(const nq_config* c) {
   } else if (c->rope_scaling != NQ_ROPE_SCALING_NONE) {
     return NQ_ERR_INVALID_ARG;
   }
+  if (c->packing != NQ_PACKING_STANDARD && c->packing != NQ_PACKING_COMPACT)
+    return NQ_ERR_INVALID_ARG;
+  if (c->packing == NQ_PACKING_COMPACT && c->parity != NQ_PARITY_STRICT)
+    return NQ_ERR_INVALID_ARG;
   if (c->rope_scaling == NQ_ROPE_SCALING_LLAMA3) {
     if (!(c->rope_low_freq_factor > 0.0) || !isfinite(c->rope_high_freq_factor) ||
         !(c->rope_high_freq_factor > c->rope_low_freq_factor) || c->rope_original_max <= 0)
@@ -58,7 +62,8 @@ Layout layout(const nq_config* c, int is_value) {
   l.bits = is_value ? c->bits_v : c->bits_k;
   l.L = 1 << l.bits;
   l.code_bytes = l.n * l.bits / 8;
-  l.coset_bytes = (l.n / 8 + 7) / 8;
+  l.compact = c->packing == NQ_PACKING_COMPACT ? 1 : 0;
+  l.coset_bytes = l.compact ? 0 : (l.n / 8 + 7) / 8;
   l.n_scales = l.n / l.G;
   return l;
 }
@@ -73,8 +78,9 @@ constexpr int64_t kMaxTokens = (int64_t)1 << 40;
 
 // Pointers, alignment and the token window [token_offset, token_offset + T)
 // of a call inside planes of token_capacity tokens per (slab, head).
-int check_packed(const nq_packed* p, int64_t T) {
-  if (p == nullptr || p->codes == nullptr || p->cosets == nullptr ||
+int check_packed(const nq_packed* p, int64_t T, const nq_config* c) {
+  const bool need_cosets = c->packing != NQ_PACKING_COMPACT;
+  if (p == nullptr || p->codes == nullptr || (need_cosets && p->cosets == nullptr) ||
       p->scales == nullptr)
     return NQ_ERR_INVALID_ARG;
   if (!aligned16(p->codes) || !aligned16(p->cosets) || !aligned16(p->scales))
@@ -130,6 +136,7 @@ nq::TensorArgs tensor_args(const nq_config* c, const Layout& l, int64_t S,
   a.G = l.G;
   a.bits = l.bits;
   a.strict = c->parity == NQ_PARITY_STRICT ? 1 : 0;
+  a.compact = l.compact;
   a.code_bytes = l.code_bytes;
   a.coset_bytes = l.coset_bytes;
   a.n_scales = l.n_scales;
@@ -214,9 +221,9 @@ int nq_quantize_kv(const nq_config* cfg, const void* k, const void* v,
   if (st != NQ_OK) return st;
   if ((st = check_shape(S, H, T)) != NQ_OK) return st;
   if (k == nullptr && v == nullptr) return NQ_ERR_INVALID_ARG;
-  if (k != nullptr && (!aligned16(k) || (st = check_packed(pk, T)) != NQ_OK))
+  if (k != nullptr && (!aligned16(k) || (st = check_packed(pk, T, cfg)) != NQ_OK))
     return st != NQ_OK ? st : NQ_ERR_INVALID_ARG;
-  if (v != nullptr && (!aligned16(v) || (st = check_packed(pv, T)) != NQ_OK))
+  if (v != nullptr && (!aligned16(v) || (st = check_packed(pv, T, cfg)) != NQ_OK))
     return st != NQ_OK ? st : NQ_ERR_INVALID_ARG;
   if (positions != nullptr && !aligned16(positions)) return NQ_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -245,9 +252,9 @@ int nq_dequantize_kv(const nq_config* cfg, const nq_packed* pk,
   if (st != NQ_OK) return st;
   if ((st = check_shape(S, H, T)) != NQ_OK) return st;
   if (k_out == nullptr && v_out == nullptr) return NQ_ERR_INVALID_ARG;
-  if (k_out != nullptr && (!aligned16(k_out) || (st = check_packed(pk, T)) != NQ_OK))
+  if (k_out != nullptr && (!aligned16(k_out) || (st = check_packed(pk, T, cfg)) != NQ_OK))
     return st != NQ_OK ? st : NQ_ERR_INVALID_ARG;
-  if (v_out != nullptr && (!aligned16(v_out) || (st = check_packed(pv, T)) != NQ_OK))
+  if (v_out != nullptr && (!aligned16(v_out) || (st = check_packed(pv, T, cfg)) != NQ_OK))
     return st != NQ_OK ? st : NQ_ERR_INVALID_ARG;
   if (positions != nullptr && !aligned16(positions)) return NQ_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -279,7 +286,7 @@ int nq_score_packed_keys(const nq_config* cfg, const nq_packed* pk, int64_t S,
   if ((st = check_shape(S, H, T)) != NQ_OK) return st;
   if (Hq <= 0 || Hq % H != 0) return NQ_ERR_INVALID_ARG;
   if (S > 65535 || H > 65535) return NQ_ERR_UNSUPPORTED;
-  if ((st = check_packed(pk, T)) != NQ_OK) return st;
+  if ((st = check_packed(pk, T, cfg)) != NQ_OK) return st;
   if (q == nullptr || scores == nullptr || !aligned16(q) || !aligned16(scores))
     return NQ_ERR_INVALID_ARG;
   const Layout l = layout(cfg, 0);
@@ -304,6 +311,7 @@ int nq_score_packed_keys(const nq_config* cfg, const nq_packed* pk, int64_t S,
   a.code_bytes = l.code_bytes;
   a.coset_bytes = l.coset_bytes;
   a.n_scales = l.n_scales;
+  a.compact = l.compact;
   a.half_L = (float)(l.L / 2);
   a.inv_sqrt_n = (float)(1.0 / sqrt((double)l.n));
   if (nq::launch_score(a, cfg->in_dtype, static_cast<hipStream_t>(stream)) != hipSuccess)
@@ -319,7 +327,7 @@ int nq_attend_packed_values(const nq_config* cfg, const nq_packed* pv,
   if ((st = check_shape(S, H, T)) != NQ_OK) return st;
   if (Hq <= 0 || Hq % H != 0) return NQ_ERR_INVALID_ARG;
   if (S > 65535 || (int64_t)H * ((Hq / H + 3) / 4 + 1) > 65535) return NQ_ERR_UNSUPPORTED;
-  if ((st = check_packed(pv, T)) != NQ_OK) return st;
+  if ((st = check_packed(pv, T, cfg)) != NQ_OK) return st;
   if (weights == nullptr || out == nullptr || !aligned16(weights) || !aligned16(out))
     return NQ_ERR_INVALID_ARG;
   const Layout l = layout(cfg, 1);
@@ -343,6 +351,7 @@ int nq_attend_packed_values(const nq_config* cfg, const nq_packed* pv,
   a.code_bytes = l.code_bytes;
   a.coset_bytes = l.coset_bytes;
   a.n_scales = l.n_scales;
+  a.compact = l.compact;
   a.half_L = (float)(l.L / 2);
   a.inv_sqrt_n = (float)(1.0 / sqrt((double)l.n));
   if (nq::launch_attend(a, static_cast<hipStream_t>(stream)) != hipSuccess) return NQ_ERR_HIP;

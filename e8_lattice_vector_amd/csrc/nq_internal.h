@@ -20,6 +20,7 @@ struct TensorArgs {
   int64_t pT;           // token stride of the packed planes (>= T); the plane
                         // bases already point at the call's first token
   int d, n, G, bits, strict, code_bytes, coset_bytes, n_scales;
+  int compact;          // coset bit folded into idx_7's low bit (no coset plane)
   float eps;            // fp32(1e-8 * sqrt(n)): floor of the group maximum of |H v|
   float half_L;         // L / 2
   double sigma_k;       // 1 / ((L/2) * sqrt(n)): stored scale = a * sigma_k
@@ -35,6 +36,7 @@ struct ScoreArgs {
   int64_t S, T;
   int64_t pT;           // token stride of the packed planes (>= T)
   int H, Hq, d, n, G, bits, code_bytes, coset_bytes, n_scales;
+  int compact;          // coset bit folded into idx_7's low bit (no coset plane)
   float half_L;
   float inv_sqrt_n;
 };
@@ -48,6 +50,7 @@ struct AttendArgs {
   int64_t S, T;
   int64_t pT;           // token stride of the packed planes (>= T)
   int H, Hq, d, n, G, bits, code_bytes, coset_bytes, n_scales;
+  int compact;          // coset bit folded into idx_7's low bit (no coset plane)
   float half_L;
   float inv_sqrt_n;
 };

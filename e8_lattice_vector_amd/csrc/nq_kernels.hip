@@ -459,6 +459,26 @@ __device__ __forceinline__ uint64_t coset_rows(uint64_t x) {
   return x;
 }
 
+// Compact strict packing: bit 7b of a group's code bits (the low bit of
+// idx_7) holds the coset bit.  A strict codeword has an even index sum, so
+// the low bit of idx_7 is the parity of the low bits of idx_0 .. idx_6.
+template <int BITS>
+struct Compact {
+  static constexpr uint32_t kBit = 1u << (7 * BITS);
+  static constexpr uint32_t kLow7 = BITS == 2 ? 0x1555u : 0x49249u;
+  static __device__ __forceinline__ uint32_t fold(uint32_t w, int c) {
+    return (w & ~kBit) | (c ? kBit : 0u);
+  }
+  // parity of idx_0..idx_6's low bits (the low bit of idx_7)
+  static __device__ __forceinline__ uint32_t low7(uint32_t w) {
+    return (uint32_t)__builtin_popcount(w & kLow7) & 1u;
+  }
+  static __device__ __forceinline__ uint32_t unfold(uint32_t w, int& c) {
+    c = (w & kBit) ? 1 : 0;
+    return (w & ~kBit) | (low7(w) ? kBit : 0u);
+  }
+};
+
 // (x << n) | (the top n bits of w): v_alignbit_b32
 __device__ __forceinline__ uint32_t shift_in(uint32_t x, float w, int n) {
   return __builtin_amdgcn_alignbit(x, __float_as_uint(w), (uint32_t)(32 - n));
@@ -496,7 +516,7 @@ __device__ __forceinline__ int64_t xcd_wave_id() {
 // wave must be active).
 template <bool STRICT>
 __device__ __forceinline__ void e8_decode2(const float g[8], uint32_t& code,
-                                           uint64_t& cosets) {
+                                           uint64_t& cosets, int& coset) {
   uint32_t X = 0, Bn = 0, f0 = 1u << 14, f1 = 0;
   float acc = 0.f, best0, best1 = -INFINITY;
 #pragma unroll
@@ -529,6 +549,7 @@ __device__ __forceinline__ void e8_decode2(const float g[8], uint32_t& code,
   const float rhs = odd0 ? 4.f * best0 : 0.f;
   const int c = lhs < rhs ? 1 : 0;
   cosets = __ballot(lhs < rhs);
+  coset = c;
   const uint32_t Bsp = spread8(~Bn);
   uint32_t w;
   if (c == 0) {
@@ -680,13 +701,14 @@ __global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
     float y[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) y[k] = __fmul_rn(v[k], rs);
+    int c;
     if (BITS == 2) {
-      e8_decode2<STRICT>(y, code, cball);
+      e8_decode2<STRICT>(y, code, cball, c);
     } else {
-      int c;
       e8_decode<BITS, STRICT>(y, code, c);
       cball = __ballot(c);
     }
+    if (STRICT && a.compact) code = Compact<BITS>::fold(code, c);
     const uint64_t cmask = coset_rows<VL>(cball);
     const int slot = it & (gl - 1);
     if (mg == slot) keep = amax;
@@ -699,7 +721,7 @@ __global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
         cp[1] = (uint8_t)((code >> 8) & 0xffu);
         cp[2] = (uint8_t)(code >> 16);
       }
-      if (m == 0) {
+      if (m == 0 && !a.compact) {
         const uint32_t cw = (uint32_t)(cmask >> row_shift) & kRowMask;
         uint8_t* q = qb + os;
         if (VL > 8) *reinterpret_cast<uint16_t*>(q) = (uint16_t)cw;
@@ -752,6 +774,7 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(TensorArgs a) {
   e8_decode<BITS, STRICT>(y, code, c);
   const uint64_t bal = __ballot(c);
   if (!live) return;
+  if (STRICT && a.compact) code = Compact<BITS>::fold(code, c);
   uint8_t* cp = a.codes + pvec * a.code_bytes + m * BITS;
   if (BITS == 2) {
     *reinterpret_cast<uint16_t*>(cp) = (uint16_t)code;
@@ -760,7 +783,7 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(TensorArgs a) {
     cp[1] = (uint8_t)((code >> 8) & 0xffu);
     cp[2] = (uint8_t)(code >> 16);
   }
-  if (m == 0) {
+  if (m == 0 && !a.compact) {
     const int lane = threadIdx.x & 63;
     const uint32_t bits = (uint32_t)(bal >> lane) &
                           (VL >= 32 ? 0xffffffffu : ((1u << VL) - 1u));
@@ -873,7 +896,7 @@ __global__ __launch_bounds__(kBlock) void dequantize_fast_kernel(TensorArgs a,
     } else {
       code = (uint32_t)cp[0] | ((uint32_t)cp[1] << 8) | ((uint32_t)cp[2] << 16);
     }
-    cbyte = a.cosets[vec * a.coset_bytes + (m >> 3)];
+    cbyte = a.compact ? 0u : a.cosets[vec * a.coset_bytes + (m >> 3)];
     sbits = a.scales[vec * a.n_scales + m / gl];
   };  // `vec` indexes the packed planes (token stride pT)
   uint32_t code_n, cbyte_n;
@@ -881,10 +904,11 @@ __global__ __launch_bounds__(kBlock) void dequantize_fast_kernel(TensorArgs a,
   load_meta(sh0 * a.pT + tc, code_n, cbyte_n, sbits_n);
   for (int64_t sh = sh0; sh < sh1; ++sh) {
     const int64_t vec = sh * a.T + tc;
-    const uint32_t code = code_n, cbyte = cbyte_n;
+    const uint32_t code_r = code_n, cbyte = cbyte_n;
     const uint16_t sbits = sbits_n;
     if (sh + 1 < sh1) load_meta((sh + 1) * a.pT + tc, code_n, cbyte_n, sbits_n);
-    const int c = (int)((cbyte >> (m & 7)) & 1u);
+    int c = (int)((cbyte >> (m & 7)) & 1u);
+    const uint32_t code = a.compact ? Compact<BITS>::unfold(code_r, c) : code_r;
     const float sc = h2f(sbits) * a.inv_sqrt_n;
     const float off = (0.5f * (float)c - a.half_L) * sc;
     float v[8];
@@ -939,7 +963,8 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(TensorArgs a) {
   } else {
     code = (uint32_t)cp[0] | ((uint32_t)cp[1] << 8) | ((uint32_t)cp[2] << 16);
   }
-  const int c = (a.cosets[pvec * a.coset_bytes + (m >> 3)] >> (m & 7)) & 1;
+  int c = a.compact ? 0 : (a.cosets[pvec * a.coset_bytes + (m >> 3)] >> (m & 7)) & 1;
+  if (a.compact) code = Compact<BITS>::unfold(code, c);
   const int gl = a.G >> 3;
   const float s = h2f(a.scales[pvec * a.n_scales + m / gl]) * a.inv_sqrt_n;
   const float off = 0.5f * (float)c - a.half_L;
@@ -1005,15 +1030,16 @@ __global__ __launch_bounds__(kBlock) void score_kernel(ScoreArgs a) {
 #pragma unroll
         for (int g = 0; g < kMaxGroup; ++g) part[g] = 0.f;
         for (int mm = sg * gl; mm < (sg + 1) * gl; ++mm) {
-          const int c = (csp[mm >> 3] >> (mm & 7)) & 1;
+          // group mm's 8b code bits start at byte mm * b
+          uint32_t w = (uint32_t)cb[mm * BITS] | ((uint32_t)cb[mm * BITS + 1] << 8);
+          if (BITS == 3) w |= (uint32_t)cb[mm * BITS + 2] << 16;
+          int c = a.compact ? 0 : (csp[mm >> 3] >> (mm & 7)) & 1;
+          if (a.compact) w = Compact<BITS>::unfold(w, c);
           const float off = 0.5f * (float)c - a.half_L;
 #pragma unroll
           for (int k = 0; k < 8; ++k) {
             const int j = 8 * mm + k;
-            const int bit = j * BITS;
-            uint32_t two = (uint32_t)cb[bit >> 3] |
-                           ((bit >> 3) + 1 < CB ? (uint32_t)cb[(bit >> 3) + 1] << 8 : 0u);
-            const int idx = (int)((two >> (bit & 7)) & (L - 1));
+            const int idx = (int)((w >> (BITS * k)) & (L - 1));
             const float p = (float)idx + off;
             for (int g = 0; g < gn; ++g) part[g] = fmaf(qt[(g0 + g) * N + j], p, part[g]);
           }
@@ -1042,6 +1068,11 @@ __global__ __launch_bounds__(kBlock) void score_kernel(ScoreArgs a) {
 // Q_m the sum of q~ over 8-group m; the centring constant sum_j q~_j (L-1)/2 -
 // sum_m Q_m L/2 + sum_m Q_m / 2 cancels exactly.  Tables hold HPP query heads
 // side by side so one LDS vector read serves all of them.
+// Compact packing: the code bit that holds c takes the coset weight
+// (c ? 0 : -Q_m / 2), and the tables of the coset bytes are keyed instead by
+// the per-key mask of the groups' idx_7 low bits (the parity of idx_0..idx_6,
+// computed with popcounts): entry sum_i (bit_i - 1/2) q~_{8 m(i) + 7}.  The
+// constant still cancels.
 // ---------------------------------------------------------------------------
 constexpr int kLutBlock = 512;
 
@@ -1116,6 +1147,10 @@ __global__ __launch_bounds__(kLutBlock) void score_lut_kernel(ScoreArgs a,
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int bit = 8 * tb + i;           // position in the key's bit stream
+        if (a.compact && bit % (8 * BITS) == 7 * BITS) {   // the folded coset bit
+          if (!((v >> i) & 1)) acc -= 0.5f * qm[hh * NG + bit / (8 * BITS)];
+          continue;
+        }
         const float w = qt[hh * N + bit / BITS] * (float)(1 << (bit % BITS));
         acc += (((v >> i) & 1) ? 0.5f : -0.5f) * w;
       }
@@ -1123,7 +1158,9 @@ __global__ __launch_bounds__(kLutBlock) void score_lut_kernel(ScoreArgs a,
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int mm = 8 * (tb - CB) + i;
-        if (mm < NG && !((v >> i) & 1)) acc -= 0.5f * qm[hh * NG + mm];
+        if (mm >= NG) continue;
+        if (a.compact) acc += (((v >> i) & 1) ? 0.5f : -0.5f) * qt[hh * N + 8 * mm + 7];
+        else if (!((v >> i) & 1)) acc -= 0.5f * qm[hh * NG + mm];
       }
     }
     lut[e] = acc;
@@ -1149,10 +1186,20 @@ __global__ __launch_bounds__(kLutBlock) void score_lut_kernel(ScoreArgs a,
 #pragma unroll
       for (int i = 0; i < CB / 4; ++i) cw[i] = reinterpret_cast<const uint32_t*>(cp)[i];
     }
-    uint32_t cs = 0;
-    const uint8_t* csp = a.cosets + vec * CSB;
+    uint32_t cs = 0;   // coset bits, or (compact) the groups' idx_7 low bits
+    if (a.compact) {
+      cw[CB / 4] = 0u;
 #pragma unroll
-    for (int i = 0; i < CSB; ++i) cs |= (uint32_t)csp[i] << (8 * i);
+      for (int mm = 0; mm < NG; ++mm) {
+        const int o = mm * 8 * BITS;
+        const uint64_t x = (uint64_t)cw[o >> 5] | ((uint64_t)cw[(o >> 5) + 1] << 32);
+        cs |= Compact<BITS>::low7((uint32_t)(x >> (o & 31))) << mm;
+      }
+    } else {
+      const uint8_t* csp = a.cosets + vec * CSB;
+#pragma unroll
+      for (int i = 0; i < CSB; ++i) cs |= (uint32_t)csp[i] << (8 * i);
+    }
     float score[HPP];
 #pragma unroll
     for (int hh = 0; hh < HPP; ++hh) score[hh] = 0.f;
@@ -1243,7 +1290,7 @@ __global__ __launch_bounds__(kAttBlock) void attend_kernel(AttendArgs a, int n_p
       } else {
         code[u] = (uint32_t)cp[0] | ((uint32_t)cp[1] << 8) | ((uint32_t)cp[2] << 16);
       }
-      cbyte[u] = a.cosets[vec * a.coset_bytes + (m >> 3)];
+      cbyte[u] = a.compact ? 0u : a.cosets[vec * a.coset_bytes + (m >> 3)];
       sbits[u] = a.scales[vec * a.n_scales + m / gl];
 #pragma unroll
       for (int g = 0; g < HPP; ++g)
@@ -1251,13 +1298,14 @@ __global__ __launch_bounds__(kAttBlock) void attend_kernel(AttendArgs a, int n_p
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int c = (int)((cbyte[u] >> (m & 7)) & 1u);
+      int c = (int)((cbyte[u] >> (m & 7)) & 1u);
+      const uint32_t cw = a.compact ? Compact<BITS>::unfold(code[u], c) : code[u];
       const float sc = h2f(sbits[u]);
       const float off = 0.5f * (float)c - a.half_L;
       float p[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k)
-        p[k] = (float)((code[u] >> (BITS * k)) & (uint32_t)(L - 1));
+        p[k] = (float)((cw >> (BITS * k)) & (uint32_t)(L - 1));
 #pragma unroll
       for (int g = 0; g < HPP; ++g) {
         const float ws = wt[u][g] * sc;

@@ -27,6 +27,7 @@ DTYPE_F16 = 0
 DTYPE_F32 = 1
 PLANE_CODES, PLANE_COSETS, PLANE_SCALES = 0, 1, 2
 ROPE_SCALING_NONE, ROPE_SCALING_LINEAR, ROPE_SCALING_LLAMA3 = 0, 1, 2
+PACKING_STANDARD, PACKING_COMPACT = 0, 1
 
 EXPORTED = ("nq_packed_bytes", "nq_workspace_bytes", "nq_status_string",
             "nq_quantize_kv", "nq_dequantize_kv", "nq_score_packed_keys",
@@ -40,7 +41,7 @@ class _Config(ctypes.Structure):
                 ("rope_theta", ctypes.c_double),
                 ("rope_scaling", ctypes.c_int32), ("rope_original_max", ctypes.c_int32),
                 ("rope_factor", ctypes.c_double), ("rope_low_freq_factor", ctypes.c_double),
-                ("rope_high_freq_factor", ctypes.c_double)]
+                ("rope_high_freq_factor", ctypes.c_double), ("packing", ctypes.c_int32)]
 
 
 class _Packed(ctypes.Structure):
@@ -108,12 +109,14 @@ class Config:
     rope_factor: float = 1.0
     rope_low_freq_factor: float = 1.0
     rope_high_freq_factor: float = 4.0
+    packing: int = PACKING_STANDARD
 
     def c(self) -> _Config:
         return _Config(self.head_dim, self.bits_k, self.bits_v, self.scale_group,
                        self.parity, self.in_dtype, float(self.rope_theta),
                        self.rope_scaling, self.rope_original_max, float(self.rope_factor),
-                       float(self.rope_low_freq_factor), float(self.rope_high_freq_factor))
+                       float(self.rope_low_freq_factor), float(self.rope_high_freq_factor),
+                       self.packing)
 
     @staticmethod
     def scaling_from_hf(rope_scaling) -> dict:
@@ -198,11 +201,12 @@ def alloc_packed(cfg: Config, is_value: bool, S: int, H: int, T: int, device) ->
     planes = []
     for plane in (PLANE_CODES, PLANE_COSETS, PLANE_SCALES):
         nb = packed_bytes(cfg, is_value, nv, plane)
-        if nb == 0:
+        # the coset plane is empty with compact packing
+        if nb == 0 and not (plane == PLANE_COSETS and cfg.packing == PACKING_COMPACT):
             raise NQError(NQ_ERR_INVALID_ARG, "packed_bytes")
         planes.append(torch.empty(nb, dtype=torch.uint8, device=device))
     codes, cosets, scales = planes
-    return Packed(codes.view(S, H, T, -1), cosets.view(S, H, T, -1),
+    return Packed(codes.view(S, H, T, -1), cosets.view(S, H, T, cosets.numel() // max(nv, 1)),
                   scales.view(torch.float16).view(S, H, T, -1))
 
 

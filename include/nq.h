@@ -54,6 +54,7 @@ typedef enum {
 
 enum { NQ_PARITY_STRICT = 0, NQ_PARITY_RELAXED = 1 };
 enum { NQ_ROPE_SCALING_NONE = 0, NQ_ROPE_SCALING_LINEAR = 1, NQ_ROPE_SCALING_LLAMA3 = 2 };
+enum { NQ_PACKING_STANDARD = 0, NQ_PACKING_COMPACT = 1 };
 enum { NQ_DTYPE_F16 = 0, NQ_DTYPE_F32 = 1 };
 enum { NQ_PLANE_CODES = 0, NQ_PLANE_COSETS = 1, NQ_PLANE_SCALES = 2 };
 
@@ -89,6 +90,15 @@ enum { NQ_PLANE_CODES = 0, NQ_PLANE_COSETS = 1, NQ_PLANE_SCALES = 2 };
  * Everything is evaluated in fp64 in that order on the host.  Requirements:
  * rope_factor > 0; LLAMA3 also 0 < low_freq_factor < high_freq_factor and
  * rope_original_max > 0; otherwise NQ_ERR_INVALID_ARG.
+ *
+ * packing ([Walk] "Bit Rate Accounting": b bits per coordinate; "The Relaxed
+ * Parity Discovery": strict E8 keeps an even coordinate sum on both cosets)
+ *  NQ_PACKING_STANDARD  codes plus a coset plane (one bit per 8-group)
+ *  NQ_PACKING_COMPACT   strict parity only (else NQ_ERR_INVALID_ARG): a
+ *      strict codeword's index sum is even, so the low bit of idx_7 is the
+ *      parity of the low bits of idx_0..idx_6; that bit position stores the
+ *      coset bit instead.  Exactly 8b bits per group; the coset plane has 0
+ *      bytes and its pointer may be NULL.
  */
 typedef struct {
   int32_t head_dim;
@@ -103,6 +113,7 @@ typedef struct {
   double rope_factor;            /* LINEAR, LLAMA3                          */
   double rope_low_freq_factor;   /* LLAMA3                                  */
   double rope_high_freq_factor;  /* LLAMA3                                  */
+  int32_t packing;               /* NQ_PACKING_*                            */
 } nq_config;
 
 /* Packed form of one KV tensor: three device planes, each row-major over
@@ -116,7 +127,9 @@ typedef struct {
  *   scales : n/G fp16 per vector, sigma = max|z| / (L/2) over the group, z the
  *            orthonormally rotated vector
  * The three pointers must be 16-byte aligned; sizes from nq_packed_bytes for
- * S * H * token_capacity vectors.
+ * S * H * token_capacity vectors.  With NQ_PACKING_COMPACT the coset plane
+ * is empty (cosets may be NULL) and bit 7b of each group's code bits holds
+ * the coset bit in place of the low bit of idx_7.
  *
  * Token window (decode-time append, [RM] "HuggingFace ecosystem": the cache
  * keeps growing during decode): a call on n_tokens tokens touches tokens

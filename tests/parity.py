@@ -33,7 +33,16 @@ def oracle_codec(cfg, is_value: bool) -> oc.Codec:
     return oc.Codec(cfg.head_dim, cfg.bits_v if is_value else cfg.bits_k,
                     cfg.scale_group, cfg.parity == 0,
                     0.0 if is_value else cfg.rope_theta,
-                    None if is_value else oracle_scaling(cfg))
+                    None if is_value else oracle_scaling(cfg),
+                    compact=cfg.packing == 1)
+
+
+def unpack_planes(codes, cosets, codec: oc.Codec):
+    """(idx [groups, 8], c [groups]) of packed planes, either packing."""
+    idx = oc.unpack_codes(codes.reshape(-1, codec.code_bytes), codec.bits, codec.n).reshape(-1, 8)
+    if codec.compact:
+        return oc.unfold_cosets(idx)
+    return idx, oc.unpack_cosets(cosets.reshape(-1, codec.coset_bytes), codec.n // 8).reshape(-1)
 
 
 def to_np(packed):
@@ -45,17 +54,16 @@ def check_codes(codes, cosets, scales, ref, codec: oc.Codec, label=""):
     """Compare GPU planes (numpy, [..., bytes]) with oracle.quantize output."""
     n, L = codec.n, codec.L
     codes = codes.reshape(-1, codec.code_bytes)
-    cosets = cosets.reshape(-1, codec.coset_bytes)
+    cosets = cosets.reshape(codes.shape[0], codec.coset_bytes)
     scales = scales.reshape(-1, codec.n_scales)
     rc = ref["codes"].reshape(-1, codec.code_bytes)
-    rs = ref["cosets"].reshape(-1, codec.coset_bytes)
+    rs = ref["cosets"].reshape(rc.shape[0], codec.coset_bytes)
     rsc = ref["scales"].reshape(-1, codec.n_scales)
     assert codes.shape == rc.shape, (label, codes.shape, rc.shape)
     # scales: bit-exact (both sides round a * (1/((L/2) sqrt n)) once to fp16)
     bad_sc = np.nonzero(scales.view(np.uint16) != rsc.view(np.uint16))
     assert len(bad_sc[0]) == 0, f"{label}: {len(bad_sc[0])} scale mismatches, first at {bad_sc[0][:5]}"
-    idx_g = oc.unpack_codes(codes, codec.bits, n).reshape(-1, 8)
-    c_g = oc.unpack_cosets(cosets, n // 8).reshape(-1)
+    idx_g, c_g = unpack_planes(codes, cosets, codec)
     idx_r = ref["idx"].reshape(-1, 8)
     c_r = ref["c"].reshape(-1)
     mism = np.any(idx_g != idx_r, axis=1) | (c_g != c_r)

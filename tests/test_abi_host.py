@@ -146,3 +146,25 @@ def test_token_window_checked_before_launch():
                                     0x20000, None, 0, None) == nq.NQ_ERR_INVALID_ARG
     assert lib.nq_attend_packed_values(ctypes.byref(c), ctypes.byref(pk), 1, 1, 2, 4, 0x10000,
                                        0x20000, None) == nq.NQ_ERR_INVALID_ARG
+
+
+def test_compact_packing_host_checks():
+    lib = nq.load()
+    ok = nq.Config(128, 2, 2, 0, nq.PARITY_STRICT, nq.DTYPE_F16, 0.0, packing=nq.PACKING_COMPACT)
+    bad = nq.Config(128, 2, 2, 0, nq.PARITY_RELAXED, nq.DTYPE_F16, 0.0, packing=nq.PACKING_COMPACT)
+    assert nq.packed_bytes(ok, 0, 10, nq.PLANE_CODES) == 320
+    assert nq.packed_bytes(ok, 0, 10, nq.PLANE_COSETS) == 0
+    assert nq.packed_bytes(bad, 0, 10, nq.PLANE_CODES) == 0
+    assert nq.packed_bytes(nq.Config(128, 2, 2, 0, 0, 0, 0.0, packing=7), 0, 10, 0) == 0
+    cc, cb = ok.c(), bad.c()
+    nocs = nq._Packed(0x1000, None, 0x3000)
+    q = lib.nq_quantize_kv
+    # relaxed + compact is rejected; compact accepts a NULL coset plane, standard does not
+    assert q(ctypes.byref(cb), 0x10000, None, 1, 1, 4, None, ctypes.byref(nocs), None, None, 0,
+             None) == nq.NQ_ERR_INVALID_ARG
+    std = nq.Config(128, 2, 2, 0, nq.PARITY_STRICT, nq.DTYPE_F16, 0.0).c()
+    assert q(ctypes.byref(std), 0x10000, None, 1, 1, 4, None, ctypes.byref(nocs), None, None, 0,
+             None) == nq.NQ_ERR_INVALID_ARG
+    # (a valid compact call would launch; only its argument checks run here)
+    assert q(ctypes.byref(cc), 0x10004, None, 1, 1, 4, None, ctypes.byref(nocs), None, None, 0,
+             None) == nq.NQ_ERR_INVALID_ARG

@@ -22,6 +22,7 @@ pytestmark = [pytest.mark.gpu,
 DEV = "cuda"
 S_, R_ = nq.PARITY_STRICT, nq.PARITY_RELAXED
 F16, F32 = nq.DTYPE_F16, nq.DTYPE_F32
+CP = nq.PACKING_COMPACT
 
 
 def log(msg):
@@ -47,6 +48,12 @@ CASES = [
                                       8192, 8.0, 1.0, 4.0), 2, 2, 700, True),
     ("linear-rope-scaled", nq.Config(64, 3, 2, 32, S_, F16, 1e4, nq.ROPE_SCALING_LINEAR,
                                      0, 4.0), 1, 3, 211, True),
+    # compact strict packing (coset bit folded into idx_7's low bit)
+    ("llama-compact", nq.Config(128, 2, 2, 0, S_, F16, 5e5, packing=CP), 2, 3, 517, False),
+    ("mistral-k3-compact", nq.Config(128, 3, 2, 64, S_, F16, 1e6, packing=CP), 2, 2, 300, True),
+    ("phi3-pad-compact", nq.Config(96, 2, 3, 32, S_, F16, 1e4, packing=CP), 1, 3, 211, False),
+    ("d8-compact-f32", nq.Config(8, 2, 3, 8, S_, F32, 0.0, packing=CP), 1, 2, 99, False),
+    ("d256-compact", nq.Config(256, 3, 2, 64, S_, F16, 1e4, packing=CP), 1, 2, 77, True),
 ]
 
 
@@ -107,10 +114,16 @@ def test_magnitude_edges(scale):
     (nq.Config(256, 3, 2, 0, S_, F16, 1e4), 2),
     (nq.Config(128, 2, 2, 64, R_, F16, 5e5), 8),
     (nq.Config(32, 2, 2, 0, R_, F16, 0.0), 2),
+    # compact packing: table path (2- and 3-bit, n 128 and 256), generic path
+    (nq.Config(128, 2, 2, 0, S_, F16, 5e5, packing=CP), 4),
+    (nq.Config(128, 3, 2, 64, S_, F16, 1e6, packing=CP), 4),
+    (nq.Config(256, 3, 2, 0, S_, F16, 1e4, packing=CP), 3),
+    (nq.Config(64, 2, 2, 32, S_, F16, 0.0, packing=CP), 2),
+    (nq.Config(16, 3, 2, 8, S_, F32, 0.0, packing=CP), 2),
 ])
 def test_score_parity(cfg, grp):
     S, H, T = 2, 2, 1500
-    log(f"[score] d={cfg.head_dim} bits={cfg.bits_k} G={cfg.scale_group} grp={grp}")
+    log(f"[score] d={cfg.head_dim} bits={cfg.bits_k} G={cfg.scale_group} grp={grp} packing={cfg.packing}")
     k, _ = _inputs(cfg, S, H, T, 5)
     pk, _ = nq.quantize_kv(cfg, k, None)
     q = synth.queries(S, H * grp, cfg.head_dim, 5, DEV, cfg.torch_dtype)
@@ -241,6 +254,8 @@ def _check_attend(out, w, planes, codec, label):
     (nq.Config(256, 2, 2, 64, S_, F16, 0.0), 2, False),
     (nq.Config(8, 2, 3, 8, R_, F32, 0.0), 1, True),
     (nq.Config(128, 3, 3, 64, R_, F16, 1e6), 5, False),
+    (nq.Config(128, 2, 2, 0, S_, F16, 5e5, packing=CP), 4, False),
+    (nq.Config(96, 3, 3, 32, S_, F16, 1e4, packing=CP), 3, True),
 ])
 def test_attend_parity(cfg, grp, signed):
     S, H, T = 2, 2, 1501
