@@ -359,16 +359,17 @@ int nq_attend_packed_values(const nq_config* cfg, const nq_packed* pv,
 }
 
 int nq_e8_decode_debug(const float* y, int64_t n_groups, int32_t bits,
-                       int32_t parity, uint8_t* idx_out, uint8_t* coset_out,
-                       void* stream) {
+                       int32_t parity, int32_t constrained, uint8_t* idx_out,
+                       uint8_t* coset_out, void* stream) {
   if (y == nullptr || idx_out == nullptr || coset_out == nullptr || n_groups <= 0)
     return NQ_ERR_INVALID_ARG;
   if (!(bits == 2 || bits == 3)) return NQ_ERR_UNSUPPORTED;
   if (parity != NQ_PARITY_STRICT && parity != NQ_PARITY_RELAXED)
     return NQ_ERR_INVALID_ARG;
+  if (constrained != 0 && constrained != 1) return NQ_ERR_INVALID_ARG;
   if (n_groups > ((int64_t)1 << 38)) return NQ_ERR_UNSUPPORTED;
   if (nq::launch_decode_debug(y, n_groups, bits, parity == NQ_PARITY_STRICT,
-                              idx_out, coset_out,
+                              constrained, idx_out, coset_out,
                               static_cast<hipStream_t>(stream)) != hipSuccess)
     return NQ_ERR_HIP;
   return NQ_OK;

@@ -69,7 +69,7 @@ hipError_t launch_dequantize(const TensorArgs& a, int out_dtype, hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, int in_dtype, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 hipError_t launch_decode_debug(const float* y, int64_t n_groups, int bits,
-                               int strict, uint8_t* idx, uint8_t* coset,
-                               hipStream_t s);
+                               int strict, int constrained, uint8_t* idx,
+                               uint8_t* coset, hipStream_t s);
 
 }  // namespace nq

@@ -1359,17 +1359,84 @@ __global__ __launch_bounds__(kAttBlock) void attend_kernel(AttendArgs a, int n_p
   }
 }
 
+// Nearest point of the whole lattice, no cube limit (the textbook
+// Conway-Sloane decoder on D8 and on D8 + 1/2 (strict) or Z^8 + 1/2
+// (relaxed)), with the same tie rules as the cube decoder: rounding ties away
+// from zero, a parity step toward y (away from zero when y is on the point),
+// the lowest index among equal |delta|, the integer coset on equal distance.
+// Distances in fp64 (exact for fp32 y).  q = 2p.
+template <bool STRICT>
+__device__ void e8_nearest_free(const float y[8], int q[8], int& coset) {
+  int qc[2][8];
+  double dist[2];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    float dl[8];
+    int s = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float a = fabsf(y[k]);
+      const float m = c == 0 ? floorf(a + 0.5f) : floorf(a) + 0.5f;
+      const float p = copysignf(m, y[k]);
+      dl[k] = y[k] - p;
+      qc[c][k] = (int)(2.f * p);
+      s += qc[c][k];
+    }
+    if ((c == 0 || STRICT) && ((s >> 1) & 1)) {   // sum p = s / 2 is odd
+      int is = 0;
+      float best = -1.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (fabsf(dl[k]) > best) { best = fabsf(dl[k]); is = k; }
+      int t = dl[is] > 0.f ? 1 : -1;
+      if (dl[is] == 0.f) t = signbit(y[is]) ? -1 : 1;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) if (k == is) qc[c][k] += 2 * t;
+    }
+    double d = 0.0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const double e = (double)y[k] - 0.5 * (double)qc[c][k];
+      d += e * e;
+    }
+    dist[c] = d;
+  }
+  coset = dist[1] < dist[0] ? 1 : 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) q[k] = coset ? qc[1][k] : qc[0][k];
+}
+
+// Decoder alone.  constrained: the cube decoder the quantize kernels use (the
+// 2-bit one on g = 2y for b = 2); otherwise the unconstrained nearest point,
+// idx = p - c/2 + L/2 stored as a two's-complement int8.
 template <int BITS, bool STRICT>
 __global__ __launch_bounds__(kBlock) void decode_debug_kernel(
-    const float* y, int64_t n, uint8_t* idx, uint8_t* coset) {
+    const float* y, int64_t n, int constrained, uint8_t* idx, uint8_t* coset) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   float v[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) v[k] = y[i * 8 + k];
-  uint32_t code;
   int c;
-  e8_decode<BITS, STRICT>(v, code, c);
+  if (!constrained) {
+    int q[8];
+    e8_nearest_free<STRICT>(v, q, c);
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+      idx[i * 8 + k] = (uint8_t)(int8_t)((q[k] - c + (1 << BITS)) / 2);
+    coset[i] = (uint8_t)c;
+    return;
+  }
+  uint32_t code;
+  if (BITS == 2) {
+    float g[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) g[k] = v[k] + v[k];
+    uint64_t ball;
+    e8_decode2<STRICT>(g, code, ball, c);
+  } else {
+    e8_decode<BITS, STRICT>(v, code, c);
+  }
 #pragma unroll
   for (int k = 0; k < 8; ++k)
     idx[i * 8 + k] = (uint8_t)((code >> (BITS * k)) & ((1u << BITS) - 1u));
@@ -1629,14 +1696,14 @@ hipError_t launch_score(const ScoreArgs& a, int in_dtype, hipStream_t s) {
   return in_dtype == 0 ? score_t<__half>(a, s) : score_t<float>(a, s);
 }
 
-hipError_t launch_decode_debug(const float* y, int64_t n, int bits, int strict,
+hipError_t launch_decode_debug(const float* y, int64_t n, int bits, int strict, int constrained,
                                uint8_t* idx, uint8_t* coset, hipStream_t s) {
   const int64_t blocks = (n + kBlock - 1) / kBlock;
   const dim3 g((unsigned)blocks), b(kBlock);
-  if (bits == 2 && strict) hipLaunchKernelGGL((decode_debug_kernel<2, true>), g, b, 0, s, y, n, idx, coset);
-  else if (bits == 2) hipLaunchKernelGGL((decode_debug_kernel<2, false>), g, b, 0, s, y, n, idx, coset);
-  else if (bits == 3 && strict) hipLaunchKernelGGL((decode_debug_kernel<3, true>), g, b, 0, s, y, n, idx, coset);
-  else if (bits == 3) hipLaunchKernelGGL((decode_debug_kernel<3, false>), g, b, 0, s, y, n, idx, coset);
+  if (bits == 2 && strict) hipLaunchKernelGGL((decode_debug_kernel<2, true>), g, b, 0, s, y, n, constrained, idx, coset);
+  else if (bits == 2) hipLaunchKernelGGL((decode_debug_kernel<2, false>), g, b, 0, s, y, n, constrained, idx, coset);
+  else if (bits == 3 && strict) hipLaunchKernelGGL((decode_debug_kernel<3, true>), g, b, 0, s, y, n, constrained, idx, coset);
+  else if (bits == 3) hipLaunchKernelGGL((decode_debug_kernel<3, false>), g, b, 0, s, y, n, constrained, idx, coset);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

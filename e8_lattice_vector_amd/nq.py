@@ -84,7 +84,7 @@ def load(path: str = LIB_PATH):
     lib.nq_score_packed_keys.restype = ctypes.c_int
     lib.nq_attend_packed_values.argtypes = [cfgp, pkp, i64, i32, i32, i64, vp, vp, vp]
     lib.nq_attend_packed_values.restype = ctypes.c_int
-    lib.nq_e8_decode_debug.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+    lib.nq_e8_decode_debug.argtypes = [vp, i64, i32, i32, i32, vp, vp, vp]
     lib.nq_e8_decode_debug.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -307,14 +307,15 @@ def attend_packed_values(cfg: Config, pv: Packed, weights, S: int, H: int, T: in
     return out
 
 
-def e8_decode_debug(y, bits: int, parity: int, stream=None):
-    """y: device fp32 [N, 8] -> (idx uint8 [N, 8], coset uint8 [N])."""
+def e8_decode_debug(y, bits: int, parity: int, stream=None, constrained: bool = True):
+    """y: device fp32 [N, 8] -> (idx uint8 [N, 8], coset uint8 [N]); with
+    constrained=False the unconstrained decoder, idx as int8 in the uint8."""
     if y.dtype != torch.float32 or y.dim() != 2 or y.shape[1] != 8 or not y.is_contiguous():
         raise NQError(NQ_ERR_INVALID_ARG, "e8_decode_debug y")
     n = y.shape[0]
     idx = torch.empty((n, 8), dtype=torch.uint8, device=y.device)
     cos = torch.empty((n,), dtype=torch.uint8, device=y.device)
-    st = load().nq_e8_decode_debug(y.data_ptr(), n, bits, parity, idx.data_ptr(),
+    st = load().nq_e8_decode_debug(y.data_ptr(), n, bits, parity, int(constrained), idx.data_ptr(),
                                    cos.data_ptr(), _stream(stream))
     _check(st, "nq_e8_decode_debug")
     return idx, cos

@@ -220,15 +220,21 @@ int nq_attend_packed_values(const nq_config* cfg, const nq_packed* pv,
                             int32_t n_q_heads, int64_t n_tokens,
                             const float* weights, float* out, void* stream);
 
-/* Test hook: the nearest-codeword decoder alone ([Walk] "The Conway-Sloane
+/* Test hook: the nearest-point decoder alone ([Walk] "The Conway-Sloane
  * Nearest-Point Algorithm") on caller-given groups y (lattice units).
- *  y          device fp32 [n_groups][8]
- *  idx_out    device uint8 [n_groups][8], idx = p - c/2 + 2^bits/2
- *  coset_out  device uint8 [n_groups]
+ *  y            device fp32 [n_groups][8]
+ *  constrained  1: the cube-limited decoder the quantize kernels use (for
+ *               b = 2 the same 2-bit decoder), valid for |y_k| <= L/2 (the
+ *               range the scale step produces); idx in [0, L-1]
+ *               0: nearest point of the whole lattice (E8, or D8 u (Z^8 + 1/2)
+ *               relaxed), no cube limit; idx = p - c/2 + L/2 written as a
+ *               two's-complement int8 (|y_k| <= 60)
+ *  idx_out      device uint8 [n_groups][8], idx = p - c/2 + L/2 (L = 2^bits)
+ *  coset_out    device uint8 [n_groups]
  * bits 2 or 3; parity NQ_PARITY_STRICT or NQ_PARITY_RELAXED. */
 int nq_e8_decode_debug(const float* y, int64_t n_groups, int32_t bits,
-                       int32_t parity, uint8_t* idx_out, uint8_t* coset_out,
-                       void* stream);
+                       int32_t parity, int32_t constrained, uint8_t* idx_out,
+                       uint8_t* coset_out, void* stream);
 
 #ifdef __cplusplus
 }

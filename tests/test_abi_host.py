@@ -87,9 +87,10 @@ def test_invalid_arguments_rejected_before_launch():
     assert at(ctypes.byref(c), None, 1, 2, 4, 8, 0x10000, 0x20000, None) == -1
     assert at(ctypes.byref(c), ctypes.byref(pk), 0, 2, 4, 8, 0x10000, 0x20000, None) == -1
     dd = lib.nq_e8_decode_debug
-    assert dd(0x1000, 10, 4, 0, 0x2000, 0x3000, None) == -2
-    assert dd(0x1000, 0, 2, 0, 0x2000, 0x3000, None) == -1
-    assert dd(0x1000, 10, 2, 5, 0x2000, 0x3000, None) == -1
+    assert dd(0x1000, 10, 4, 0, 1, 0x2000, 0x3000, None) == -2
+    assert dd(0x1000, 0, 2, 0, 1, 0x2000, 0x3000, None) == -1
+    assert dd(0x1000, 10, 2, 5, 1, 0x2000, 0x3000, None) == -1
+    assert dd(0x1000, 10, 2, 0, 2, 0x2000, 0x3000, None) == -1
     for s in (0, -1, -2, -3, -4, 9):
         assert isinstance(nq.status_string(s), str)
 

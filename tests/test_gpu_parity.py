@@ -168,6 +168,34 @@ def test_decoder_alone(bits, parity):
     assert n_bad <= int(1e-6 * len(y))
 
 
+@pytest.mark.parametrize("parity", [S_, R_])
+def test_unconstrained_decoder(parity):
+    """Nearest point of the whole lattice: minimal vectors decode to
+    themselves; random points in [-3, 3]^8 (with exact ties) match the
+    oracle's unconstrained decoder."""
+    strict = parity == S_
+    mins = lattice.enumerate_ball(2.0, strict)
+    mins = mins[(mins ** 2).sum(-1) == 2.0]
+    assert len(mins) == (240 if strict else 368)
+    rng = np.random.default_rng(30 + parity)
+    y = rng.uniform(-3, 3, size=(100000, 8))
+    y[:20000] = np.round(y[:20000] * 2) / 2                               # exact ties
+    y = np.concatenate([mins, -mins, y]).astype(np.float32)
+    log(f"[decoder-free] parity={parity} groups={len(y)}")
+    idx, c = nq.e8_decode_debug(torch.from_numpy(y).to(DEV), 2, parity, constrained=False)
+    torch.cuda.synchronize()
+    gi = idx.cpu().numpy().view(np.int8).astype(np.float64)
+    gp = gi - 2 + 0.5 * c.cpu().numpy()[:, None]
+    assert np.array_equal(gp[:len(mins)], mins) and np.array_equal(gp[len(mins):2 * len(mins)], -mins)
+    rp = lattice.decode_unconstrained(y.astype(np.float64), strict)
+    mism = np.any(gp != rp, axis=1)
+    if mism.any():
+        yy = y[mism].astype(np.float64)
+        regret = ((yy - gp[mism]) ** 2).sum(-1) - ((yy - rp[mism]) ** 2).sum(-1)
+        assert lattice.in_lattice(gp[mism], strict).all() and (regret < 1e-6).all()
+    assert int(mism.sum()) <= int(1e-6 * len(y)), int(mism.sum())
+
+
 def _sample_idx(rng, S, H, T, n):
     return rng.integers(0, S, n), rng.integers(0, H, n), rng.integers(0, T, n)
 
