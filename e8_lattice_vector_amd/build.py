@@ -4,6 +4,7 @@ Usage: python -m e8_lattice_vector_amd.build   (or build() from Python)
 """
 
 import os
+import re
 import subprocess
 import sys
 
@@ -23,7 +24,24 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
     "-Wno-unused-command-line-argument",
+    # per-kernel register / scratch report, checked below
+    "-Rpass-analysis=kernel-resource-usage",
 ]
+
+
+def spilling_kernels(remarks: str):
+    """Kernels whose resource report shows scratch (register spills): every
+    kernel here is sized to keep its state in registers."""
+    out, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"remark:\s+ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and int(m.group(1)) > 0:
+            out.append((name, int(m.group(1))))
+    return out
 
 
 def build(verbose: bool = False) -> str:
@@ -37,6 +55,10 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
         raise RuntimeError("hipcc failed building libnq.so")
+    spills = spilling_kernels(r.stderr)
+    if spills:
+        os.remove(tmp)
+        raise RuntimeError(f"kernels spill to scratch: {spills[:5]} ({len(spills)} in all)")
     os.replace(tmp, LIB)
     return LIB
 

@@ -829,7 +829,7 @@ struct OutIo<float> {
 // sign-twisted DPP butterflies, so lane l ends with sigma_l * x^; sigma_l is
 // removed by flipping sign bits at the store.  Keys then get RoPE forward:
 // x_i = y_i c - y_{i+h} s, x_{i+h} = y_{i+h} c + y_i s.
-template <int N, int BITS, typename OutT, int ROPE>
+template <int N, int BITS, typename OutT, int ROPE, bool CMP>
 __global__ __launch_bounds__(kBlock) void dequantize_fast_kernel(TensorArgs a,
                                                                  int sh_chunk,
                                                                  int tile_major) {
@@ -896,7 +896,7 @@ __global__ __launch_bounds__(kBlock) void dequantize_fast_kernel(TensorArgs a,
     } else {
       code = (uint32_t)cp[0] | ((uint32_t)cp[1] << 8) | ((uint32_t)cp[2] << 16);
     }
-    cbyte = a.compact ? 0u : a.cosets[vec * a.coset_bytes + (m >> 3)];
+    cbyte = CMP ? 0u : a.cosets[vec * a.coset_bytes + (m >> 3)];
     sbits = a.scales[vec * a.n_scales + m / gl];
   };  // `vec` indexes the packed planes (token stride pT)
   uint32_t code_n, cbyte_n;
@@ -908,7 +908,7 @@ __global__ __launch_bounds__(kBlock) void dequantize_fast_kernel(TensorArgs a,
     const uint16_t sbits = sbits_n;
     if (sh + 1 < sh1) load_meta((sh + 1) * a.pT + tc, code_n, cbyte_n, sbits_n);
     int c = (int)((cbyte >> (m & 7)) & 1u);
-    const uint32_t code = a.compact ? Compact<BITS>::unfold(code_r, c) : code_r;
+    const uint32_t code = CMP ? Compact<BITS>::unfold(code_r, c) : code_r;
     const float sc = h2f(sbits) * a.inv_sqrt_n;
     const float off = (0.5f * (float)c - a.half_L) * sc;
     float v[8];
@@ -1092,7 +1092,7 @@ __device__ __forceinline__ void lut_add(float* acc, float4 v) {
   acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
 }
 
-template <int BITS, int N, int HPP, typename QT>
+template <int BITS, int N, int HPP, typename QT, bool CMP>
 __global__ __launch_bounds__(kLutBlock) void score_lut_kernel(ScoreArgs a,
                                                               int n_pass,
                                                               int64_t chunk) {
@@ -1147,7 +1147,7 @@ __global__ __launch_bounds__(kLutBlock) void score_lut_kernel(ScoreArgs a,
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int bit = 8 * tb + i;           // position in the key's bit stream
-        if (a.compact && bit % (8 * BITS) == 7 * BITS) {   // the folded coset bit
+        if (CMP && bit % (8 * BITS) == 7 * BITS) {   // the folded coset bit
           if (!((v >> i) & 1)) acc -= 0.5f * qm[hh * NG + bit / (8 * BITS)];
           continue;
         }
@@ -1159,7 +1159,7 @@ __global__ __launch_bounds__(kLutBlock) void score_lut_kernel(ScoreArgs a,
       for (int i = 0; i < 8; ++i) {
         const int mm = 8 * (tb - CB) + i;
         if (mm >= NG) continue;
-        if (a.compact) acc += (((v >> i) & 1) ? 0.5f : -0.5f) * qt[hh * N + 8 * mm + 7];
+        if (CMP) acc += (((v >> i) & 1) ? 0.5f : -0.5f) * qt[hh * N + 8 * mm + 7];
         else if (!((v >> i) & 1)) acc -= 0.5f * qm[hh * NG + mm];
       }
     }
@@ -1187,7 +1187,7 @@ __global__ __launch_bounds__(kLutBlock) void score_lut_kernel(ScoreArgs a,
       for (int i = 0; i < CB / 4; ++i) cw[i] = reinterpret_cast<const uint32_t*>(cp)[i];
     }
     uint32_t cs = 0;   // coset bits, or (compact) the groups' idx_7 low bits
-    if (a.compact) {
+    if (CMP) {
       cw[CB / 4] = 0u;
 #pragma unroll
       for (int mm = 0; mm < NG; ++mm) {
@@ -1241,10 +1241,15 @@ __global__ __launch_bounds__(kLutBlock) void score_lut_kernel(ScoreArgs a,
 // key per step, lane m accumulates its 8-group; rows and waves are reduced
 // through LDS in a fixed order (deterministic).
 // ---------------------------------------------------------------------------
-constexpr int kAttBlock = 1024;
+// Threads per workgroup: 1024, or 512 where the accumulators (HPP heads x 8
+// coordinates), the in-flight weights and 3-bit code words need more than
+// the 128 registers a lane has at 1024 threads (8 heads per pass; 4 heads of
+// 3-bit codes); no instance spills.
+template <int BITS, int HPP>
+constexpr int att_block() { return (HPP >= 8 || (HPP >= 4 && BITS == 3)) ? 512 : 1024; }
 
-template <int BITS, int N, int HPP>
-__global__ __launch_bounds__(kAttBlock) void attend_kernel(AttendArgs a, int n_pass) {
+template <int BITS, int N, int HPP, bool CMP>
+__global__ __launch_bounds__((att_block<BITS, HPP>())) void attend_kernel(AttendArgs a, int n_pass) {
   constexpr int VL = N / 8;
   constexpr int KPW = 64 / VL;             // keys per wave per step
   constexpr int L = 1 << BITS;
@@ -1290,7 +1295,7 @@ __global__ __launch_bounds__(kAttBlock) void attend_kernel(AttendArgs a, int n_p
       } else {
         code[u] = (uint32_t)cp[0] | ((uint32_t)cp[1] << 8) | ((uint32_t)cp[2] << 16);
       }
-      cbyte[u] = a.compact ? 0u : a.cosets[vec * a.coset_bytes + (m >> 3)];
+      cbyte[u] = CMP ? 0u : a.cosets[vec * a.coset_bytes + (m >> 3)];
       sbits[u] = a.scales[vec * a.n_scales + m / gl];
 #pragma unroll
       for (int g = 0; g < HPP; ++g)
@@ -1299,7 +1304,7 @@ __global__ __launch_bounds__(kAttBlock) void attend_kernel(AttendArgs a, int n_p
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       int c = (int)((cbyte[u] >> (m & 7)) & 1u);
-      const uint32_t cw = a.compact ? Compact<BITS>::unfold(code[u], c) : code[u];
+      const uint32_t cw = CMP ? Compact<BITS>::unfold(code[u], c) : code[u];
       const float sc = h2f(sbits[u]);
       const float off = 0.5f * (float)c - a.half_L;
       float p[8];
@@ -1517,8 +1522,12 @@ hipError_t dequantize_fast_launch(const TensorArgs& a, hipStream_t s) {
   const int chunk = sh_chunk_for(SH, n_tt);
   const int64_t waves = n_tt * ((SH + chunk - 1) / chunk);
   const int64_t blocks = ((waves + kBlock / 64 - 1) / (kBlock / 64) + 7) / 8 * 8;
-  hipLaunchKernelGGL((dequantize_fast_kernel<N, BITS, T, ROPE>), dim3((unsigned)blocks),
-                     dim3(kBlock), 0, s, a, chunk, 0);
+  if (a.compact)
+    hipLaunchKernelGGL((dequantize_fast_kernel<N, BITS, T, ROPE, true>), dim3((unsigned)blocks),
+                       dim3(kBlock), 0, s, a, chunk, 0);
+  else
+    hipLaunchKernelGGL((dequantize_fast_kernel<N, BITS, T, ROPE, false>), dim3((unsigned)blocks),
+                       dim3(kBlock), 0, s, a, chunk, 0);
   return hipGetLastError();
 }
 
@@ -1541,7 +1550,8 @@ template <int BITS, int N, int HPP, typename T>
 hipError_t score_lut_launch(const ScoreArgs& a, int n_pass, hipStream_t s) {
   constexpr int CB = N * BITS / 8, NG = N / 8, CSB = (NG + 7) / 8;
   const size_t lds = sizeof(float) * ((size_t)(CB + CSB) * 256 * HPP + HPP * N + HPP * NG);
-  auto kern = score_lut_kernel<BITS, N, HPP, T>;
+  auto kern = a.compact ? score_lut_kernel<BITS, N, HPP, T, true>
+                        : score_lut_kernel<BITS, N, HPP, T, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -1630,13 +1640,13 @@ template <int BITS, int N, int HPP>
 hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
   const int grp = a.Hq / a.H;
   const int n_pass = (grp + HPP - 1) / HPP;
-  const size_t lds = sizeof(float) * (size_t)(kAttBlock / 64) * HPP * N;
-  auto kern = attend_kernel<BITS, N, HPP>;
+  const size_t lds = sizeof(float) * (size_t)(att_block<BITS, HPP>() / 64) * HPP * N;
+  auto kern = a.compact ? attend_kernel<BITS, N, HPP, true> : attend_kernel<BITS, N, HPP, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const dim3 grid(1u, (unsigned)(a.H * n_pass), (unsigned)a.S);
-  hipLaunchKernelGGL(kern, grid, dim3(kAttBlock), lds, s, a, n_pass);
+  hipLaunchKernelGGL(kern, grid, dim3(att_block<BITS, HPP>()), lds, s, a, n_pass);
   return hipGetLastError();
 }
 

@@ -169,3 +169,12 @@ def test_compact_packing_host_checks():
     # (a valid compact call would launch; only its argument checks run here)
     assert q(ctypes.byref(cc), 0x10004, None, 1, 1, 4, None, ctypes.byref(nocs), None, None, 0,
              None) == nq.NQ_ERR_INVALID_ARG
+
+
+def test_build_spill_check_parses_remarks():
+    from e8_lattice_vector_amd import build
+    txt = ("x.hip:2:1: remark: Function Name: _Z1kv [-Rpass-analysis=kernel-resource-usage]\n"
+           "x.hip:2:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]\n"
+           "x.hip:9:1: remark: Function Name: _Z2k2v [-Rpass-analysis=kernel-resource-usage]\n"
+           "x.hip:9:1: remark:     ScratchSize [bytes/lane]: 12 [-Rpass-analysis=kernel-resource-usage]\n")
+    assert build.spilling_kernels(txt) == [("_Z2k2v", 12)]
