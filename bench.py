@@ -69,13 +69,18 @@ def cpu_baseline(w, tokens):
     q = synth.queries(1, 32, w.d, 0).numpy()
     ck = oc.Codec(w.d, w.bits_k, w.G, w.strict, w.theta)
     cv = oc.Codec(w.d, w.bits_v, w.G, w.strict, 0.0)
-    t0 = time.perf_counter()
-    rk = oc.quantize(k, ck, is_key=True)
-    rv = oc.quantize(v, cv)
-    oc.dequantize(rk["codes"], rk["cosets"], rk["scales"], ck, is_key=True)
-    oc.dequantize(rv["codes"], rv["cosets"], rv["scales"], cv)
-    oc.score(q, rk["codes"], rk["cosets"], rk["scales"], ck)
-    dt = time.perf_counter() - t0
+    from threadpoolctl import threadpool_limits
+
+    # one thread, so that "cores" is what the run used (numpy's BLAS would
+    # otherwise spread the scoring products over the host's cores)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        rk = oc.quantize(k, ck, is_key=True)
+        rv = oc.quantize(v, cv)
+        oc.dequantize(rk["codes"], rk["cosets"], rk["scales"], ck, is_key=True)
+        oc.dequantize(rv["codes"], rv["cosets"], rv["scales"], cv)
+        oc.score(q, rk["codes"], rk["cosets"], rk["scales"], ck)
+        dt = time.perf_counter() - t0
     cache_tokens = tokens / w.S  # one of S slabs
     return {
         "value": cache_tokens / dt,
