@@ -1076,23 +1076,44 @@ __global__ __launch_bounds__(kBlock) void score_kernel(ScoreArgs a) {
 // ---------------------------------------------------------------------------
 constexpr int kLutBlock = 512;
 
+// Table entries: HPP floats side by side.  2 and 4 heads use native vector
+// types and vector accumulation, so that each lookup stays one 8- or 16-byte
+// LDS read (per-component use lets the compiler split it into scalar reads).
+typedef float nq_f2 __attribute__((ext_vector_type(2)));
+typedef float nq_f4 __attribute__((ext_vector_type(4)));
 template <int HPP>
 struct LutVec;
 template <> struct LutVec<1> { using T = float; };
-template <> struct LutVec<2> { using T = float2; };
+template <> struct LutVec<2> { using T = nq_f2; };
 template <> struct LutVec<3> { using T = float3; };
-template <> struct LutVec<4> { using T = float4; };
+template <> struct LutVec<4> { using T = nq_f4; };
 
-__device__ __forceinline__ void lut_add(float* acc, float v) { acc[0] += v; }
-__device__ __forceinline__ void lut_add(float* acc, float2 v) { acc[0] += v.x; acc[1] += v.y; }
-__device__ __forceinline__ void lut_add(float* acc, float3 v) {
-  acc[0] += v.x; acc[1] += v.y; acc[2] += v.z;
-}
-__device__ __forceinline__ void lut_add(float* acc, float4 v) {
-  acc[0] += v.x; acc[1] += v.y; acc[2] += v.z; acc[3] += v.w;
-}
+template <typename V>
+struct LutAcc {   // vector accumulator for native vectors
+  V v;
+  __device__ __forceinline__ void zero() { v = V(0.f); }
+  __device__ __forceinline__ void add(V x) { v = v + x; }
+  __device__ __forceinline__ float get(int i) const { return v[i]; }
+};
+template <>
+struct LutAcc<float3> {
+  float v[3];
+  __device__ __forceinline__ void zero() { v[0] = v[1] = v[2] = 0.f; }
+  __device__ __forceinline__ void add(float3 x) { v[0] += x.x; v[1] += x.y; v[2] += x.z; }
+  __device__ __forceinline__ float get(int i) const { return v[i]; }
+};
+template <>
+struct LutAcc<float> {
+  float v;
+  __device__ __forceinline__ void zero() { v = 0.f; }
+  __device__ __forceinline__ void add(float x) { v += x; }
+  __device__ __forceinline__ float get(int) const { return v; }
+};
 
-template <int BITS, int N, int HPP, typename QT, bool CMP>
+
+// NS = scale groups per key (n / G: 1, 2 or 4); a compile-time count keeps
+// the per-key lookups free of branches, so their LDS reads overlap.
+template <int BITS, int N, int HPP, typename QT, bool CMP, int NS>
 __global__ __launch_bounds__(kLutBlock) void score_lut_kernel(ScoreArgs a,
                                                               int n_pass,
                                                               int64_t chunk) {
@@ -1101,7 +1122,7 @@ __global__ __launch_bounds__(kLutBlock) void score_lut_kernel(ScoreArgs a,
   constexpr int CSB = (NG + 7) / 8;       // coset bytes per key
   constexpr int NT = CB + CSB;            // tables
   using V = typename LutVec<HPP>::T;
-  extern __shared__ float lds[];
+  extern __shared__ __align__(16) float lds[];   // 16-byte table entries
   float* lut = lds;                       // [NT][256][HPP]
   float* qt = lds + NT * 256 * HPP;       // [HPP][N] rotated queries
   float* qm = qt + HPP * N;               // [HPP][NG] group sums
@@ -1137,38 +1158,62 @@ __global__ __launch_bounds__(kLutBlock) void score_lut_kernel(ScoreArgs a,
     qm[i] = sum;
   }
   __syncthreads();
-  // tables
-  for (int e = threadIdx.x; e < NT * 256 * HPP; e += blockDim.x) {
-    const int hh = e % HPP;
-    const int v = (e / HPP) & 255;
-    const int tb = e / (HPP * 256);
-    float acc = 0.f;
-    if (tb < CB) {
+  // Tables.  Bit i of a table's byte adds A_i when set and B_i when clear:
+  //   code bit            A = +w/2, B = -w/2 (w = q~_j 2^b for its coordinate)
+  //   coset bit           A = 0,    B = -Q_m/2 (also the folded c of compact)
+  //   compact parity bit  A = +q~_{8m+7}/2, B = -q~_{8m+7}/2
+  // Each work item (table, head, high nibble h) forms the 16 low-nibble sums
+  // from two 4-entry pair tables and writes entries 16 h .. 16 h + 15.
+  for (int item = threadIdx.x; item < NT * HPP * 16; item += blockDim.x) {
+    const int h = item & 15;
+    const int hh = (item >> 4) % HPP;
+    const int tb = (item >> 4) / HPP;
+    float A[8], B[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 8; ++i) {
+      if (tb < CB) {
         const int bit = 8 * tb + i;           // position in the key's bit stream
         if (CMP && bit % (8 * BITS) == 7 * BITS) {   // the folded coset bit
-          if (!((v >> i) & 1)) acc -= 0.5f * qm[hh * NG + bit / (8 * BITS)];
-          continue;
+          A[i] = 0.f;
+          B[i] = -0.5f * qm[hh * NG + bit / (8 * BITS)];
+        } else {
+          const float w = qt[hh * N + bit / BITS] * (float)(1 << (bit % BITS));
+          A[i] = 0.5f * w;
+          B[i] = -0.5f * w;
         }
-        const float w = qt[hh * N + bit / BITS] * (float)(1 << (bit % BITS));
-        acc += (((v >> i) & 1) ? 0.5f : -0.5f) * w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      } else {
         const int mm = 8 * (tb - CB) + i;
-        if (mm >= NG) continue;
-        if (CMP) acc += (((v >> i) & 1) ? 0.5f : -0.5f) * qt[hh * N + 8 * mm + 7];
-        else if (!((v >> i) & 1)) acc -= 0.5f * qm[hh * NG + mm];
+        if (mm >= NG) {
+          A[i] = 0.f;
+          B[i] = 0.f;
+        } else if (CMP) {
+          A[i] = 0.5f * qt[hh * N + 8 * mm + 7];
+          B[i] = -A[i];
+        } else {
+          A[i] = 0.f;
+          B[i] = -0.5f * qm[hh * NG + mm];
+        }
       }
     }
-    lut[e] = acc;
+    float hi = 0.f;
+#pragma unroll
+    for (int i = 4; i < 8; ++i) hi += ((h >> (i - 4)) & 1) ? A[i] : B[i];
+    float p01[4], p23[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      p01[u] = ((u & 1) ? A[0] : B[0]) + ((u & 2) ? A[1] : B[1]);
+      p23[u] = ((u & 1) ? A[2] : B[2]) + ((u & 2) ? A[3] : B[3]);
+    }
+    float* row = lut + ((size_t)tb * 256 + h * 16) * HPP + hh;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) row[u * HPP] = (p01[u & 3] + p23[u >> 2]) + hi;
   }
   __syncthreads();
 
-  const int gl = a.G >> 3;                 // 8-groups per scale group
-  const int ns = NG / gl;                  // scale groups per key
+  const V* lutv = reinterpret_cast<const V*>(__builtin_assume_aligned(lut, 16));
+  constexpr int CBG = CB / NS;             // code bytes per scale group
+  constexpr int KG = CSB / NS;             // coset (parity) bytes per scale group
+  static_assert(CB % NS == 0 && CSB % NS == 0, "scale groups must cover whole bytes");
   const int64_t t0 = (int64_t)blockIdx.x * chunk;
   const int64_t t1 = min(a.T, t0 + chunk);
   const int64_t base = (s * a.H + h) * a.pT;   // packed planes: token stride pT
@@ -1203,27 +1248,23 @@ __global__ __launch_bounds__(kLutBlock) void score_lut_kernel(ScoreArgs a,
     float score[HPP];
 #pragma unroll
     for (int hh = 0; hh < HPP; ++hh) score[hh] = 0.f;
-    for (int g = 0; g < ns; ++g) {
-      float acc[HPP];
 #pragma unroll
-      for (int hh = 0; hh < HPP; ++hh) acc[hh] = 0.f;
-      const int b0 = g * gl * BITS, b1 = b0 + gl * BITS;   // code bytes of group
+    for (int g = 0; g < NS; ++g) {
+      LutAcc<V> acc;
+      acc.zero();
 #pragma unroll
-      for (int b = 0; b < CB; ++b) {
-        if (b < b0 || b >= b1) continue;
+      for (int b = g * CBG; b < (g + 1) * CBG; ++b) {
         const uint32_t v = (cw[b >> 2] >> (8 * (b & 3))) & 0xffu;
-        lut_add(acc, reinterpret_cast<const V*>(lut)[b * 256 + v]);
+        acc.add(lutv[b * 256 + v]);
       }
-      const int k0 = (g * gl) >> 3, k1 = ((g + 1) * gl + 7) >> 3;
 #pragma unroll
-      for (int k = 0; k < CSB; ++k) {
-        if (k < k0 || k >= k1) continue;
+      for (int k = g * KG; k < (g + 1) * KG; ++k) {
         const uint32_t v = (cs >> (8 * k)) & 0xffu;
-        lut_add(acc, reinterpret_cast<const V*>(lut)[(CB + k) * 256 + v]);
+        acc.add(lutv[(CB + k) * 256 + v]);
       }
       const float sc = h2f(a.scales[vec * a.n_scales + g]);
 #pragma unroll
-      for (int hh = 0; hh < HPP; ++hh) score[hh] = fmaf(acc[hh], sc, score[hh]);
+      for (int hh = 0; hh < HPP; ++hh) score[hh] = fmaf(acc.get(hh), sc, score[hh]);
     }
 #pragma unroll
     for (int hh = 0; hh < HPP; ++hh)
@@ -1546,24 +1587,51 @@ hipError_t dequantize_n(const TensorArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BITS, int N, int HPP, typename T>
+template <int BITS, int N, int HPP, typename T, int NS>
 hipError_t score_lut_launch(const ScoreArgs& a, int n_pass, hipStream_t s) {
   constexpr int CB = N * BITS / 8, NG = N / 8, CSB = (NG + 7) / 8;
   const size_t lds = sizeof(float) * ((size_t)(CB + CSB) * 256 * HPP + HPP * N + HPP * NG);
-  auto kern = a.compact ? score_lut_kernel<BITS, N, HPP, T, true>
-                        : score_lut_kernel<BITS, N, HPP, T, false>;
+  auto kern = a.compact ? score_lut_kernel<BITS, N, HPP, T, true, NS>
+                        : score_lut_kernel<BITS, N, HPP, T, false, NS>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  // enough workgroups to cover the chip when there are few (slab, head) pairs
+  // The tables take most of a CU's LDS, so one workgroup runs per CU: with
+  // 256 or more (slab, head, pass) triples each builds its tables once and
+  // streams all its keys; fewer are split over token chunks to cover the CUs.
   const int64_t pairs = a.S * a.H * n_pass;
-  int64_t n_chunks = (1024 + pairs - 1) / pairs;
+  int64_t n_chunks = (256 + pairs - 1) / pairs;
   const int64_t min_chunk = 4 * kLutBlock;
   n_chunks = max((int64_t)1, min(n_chunks, (a.T + min_chunk - 1) / min_chunk));
   const int64_t chunk = (a.T + n_chunks - 1) / n_chunks;
   const dim3 grid((unsigned)n_chunks, (unsigned)(a.H * n_pass), (unsigned)a.S);
   hipLaunchKernelGGL(kern, grid, dim3(kLutBlock), lds, s, a, n_pass, chunk);
   return hipGetLastError();
+}
+
+// Query heads whose tables fit in a CU's 160 KB of LDS (the launcher picks
+// hpp from the device's limit, never above this).
+template <int BITS, int N>
+constexpr int lut_max_hpp() {
+  constexpr int CB = N * BITS / 8, NG = N / 8, CSB = (NG + 7) / 8;
+  constexpr int per_head = 4 * ((CB + CSB) * 256 + N + NG);
+  return 160 * 1024 / per_head;
+}
+
+template <int BITS, int N, typename T, int NS>
+hipError_t score_lut_hpp(const ScoreArgs& a, int hpp, int n_pass, hipStream_t s) {
+  constexpr int kMax = lut_max_hpp<BITS, N>();
+  if (hpp == 1) return score_lut_launch<BITS, N, 1, T, NS>(a, n_pass, s);
+  if constexpr (kMax >= 2) {
+    if (hpp == 2) return score_lut_launch<BITS, N, 2, T, NS>(a, n_pass, s);
+  }
+  if constexpr (kMax >= 3) {
+    if (hpp == 3) return score_lut_launch<BITS, N, 3, T, NS>(a, n_pass, s);
+  }
+  if constexpr (kMax >= 4) {
+    if (hpp == 4) return score_lut_launch<BITS, N, 4, T, NS>(a, n_pass, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int BITS, int N, typename T>
@@ -1576,12 +1644,15 @@ hipError_t score_lut_n(const ScoreArgs& a, int max_lds, hipStream_t s) {
   if (hpp_max > 4) hpp_max = 4;
   const int n_pass = (grp + hpp_max - 1) / hpp_max;
   const int hpp = (grp + n_pass - 1) / n_pass;
-  switch (hpp) {
-    case 1: return score_lut_launch<BITS, N, 1, T>(a, n_pass, s);
-    case 2: return score_lut_launch<BITS, N, 2, T>(a, n_pass, s);
-    case 3: return score_lut_launch<BITS, N, 3, T>(a, n_pass, s);
-    default: return score_lut_launch<BITS, N, 4, T>(a, n_pass, s);
+  const int ns = N / a.G;   // 1, 2 or 4 (G = n or a multiple of 64)
+  if (ns == 1) return score_lut_hpp<BITS, N, T, 1>(a, hpp, n_pass, s);
+  if constexpr (N >= 128) {
+    if (ns == 2) return score_lut_hpp<BITS, N, T, 2>(a, hpp, n_pass, s);
   }
+  if constexpr (N >= 256) {
+    if (ns == 4) return score_lut_hpp<BITS, N, T, 4>(a, hpp, n_pass, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int N, int BITS, typename T>
