@@ -945,6 +945,106 @@ __global__ __launch_bounds__(kBlock) void dequantize_fast_kernel(TensorArgs a,
   }
 }
 
+// Token-walking variant for tensors without RoPE (values; keys with theta =
+// 0), n = 64 or 128: wave -> ((slab, head) plane, run of kTwTiles token
+// tiles).  The wave first copies the run's packed bytes (codes, cosets,
+// scales: each a contiguous stretch of its plane) into its LDS slice with
+// 16-byte loads, then walks the tiles reading only LDS, so its stores are
+// never held up by a load and each wave writes one contiguous stretch of the
+// output.  (The plane-walking kernel keeps each lane's RoPE rows in
+// registers, which needs a fixed token tile per wave.)
+constexpr int kTwTiles = 32;
+
+__device__ __forceinline__ int align16(int x) { return (x + 15) & ~15; }
+
+// bytes of one wave's LDS slice
+__host__ __device__ __forceinline__ int tw_slice_bytes(int run, int code_bytes,
+                                                       int coset_bytes, int n_scales) {
+  return ((run * code_bytes + 15) & ~15) + ((run * coset_bytes + 15) & ~15) +
+         ((run * n_scales * 2 + 15) & ~15);
+}
+
+template <int N, int BITS, typename OutT, bool CMP>
+__global__ __launch_bounds__(kBlock) void dequantize_tw_kernel(TensorArgs a) {
+  constexpr int VL = N / 8;
+  constexpr int TPW = 64 / VL;
+  constexpr int L = 1 << BITS;
+  constexpr int CB = N * BITS / 8;          // code bytes per vector (16 .. 48)
+  constexpr int RUN = kTwTiles * TPW;       // tokens per run
+  static_assert(CB % 16 == 0, "16-byte staging of the code rows");
+  extern __shared__ __align__(16) uint8_t smem[];
+  const int lane = threadIdx.x & 63;
+  const int row = lane / VL;
+  const int l = lane % VL;
+  const int m = lane_group(l);
+  const int csb = a.coset_bytes, ns = a.n_scales;
+  uint8_t* lc = smem + (threadIdx.x >> 6) * tw_slice_bytes(RUN, CB, csb, ns);
+  uint8_t* lq = lc + RUN * CB;
+  uint16_t* lg = reinterpret_cast<uint16_t*>(lq + align16(RUN * csb));
+  const int64_t n_tt = (a.T + TPW - 1) / TPW;
+  const int64_t n_run = (n_tt + kTwTiles - 1) / kTwTiles;
+  const int64_t SH = a.n_vec / a.T;
+  const int64_t wave = xcd_wave_id();
+  const int64_t sh = wave / n_run;
+  if (sh >= SH) return;                     // whole wave; no block barrier below
+  const int64_t tt0 = (wave % n_run) * kTwTiles;
+  const int64_t tok0 = tt0 * TPW;
+  const int nt = (int)min((int64_t)RUN, a.T - tok0);   // tokens of this run
+  const int64_t v0 = sh * a.pT + tok0;                 // first packed vector
+  {
+    // codes: nt * CB bytes, 16-byte aligned at both ends
+    const uint4* gc = reinterpret_cast<const uint4*>(a.codes + v0 * CB);
+    uint4* dc = reinterpret_cast<uint4*>(lc);
+    for (int i = lane; i < nt * (CB / 16); i += 64) dc[i] = gc[i];
+    if (!CMP) {
+      const uint8_t* gq = a.cosets + v0 * csb;
+      for (int i = lane; i < nt * csb; i += 64) lq[i] = gq[i];
+    }
+    const uint16_t* gg = a.scales + v0 * ns;
+    for (int i = lane; i < nt * ns; i += 64) lg[i] = gg[i];
+  }
+  // the slice is written and read by this wave only; LDS operations of a
+  // wave complete in order, and the wait makes the writes visible
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  const int j0 = 8 * m;
+  const bool data_lane = j0 < a.d;
+  const int gl = a.G >> 3;
+  const bool neg_sigma = (__builtin_popcount(m) & 1) != 0;
+  float coef[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) coef[k] = ((m >> k) & 1) ? -1.f : 1.f;
+  const uint32_t flip = neg_sigma ? OutIo<OutT>::kFlip : 0u;
+  const int n_tiles = (nt + TPW - 1) / TPW;
+  for (int it = 0; it < n_tiles; ++it) {
+    const int lt = min(it * TPW + row, nt - 1);   // token within the run
+    uint32_t code;
+    if (BITS == 2) {
+      code = *reinterpret_cast<const uint16_t*>(lc + lt * CB + m * BITS);
+    } else {
+      const uint8_t* cp = lc + lt * CB + m * BITS;
+      code = (uint32_t)cp[0] | ((uint32_t)cp[1] << 8) | ((uint32_t)cp[2] << 16);
+    }
+    int c = CMP ? 0 : (int)((lq[lt * csb + (m >> 3)] >> (m & 7)) & 1u);
+    if (CMP) code = Compact<BITS>::unfold(code, c);
+    const float sc = h2f(lg[lt * ns + m / gl]) * a.inv_sqrt_n;
+    const float off = (0.5f * (float)c - a.half_L) * sc;
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t idx = (code >> (BITS * k)) & (uint32_t)(L - 1);
+      v[k] = __fmaf_rn((float)idx, sc, off);
+    }
+    fwht_lane(v);
+    if (VL > 1) stage_fmac<0>(v, coef[0]);
+    if (VL > 2) stage_fmac<1>(v, coef[1]);
+    if (VL > 4) stage_fmac<2>(v, coef[2]);
+    if (VL > 8) stage_fmac<3>(v, coef[3]);
+    if (it * TPW + row < nt && data_lane)
+      OutIo<OutT>::store8(a.y, (sh * a.T + tok0 + it * TPW + row) * a.d + j0, v, flip);
+  }
+}
+
 template <int N, int BITS, typename OutT>
 __global__ __launch_bounds__(kBlock) void dequantize_kernel(TensorArgs a) {
   constexpr int VL = N / 8;
@@ -1573,7 +1673,30 @@ hipError_t dequantize_fast_launch(const TensorArgs& a, hipStream_t s) {
 }
 
 template <int N, int BITS, typename T>
+hipError_t dequantize_tw_launch(const TensorArgs& a, hipStream_t s) {
+  constexpr int TPW = 64 / (N / 8);
+  constexpr int RUN = kTwTiles * TPW;
+  const int64_t SH = a.n_vec / a.T;
+  const int64_t n_tt = (a.T + TPW - 1) / TPW;
+  const int64_t waves = SH * ((n_tt + kTwTiles - 1) / kTwTiles);
+  const int64_t blocks = ((waves + kBlock / 64 - 1) / (kBlock / 64) + 7) / 8 * 8;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  const size_t lds = (size_t)(kBlock / 64) *
+                     tw_slice_bytes(RUN, N * BITS / 8, a.coset_bytes, a.n_scales);
+  auto kern = a.compact ? dequantize_tw_kernel<N, BITS, T, true>
+                        : dequantize_tw_kernel<N, BITS, T, false>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kBlock), lds, s, a);
+  return hipGetLastError();
+}
+
+template <int N, int BITS, typename T>
 hipError_t dequantize_n(const TensorArgs& a, hipStream_t s) {
+  if constexpr ((N == 64 || N == 128) && (N * BITS / 8) % 16 == 0) {
+    if (a.rope == nullptr) return dequantize_tw_launch<N, BITS, T>(a, s);
+  }
   if constexpr (N <= 128) {
     if (a.rope == nullptr) return dequantize_fast_launch<N, BITS, T, 0>(a, s);
     if (a.d == 8) return dequantize_fast_launch<N, BITS, T, 3>(a, s);
