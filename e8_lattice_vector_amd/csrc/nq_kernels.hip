@@ -517,17 +517,20 @@ __device__ __forceinline__ int64_t xcd_wave_id() {
 template <bool STRICT>
 __device__ __forceinline__ void e8_decode2(const float g[8], uint32_t& code,
                                            uint64_t& cosets, int& coset) {
+  // With e = |t| - 1: min(|t|, 3 - a) = 1 - |e| and kappa = 1 - |e| exactly
+  // (|t| is a multiple of 2^-24 in [0, 3]), so D1 - D0 = 8 - 2 sum |e|, the
+  // strict step takes the smallest |e| (lowest index on ties) and costs
+  // 4 |e|.  |.| comes free as a source modifier.
   uint32_t X = 0, Bn = 0, f0 = 1u << 14, f1 = 0;
-  float acc = 0.f, best0, best1 = -INFINITY;
+  float acc = 0.f, best0, best1 = INFINITY;
 #pragma unroll
   for (int k = 7; k >= 0; --k) {
-    const float a = fabsf(g[k]);
-    const float t = a - 1.0f;
+    const float t = fabsf(g[k]) - 1.0f;
     const float at = fabsf(t);
-    const float w = 3.0f - a;
+    const float ae = fabsf(at - 1.0f);
     X = shift_in(X, g[k], 2);
     Bn = shift_in(Bn, t, 1);
-    acc = acc + fminf(at, w);
+    acc = acc + ae;
     if (k == 7) {
       best0 = at;
     } else if (at <= best0) {
@@ -535,16 +538,15 @@ __device__ __forceinline__ void e8_decode2(const float g[8], uint32_t& code,
       f0 = 1u << (2 * k);
     }
     if (STRICT) {
-      const float k1 = (a >= 2.f) ? w : at;
-      if (k1 >= best1) { best1 = k1; f1 = 1u << (2 * k); }
+      if (ae <= best1) { best1 = ae; f1 = 1u << (2 * k); }
     }
   }
   const uint32_t odd0 = __builtin_popcount(Bn) & 1u;
-  float lhs = __fmaf_rn(2.f, acc, -8.f);
+  float lhs = __fmaf_rn(-2.f, acc, 8.f);
   uint32_t odd1 = 0;
   if (STRICT) {
     odd1 = __builtin_popcount(X) & 1u;
-    if (odd1) lhs = lhs + __fmaf_rn(-4.f, best1, 4.f);
+    if (odd1) lhs = lhs + 4.f * best1;
   }
   const float rhs = odd0 ? 4.f * best0 : 0.f;
   const int c = lhs < rhs ? 1 : 0;
