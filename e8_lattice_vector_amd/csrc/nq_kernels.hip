@@ -1507,6 +1507,210 @@ __global__ __launch_bounds__((att_block<BITS, HPP>())) void attend_kernel(Attend
   }
 }
 
+// The same value sum on the matrix cores, for 2-bit values with one scale per
+// vector at n = 128 (one 16 x 16 x 32 bf16 product per 32 tokens and 16
+// coordinates).  z_h[j] = sum_t (w_h,t s_t) (idx_t,j - 2 + c_t/2) is a dense
+// contraction over tokens: the A operand holds the weights (rows: query heads),
+// the B operand the code values (columns: the 8-groups), K runs over tokens.
+//  * B: 64 (idx - 2 + c/2) is a signed byte: (idx ^ 2) in its two top bits and
+//    the coset bit below them; it converts exactly to fp32 and to bf16, so the
+//    centred values (no cancellation against the sum of the weights) carry no
+//    rounding.  The factor 64 is removed at the end.
+//  * A: w s in fp32, split into its top 16 bits (hi, rows 0..7) and the bf16
+//    truncation of the remainder (lo, rows 8..15); hi + lo differs from w s
+//    by less than 2^-14 |w s|.  D = hi-rows + lo-rows.
+// Lane l supplies A row l % 16 and B column l % 16 for the 8 tokens
+// 8 (l / 16) .. + 7 of the chunk, and holds D rows 4 (l / 16) .. + 3 of
+// column l % 16.  Column g of block (q, half) is coordinate 8 g + 4 half + q.
+// ---------------------------------------------------------------------------
+typedef __bf16 nq_bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t nq_u4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float i8_to_f(uint32_t x, int byte) {
+  return (float)(int)(int8_t)(x >> (8 * byte));
+}
+
+// One lane's share of a 32-token chunk: the group words of its 8-group for
+// tokens tb .. tb + 7 (two per word), their coset words (two per word), their
+// scales (two per word) and its query head's weights.
+struct AttChunk {
+  uint32_t cw[4], cs[4], sw[4];
+  float wt[8];
+};
+
+// FULL: tokens tb .. tb + 7 all exist and the scale / coset planes and the
+// weight rows are 16-byte aligned there.  Otherwise indices are clamped to
+// the last token and the weights of missing tokens are 0.
+template <bool FULL, bool CMP>
+__device__ __forceinline__ void att_load(AttChunk& k, const uint8_t* __restrict__ cp,
+                                         const uint16_t* __restrict__ csp,
+                                         const uint16_t* __restrict__ scp,
+                                         const float* __restrict__ wr, int tb, int T,
+                                         bool arow) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t t0 = FULL ? tb + 2 * j : min(tb + 2 * j, T - 1);
+    const uint32_t t1 = FULL ? tb + 2 * j + 1 : min(tb + 2 * j + 1, T - 1);
+    k.cw[j] = (uint32_t)*reinterpret_cast<const uint16_t*>(cp + t0 * 32u) |
+              ((uint32_t)*reinterpret_cast<const uint16_t*>(cp + t1 * 32u) << 16);
+    if (!FULL) {
+      k.sw[j] = (uint32_t)scp[t0] | ((uint32_t)scp[t1] << 16);
+      if (!CMP) k.cs[j] = (uint32_t)csp[t0] | ((uint32_t)csp[t1] << 16);
+    }
+  }
+  if (FULL) {
+    const uint4 sv = *reinterpret_cast<const uint4*>(scp + (uint32_t)tb);
+    k.sw[0] = sv.x; k.sw[1] = sv.y; k.sw[2] = sv.z; k.sw[3] = sv.w;
+    if (!CMP) {
+      const uint4 cv = *reinterpret_cast<const uint4*>(csp + (uint32_t)tb);
+      k.cs[0] = cv.x; k.cs[1] = cv.y; k.cs[2] = cv.z; k.cs[3] = cv.w;
+    }
+  }
+  if (arow) {
+    if (FULL) {
+      const float4 w0 = *reinterpret_cast<const float4*>(wr + (uint32_t)tb);
+      const float4 w1 = *reinterpret_cast<const float4*>(wr + (uint32_t)tb + 4);
+      k.wt[0] = w0.x; k.wt[1] = w0.y; k.wt[2] = w0.z; k.wt[3] = w0.w;
+      k.wt[4] = w1.x; k.wt[5] = w1.y; k.wt[6] = w1.z; k.wt[7] = w1.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) k.wt[i] = tb + i < T ? wr[(uint32_t)(tb + i)] : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) k.wt[i] = 0.f;
+  }
+}
+
+template <bool CMP>
+__device__ __forceinline__ void att_mma(nq_f4 (&acc)[4][2], const AttChunk& k, int col,
+                                        uint32_t pmask) {
+  nq_u4 av;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float x[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const float ws = k.wt[2 * j + e] * h2f((uint16_t)(k.sw[j] >> (16 * e)));
+      x[e] = ws - __uint_as_float(__float_as_uint(ws) & pmask);
+    }
+    av[j] = __builtin_amdgcn_perm(__float_as_uint(x[1]), __float_as_uint(x[0]), 0x07060302u);
+  }
+  const nq_bf16x8 A = __builtin_bit_cast(nq_bf16x8, av);
+  uint32_t xa[4], C[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    uint32_t x = k.cw[j];
+    uint32_t cb;
+    if (CMP) {
+      cb = (x >> 14) & 0x00010001u;
+      const uint32_t p0 = (uint32_t)__builtin_popcount(x & 0x00001555u) & 1u;
+      const uint32_t p1 = (uint32_t)__builtin_popcount(x & 0x15550000u) & 1u;
+      x = (x & ~0x40004000u) | (p0 << 14) | (p1 << 30);
+    } else {
+      cb = (k.cs[j] >> col) & 0x00010001u;
+    }
+    C[j] = __umul24(cb, 0x2020u);
+    xa[j] = x ^ 0xaaaaaaaau;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    nq_bf16x8 B0, B1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t t = ((xa[j] << (6 - 2 * q)) & 0xc0c0c0c0u) | C[j];
+      B0[2 * j] = (__bf16)i8_to_f(t, 0);
+      B0[2 * j + 1] = (__bf16)i8_to_f(t, 2);
+      B1[2 * j] = (__bf16)i8_to_f(t, 1);
+      B1[2 * j + 1] = (__bf16)i8_to_f(t, 3);
+    }
+    acc[q][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B0, acc[q][0], 0, 0, 0);
+    acc[q][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B1, acc[q][1], 0, 0, 0);
+  }
+}
+
+template <int HPP, bool CMP>
+__global__ __launch_bounds__(1024) void attend_mfma_kernel(AttendArgs a, int n_pass) {
+  constexpr int N = 128;
+  constexpr int U = 2;                     // chunks of 32 tokens per wave per step
+  extern __shared__ float lds[];           // [n_waves][HPP][N]
+  const int64_t s = blockIdx.z;
+  const int h = blockIdx.y / n_pass;
+  const int pass = blockIdx.y % n_pass;
+  const int grp = a.Hq / a.H;
+  const int hq0 = h * grp + pass * HPP;
+  const int nh = min(HPP, h * grp + grp - hq0);
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int col = lane & 15;               // B column = 8-group; A row
+  const int kg = lane >> 4;                // tokens 8 kg .. 8 kg + 7 of a chunk
+  const int hh = col & 7;                  // the A row's query head
+  const bool arow = hh < nh;
+  const uint32_t pmask = col >= 8 ? 0xffff0000u : 0u;
+  const int T = (int)a.T;
+  const int64_t base = (s * a.H + h) * a.pT;
+  const float* wr = a.w + (s * a.Hq + hq0 + (arow ? hh : 0)) * a.T;
+  const uint8_t* cp = a.codes + base * (N / 4) + 2 * col;
+  const uint16_t* csp = reinterpret_cast<const uint16_t*>(a.cosets) + base;
+  const uint16_t* scp = a.scales + base;
+  const bool vec = (T & 3) == 0 &&
+                   (((uintptr_t)scp | (CMP ? (uintptr_t)0 : (uintptr_t)csp)) & 15) == 0;
+  nq_f4 acc[4][2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q][0] = acc[q][1] = nq_f4{0.f, 0.f, 0.f, 0.f};
+  const int step = nw * 32;
+  for (int c0 = wv * 32; c0 < T; c0 += U * step) {
+    AttChunk k[U];
+    if (vec && c0 + (U - 1) * step + 32 <= T) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        att_load<true, CMP>(k[u], cp, csp, scp, wr, c0 + u * step + 8 * kg, T, arow);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        att_load<false, CMP>(k[u], cp, csp, scp, wr, c0 + u * step + 8 * kg, T, arow);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) att_mma<CMP>(acc, k[u], col, pmask);
+  }
+  // rows 8..15 (lanes 32..63) hold the low parts of rows 0..7 (lanes 0..31)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float v = acc[q][hf][r] + __shfl_xor(acc[q][hf][r], 32);
+        const int head = 4 * kg + r;
+        if (kg < 2 && head < HPP) lds[(wv * HPP + head) * N + 8 * col + 4 * hf + q] = v;
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < HPP * N; i += blockDim.x) {
+    float sum = 0.f;
+    for (int w = 0; w < nw; ++w) sum += lds[w * HPP * N + i];
+    lds[i] = sum;
+  }
+  __syncthreads();
+  for (int hs = 1; hs < N; hs <<= 1) {
+    for (int i = threadIdx.x; i < HPP * (N / 2); i += blockDim.x) {
+      const int g = i / (N / 2), r = i % (N / 2);
+      const int j = (r / hs) * 2 * hs + (r % hs);
+      const float x0 = lds[g * N + j], x1 = lds[g * N + j + hs];
+      lds[g * N + j] = x0 + x1;
+      lds[g * N + j + hs] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  const float osc = a.inv_sqrt_n * (1.f / 64.f);
+  for (int i = threadIdx.x; i < nh * a.d; i += blockDim.x) {
+    const int g = i / a.d, j = i % a.d;
+    a.out[(s * a.Hq + hq0 + g) * (int64_t)a.d + j] = lds[g * N + j] * osc;
+  }
+}
+
 // Nearest point of the whole lattice, no cube limit (the textbook
 // Conway-Sloane decoder on D8 and on D8 + 1/2 (strict) or Z^8 + 1/2
 // (relaxed)), with the same tie rules as the cube decoder: rounding ties away
@@ -1846,9 +2050,32 @@ hipError_t attend_launch(const AttendArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int HPP>
+hipError_t attend_mfma_launch(const AttendArgs& a, hipStream_t s) {
+  constexpr int kThreads = 1024;
+  const int grp = a.Hq / a.H;
+  const int n_pass = (grp + HPP - 1) / HPP;
+  const size_t lds = sizeof(float) * (size_t)(kThreads / 64) * HPP * 128;
+  auto kern = a.compact ? attend_mfma_kernel<HPP, true> : attend_mfma_kernel<HPP, false>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const dim3 grid(1u, (unsigned)(a.H * n_pass), (unsigned)a.S);
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, a, n_pass);
+  return hipGetLastError();
+}
+
 template <int BITS, int N>
 hipError_t attend_n(const AttendArgs& a, hipStream_t s) {
   const int grp = a.Hq / a.H;
+  if constexpr (BITS == 2 && N == 128) {
+    if (a.n_scales == 1 && a.T < ((int64_t)1 << 26)) {
+      if (grp <= 1) return attend_mfma_launch<1>(a, s);
+      if (grp <= 2) return attend_mfma_launch<2>(a, s);
+      if (grp <= 4) return attend_mfma_launch<4>(a, s);
+      return attend_mfma_launch<8>(a, s);
+    }
+  }
   if (grp <= 1) return attend_launch<BITS, N, 1>(a, s);
   if (grp <= 2) return attend_launch<BITS, N, 2>(a, s);
   if (grp <= 4 || N > 128) return attend_launch<BITS, N, 4>(a, s);

@@ -300,6 +300,36 @@ def test_attend_parity(cfg, grp, signed):
                   oracle_codec(cfg, True), "attend")
 
 
+@pytest.mark.parametrize("d,parity,packing,grp,T,signed,t0", [
+    (128, R_, 0, 8, 2084, False, 0),     # 8 heads a pass, full chunks and a tail
+    (128, S_, 0, 1, 4096, True, 0),
+    (128, S_, CP, 2, 37, False, 0),      # one partial chunk
+    (128, R_, 0, 12, 1000, True, 0),     # passes of 8 and 4 heads
+    (96, R_, 0, 4, 3000, False, 0),      # d < n
+    (128, R_, 0, 4, 1200, False, 5),     # window at an unaligned token offset
+    (128, S_, CP, 4, 2048, True, 64),    # window at an aligned offset
+    (128, R_, 0, 4, 1, False, 0),
+])
+def test_attend_one_scale_shapes(d, parity, packing, grp, T, signed, t0):
+    """2-bit values with one scale per vector (the matrix-core contraction):
+    head counts, ragged and tiny token counts, token windows."""
+    cfg = nq.Config(d, 2, 2, 0, parity, F16, 0.0, packing=packing)
+    S, H = 2, 2
+    log(f"[attend1] d={d} parity={parity} packing={packing} grp={grp} T={T} t0={t0}")
+    _, v = _inputs(cfg, S, H, T, 21)
+    pv = nq.alloc_packed(cfg, True, S, H, t0 + T + 3, DEV)
+    nq.quantize_kv(cfg, None, v, pv=pv, token_offset=t0)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(13)
+    x = torch.randn((S, H * grp, T), generator=g, device=DEV)
+    w = (x if signed else torch.softmax(x * 3, dim=-1)).contiguous()
+    out = nq.attend_packed_values(cfg, pv, w, S, H, T, token_offset=t0)
+    torch.cuda.synchronize()
+    planes = [pl[:, :, t0:t0 + T].cpu().numpy() for pl in (pv.codes, pv.cosets, pv.scales)]
+    _check_attend(out.cpu().numpy(), w.cpu().numpy().astype(np.float64), planes,
+                  oracle_codec(cfg, True), "attend1")
+
+
 def test_attend_llama_full_sampled():
     """Llama-3.1-8B 32K values, 32 query heads (GQA 4), softmax weights;
     every output of 4 sampled (slab, KV head) pairs checked against the
