@@ -1522,6 +1522,8 @@ __global__ __launch_bounds__((att_block<BITS, HPP>())) void attend_kernel(Attend
 // Lane l supplies A row l % 16 and B column l % 16 for the 8 tokens
 // 8 (l / 16) .. + 7 of the chunk, and holds D rows 4 (l / 16) .. + 3 of
 // column l % 16.  Column g of block (q, half) is coordinate 8 g + 4 half + q.
+// This form serves passes of 5..8 query heads; up to 4 heads use the table
+// form further down, which needs fewer instructions per token.
 // ---------------------------------------------------------------------------
 typedef __bf16 nq_bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t nq_u4 __attribute__((ext_vector_type(4)));
@@ -1708,6 +1710,152 @@ __global__ __launch_bounds__(1024) void attend_mfma_kernel(AttendArgs a, int n_p
   for (int i = threadIdx.x; i < nh * a.d; i += blockDim.x) {
     const int g = i / a.d, j = i % a.d;
     a.out[(s * a.Hq + hq0 + g) * (int64_t)a.d + j] = lds[g * N + j] * osc;
+  }
+}
+
+// Variant for up to 4 query heads a pass: the 16 A rows are (head, hi / lo
+// part, sub) and the two bf16 of a K-slot pair are two coordinates of one
+// token (sub 0 and 1), so a lookup in a 4 KB LDS table -- entry (c, code byte)
+// holds the bf16 of idx - 2 + c/2 for the byte's 4 coordinates -- yields B
+// operand words directly.  Column g of block b holds coordinates 8 g + 2 b
+// (sub 0) and 8 g + 2 b + 1 (sub 1); the A row of sub 0 carries the weight in
+// the low bf16 of each pair and 0 in the high one, sub 1 the reverse.
+template <bool CMP>
+__device__ __forceinline__ void att_mma4(nq_f4 (&acc)[4], const AttChunk& k,
+                                         const uint2* __restrict__ tbl, int col,
+                                         uint32_t pmask, uint32_t asel) {
+  const char* tb = reinterpret_cast<const char*>(tbl);
+#pragma unroll
+  for (int hc = 0; hc < 2; ++hc) {
+    nq_u4 av;
+    uint32_t bw[4][4];
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      const int w = 2 * hc + jp;           // tokens 2 w and 2 w + 1 of the lane
+      uint32_t cw = k.cw[w];
+      uint32_t cc;                          // their coset bits at bits 0 and 16
+      if (CMP) {
+        cc = (cw >> 14) & 0x00010001u;
+        const uint32_t p0 = (uint32_t)__builtin_popcount(cw & 0x00001555u) & 1u;
+        const uint32_t p1 = (uint32_t)__builtin_popcount(cw & 0x15550000u) & 1u;
+        cw = (cw & ~0x40004000u) | (p0 << 14) | (p1 << 30);
+      } else {
+        cc = (k.cs[w] >> col) & 0x00010001u;
+      }
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int j = 2 * jp + e;
+        const float ws = k.wt[2 * w + e] * h2f((uint16_t)(k.sw[w] >> (16 * e)));
+        const float x = ws - __uint_as_float(__float_as_uint(ws) & pmask);
+        av[j] = __builtin_amdgcn_perm(__float_as_uint(x), __float_as_uint(x), asel);
+        // 16-bit halves: table indices (code byte 0 | c << 8), (code byte 1 | c << 8)
+        const uint32_t ix = __builtin_amdgcn_perm(cc, cw, e ? 0x06030602u : 0x04010400u);
+        const uint32_t ad = ((ix << 3) & 0xfff8fff8u);
+        const uint2 e0 = *reinterpret_cast<const uint2*>(tb + (ad & 0xffffu));
+        const uint2 e1 = *reinterpret_cast<const uint2*>(tb + (ad >> 16));
+        bw[0][j] = e0.x;
+        bw[1][j] = e0.y;
+        bw[2][j] = e1.x;
+        bw[3][j] = e1.y;
+      }
+    }
+    const nq_bf16x8 A = __builtin_bit_cast(nq_bf16x8, av);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const nq_u4 bv = {bw[b][0], bw[b][1], bw[b][2], bw[b][3]};
+      acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(nq_bf16x8, bv),
+                                                       acc[b], 0, 0, 0);
+    }
+  }
+}
+
+template <int HPP, bool CMP>
+__global__ __launch_bounds__(1024) void attend_mfma4_kernel(AttendArgs a, int n_pass) {
+  static_assert(HPP <= 4, "rows are (head, part, sub)");
+  constexpr int N = 128;
+  constexpr int U = 2;                     // chunks of 32 tokens per wave per step
+  extern __shared__ float red[];           // [n_waves][HPP][N]
+  __shared__ uint2 tbl[512];               // entry c * 256 + code byte
+  uint32_t* tw = reinterpret_cast<uint32_t*>(tbl);
+  for (int i = threadIdx.x; i < 1024; i += blockDim.x) {
+    const int c = i >> 9, byte = (i >> 1) & 255, f = 4 * (i & 1);
+    const float lo = (float)((byte >> f) & 3) - 2.f + 0.5f * (float)c;
+    const float hi = (float)((byte >> (f + 2)) & 3) - 2.f + 0.5f * (float)c;
+    tw[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+  }
+  const int64_t s = blockIdx.z;
+  const int h = blockIdx.y / n_pass;
+  const int pass = blockIdx.y % n_pass;
+  const int grp = a.Hq / a.H;
+  const int hq0 = h * grp + pass * HPP;
+  const int nh = min(HPP, h * grp + grp - hq0);
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int col = lane & 15;               // B column = 8-group; A row
+  const int kg = lane >> 4;                // tokens 8 kg .. 8 kg + 7 of a chunk
+  const int hh = col & 3;                  // the A row's query head, part, sub
+  const bool arow = hh < nh;
+  const uint32_t pmask = (col & 4) ? 0xffff0000u : 0u;
+  const uint32_t asel = (col & 8) ? 0x03020c0cu : 0x0c0c0302u;
+  const int T = (int)a.T;
+  const int64_t base = (s * a.H + h) * a.pT;
+  const float* wr = a.w + (s * a.Hq + hq0 + (arow ? hh : 0)) * a.T;
+  const uint8_t* cp = a.codes + base * (N / 4) + 2 * col;
+  const uint16_t* csp = reinterpret_cast<const uint16_t*>(a.cosets) + base;
+  const uint16_t* scp = a.scales + base;
+  const bool vec = (T & 3) == 0 &&
+                   (((uintptr_t)scp | (CMP ? (uintptr_t)0 : (uintptr_t)csp)) & 15) == 0;
+  nq_f4 acc[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) acc[b] = nq_f4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  const int step = nw * 32;
+  for (int c0 = wv * 32; c0 < T; c0 += U * step) {
+    AttChunk k[U];
+    if (vec && c0 + (U - 1) * step + 32 <= T) {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        att_load<true, CMP>(k[u], cp, csp, scp, wr, c0 + u * step + 8 * kg, T, arow);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        att_load<false, CMP>(k[u], cp, csp, scp, wr, c0 + u * step + 8 * kg, T, arow);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) att_mma4<CMP>(acc, k[u], tbl, col, pmask, asel);
+  }
+  // rows 4..7 / 12..15 (lanes 16..31 / 48..63) hold the low parts of rows
+  // 0..3 / 8..11 (lanes 0..15 / 32..47); lanes 0..15 have sub 0, 32..47 sub 1
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = acc[b][r] + __shfl_xor(acc[b][r], 16);
+      if ((kg & 1) == 0 && r < HPP)
+        red[(wv * HPP + r) * N + 8 * col + 2 * b + (kg >> 1)] = v;
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < HPP * N; i += blockDim.x) {
+    float sum = 0.f;
+    for (int w = 0; w < nw; ++w) sum += red[w * HPP * N + i];
+    red[i] = sum;
+  }
+  __syncthreads();
+  for (int hs = 1; hs < N; hs <<= 1) {
+    for (int i = threadIdx.x; i < HPP * (N / 2); i += blockDim.x) {
+      const int g = i / (N / 2), r = i % (N / 2);
+      const int j = (r / hs) * 2 * hs + (r % hs);
+      const float x0 = red[g * N + j], x1 = red[g * N + j + hs];
+      red[g * N + j] = x0 + x1;
+      red[g * N + j + hs] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < nh * a.d; i += blockDim.x) {
+    const int g = i / a.d, j = i % a.d;
+    a.out[(s * a.Hq + hq0 + g) * (int64_t)a.d + j] = red[g * N + j] * a.inv_sqrt_n;
   }
 }
 
@@ -2065,14 +2213,29 @@ hipError_t attend_mfma_launch(const AttendArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int HPP>
+hipError_t attend_mfma4_launch(const AttendArgs& a, hipStream_t s) {
+  constexpr int kThreads = 1024;
+  const int grp = a.Hq / a.H;
+  const int n_pass = (grp + HPP - 1) / HPP;
+  const size_t lds = sizeof(float) * (size_t)(kThreads / 64) * HPP * 128;
+  auto kern = a.compact ? attend_mfma4_kernel<HPP, true> : attend_mfma4_kernel<HPP, false>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const dim3 grid(1u, (unsigned)(a.H * n_pass), (unsigned)a.S);
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, a, n_pass);
+  return hipGetLastError();
+}
+
 template <int BITS, int N>
 hipError_t attend_n(const AttendArgs& a, hipStream_t s) {
   const int grp = a.Hq / a.H;
   if constexpr (BITS == 2 && N == 128) {
     if (a.n_scales == 1 && a.T < ((int64_t)1 << 26)) {
-      if (grp <= 1) return attend_mfma_launch<1>(a, s);
-      if (grp <= 2) return attend_mfma_launch<2>(a, s);
-      if (grp <= 4) return attend_mfma_launch<4>(a, s);
+      if (grp <= 1) return attend_mfma4_launch<1>(a, s);
+      if (grp <= 2) return attend_mfma4_launch<2>(a, s);
+      if (grp <= 4) return attend_mfma4_launch<4>(a, s);
       return attend_mfma_launch<8>(a, s);
     }
   }
