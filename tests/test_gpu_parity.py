@@ -300,24 +300,31 @@ def test_attend_parity(cfg, grp, signed):
                   oracle_codec(cfg, True), "attend")
 
 
-@pytest.mark.parametrize("d,parity,packing,grp,T,signed,t0", [
-    (128, R_, 0, 8, 2084, False, 0),     # 8 heads a pass, full chunks and a tail
-    (128, S_, 0, 1, 4096, True, 0),
-    (128, S_, CP, 2, 37, False, 0),      # one partial chunk
-    (128, R_, 0, 12, 1000, True, 0),     # passes of 8 and 4 heads
-    (96, R_, 0, 4, 3000, False, 0),      # d < n
-    (128, R_, 0, 4, 1200, False, 5),     # window at an unaligned token offset
-    (128, S_, CP, 4, 2048, True, 64),    # window at an aligned offset
-    (128, R_, 0, 4, 1, False, 0),
+@pytest.mark.parametrize("d,parity,packing,grp,T,signed,t0,extra", [
+    (128, R_, 0, 8, 2084, False, 0, 3),     # 8 heads a pass, full chunks and a tail
+    (128, S_, 0, 1, 4096, True, 0, 3),
+    (128, S_, CP, 2, 37, False, 0, 3),      # one partial chunk
+    (128, R_, 0, 12, 1000, True, 0, 3),     # passes of 8 and 4 heads
+    (96, R_, 0, 4, 3000, False, 0, 3),      # d < n
+    (128, R_, 0, 4, 1200, False, 5, 3),     # window at an unaligned token offset
+    (128, S_, CP, 4, 2048, True, 64, 3),    # window at an aligned offset
+    (128, R_, 0, 4, 1, False, 0, 3),
+    # token stride a multiple of 8 and T of 4: 16-byte loads of scales, cosets, weights
+    (128, R_, 0, 4, 2084, False, 0, 4),     # pipelined chunks and a tail chunk
+    (128, S_, CP, 2, 64, True, 8, 0),       # aligned window; most waves idle
+    (128, R_, 0, 1, 20, False, 0, 4),       # tail chunk only
+    (96, S_, 0, 3, 4608, True, 0, 0),       # 3 heads in a 4-head pass
 ])
-def test_attend_one_scale_shapes(d, parity, packing, grp, T, signed, t0):
+def test_attend_one_scale_shapes(d, parity, packing, grp, T, signed, t0, extra):
     """2-bit values with one scale per vector (the matrix-core contraction):
-    head counts, ragged and tiny token counts, token windows."""
+    head counts, ragged and tiny token counts, token windows, plane
+    alignments with and without 16-byte metadata loads."""
     cfg = nq.Config(d, 2, 2, 0, parity, F16, 0.0, packing=packing)
     S, H = 2, 2
-    log(f"[attend1] d={d} parity={parity} packing={packing} grp={grp} T={T} t0={t0}")
+    log(f"[attend1] d={d} parity={parity} packing={packing} grp={grp} T={T} t0={t0} "
+        f"cap={t0 + T + extra}")
     _, v = _inputs(cfg, S, H, T, 21)
-    pv = nq.alloc_packed(cfg, True, S, H, t0 + T + 3, DEV)
+    pv = nq.alloc_packed(cfg, True, S, H, t0 + T + extra, DEV)
     nq.quantize_kv(cfg, None, v, pv=pv, token_offset=t0)
     g = torch.Generator(device=DEV)
     g.manual_seed(13)
