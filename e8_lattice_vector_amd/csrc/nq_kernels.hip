@@ -1720,6 +1720,19 @@ __global__ __launch_bounds__(1024) void attend_mfma_kernel(AttendArgs a, int n_p
 // operand words directly.  Column g of block b holds coordinates 8 g + 2 b
 // (sub 0) and 8 g + 2 b + 1 (sub 1); the A row of sub 0 carries the weight in
 // the low bf16 of each pair and 0 in the high one, sub 1 the reverse.
+// The 2-bit code values of one byte as bf16: entry c * 256 + byte holds
+// idx - 2 + c/2 for the byte's 4 coordinates (exact in bf16), low
+// coordinate first.  Written by the whole workgroup; a barrier must follow.
+__device__ __forceinline__ void value_table(uint2* tbl) {
+  uint32_t* tw = reinterpret_cast<uint32_t*>(tbl);
+  for (int i = threadIdx.x; i < 1024; i += blockDim.x) {
+    const int c = i >> 9, byte = (i >> 1) & 255, f = 4 * (i & 1);
+    const float lo = (float)((byte >> f) & 3) - 2.f + 0.5f * (float)c;
+    const float hi = (float)((byte >> (f + 2)) & 3) - 2.f + 0.5f * (float)c;
+    tw[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+  }
+}
+
 template <bool CMP>
 __device__ __forceinline__ void att_mma4(nq_f4 (&acc)[4], const AttChunk& k,
                                          const uint2* __restrict__ tbl, int col,
@@ -1776,13 +1789,7 @@ __global__ __launch_bounds__(1024) void attend_mfma4_kernel(AttendArgs a, int n_
   constexpr int U = 2;                     // chunks of 32 tokens per wave per step
   extern __shared__ float red[];           // [n_waves][HPP][N]
   __shared__ uint2 tbl[512];               // entry c * 256 + code byte
-  uint32_t* tw = reinterpret_cast<uint32_t*>(tbl);
-  for (int i = threadIdx.x; i < 1024; i += blockDim.x) {
-    const int c = i >> 9, byte = (i >> 1) & 255, f = 4 * (i & 1);
-    const float lo = (float)((byte >> f) & 3) - 2.f + 0.5f * (float)c;
-    const float hi = (float)((byte >> (f + 2)) & 3) - 2.f + 0.5f * (float)c;
-    tw[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
-  }
+  value_table(tbl);
   const int64_t s = blockIdx.z;
   const int h = blockIdx.y / n_pass;
   const int pass = blockIdx.y % n_pass;
@@ -1856,6 +1863,157 @@ __global__ __launch_bounds__(1024) void attend_mfma4_kernel(AttendArgs a, int n_
   for (int i = threadIdx.x; i < nh * a.d; i += blockDim.x) {
     const int g = i / a.d, j = i % a.d;
     a.out[(s * a.Hq + hq0 + g) * (int64_t)a.d + j] = red[g * N + j] * a.inv_sqrt_n;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Packed-key scores on the matrix cores, for 2-bit keys with one scale per
+// vector at n = 128.  With q~ = H pad(q) and p = idx - 2 + c/2,
+//   score = (s / sqrt n) sum_j q~_j p_j ,
+// a dense contraction over the coordinates j: for 16 keys at a time,
+// D[row][key] = sum_j A[row][j] B[j][key], B from the value table (exact
+// bf16) and A the rotated queries, split into bf16 hi (rows 0..3) and lo
+// (rows 4..7) parts (error below 2^-16 |q~_j| each).  Four 16x16x32 products
+// cover the 128 coordinates.  Lane (key l % 16, group block g = l / 16)
+// takes the 8-groups 4 g .. 4 g + 3 of its key (8 contiguous code bytes);
+// product b uses 8-group 4 g + b, whose two table entries are that lane's B
+// operand as they come.  D rows 0..3 + rows 4..7 are summed across lane
+// rows (v_permlane16_swap); each wave scores 32 consecutive keys per step, and two
+// workgroups share a CU.
+// ---------------------------------------------------------------------------
+constexpr int kScoreMfmaBlock = 1024;
+
+template <int HPP, typename QT, bool CMP>
+__global__ __launch_bounds__(kScoreMfmaBlock, 8) void score_mfma_kernel(ScoreArgs a, int n_pass,
+                                                                     int64_t chunk) {
+  static_assert(HPP <= 4, "rows are (head, part)");
+  constexpr int N = 128;
+  constexpr int U = 2;                     // 16-key blocks per wave per step
+  extern __shared__ float qt[];            // [HPP][N] rotated queries
+  __shared__ uint2 tbl[512];
+  value_table(tbl);
+  const int64_t s = blockIdx.z;
+  const int h = blockIdx.y / n_pass;
+  const int pass = blockIdx.y % n_pass;
+  const int grp = a.Hq / a.H;
+  const int hq0 = h * grp + pass * HPP;
+  const int nh = min(HPP, h * grp + grp - hq0);
+  for (int i = threadIdx.x; i < HPP * N; i += blockDim.x) {
+    const int hh = i / N, j = i % N;
+    qt[i] = (hh < nh && j < a.d)
+                ? Io<QT>::load1(a.q, (s * a.Hq + hq0 + hh) * (int64_t)a.d + j)
+                : 0.f;
+  }
+  __syncthreads();
+  for (int hs = 1; hs < N; hs <<= 1) {
+    for (int i = threadIdx.x; i < HPP * (N / 2); i += blockDim.x) {
+      const int hh = i / (N / 2), r = i % (N / 2);
+      const int j = (r / hs) * 2 * hs + (r % hs);
+      const float x0 = qt[hh * N + j], x1 = qt[hh * N + j + hs];
+      qt[hh * N + j] = x0 + x1;
+      qt[hh * N + j + hs] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int col = lane & 15;               // key of the block; A row
+  const int kg = lane >> 4;                // 8-groups 4 kg .. 4 kg + 3
+  const int hh = col & 3;
+  const bool arow = col < 8 && hh < nh;
+  nq_bf16x8 A[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    nq_u4 av;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t pr = 0;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float v = arow ? qt[hh * N + 8 * (4 * kg + b) + 2 * e + k] : 0.f;
+        const float hi = (float)(__bf16)v;
+        const float x = (col & 4) ? v - hi : v;
+        const uint32_t bits = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+        pr |= bits << (16 * k);
+      }
+      av[e] = pr;
+    }
+    A[b] = __builtin_bit_cast(nq_bf16x8, av);
+  }
+  const char* tb = reinterpret_cast<const char*>(tbl);
+  // this workgroup's keys t0 .. t0 + nk - 1 (nk < 2^26: 32-bit offsets)
+  const int64_t t0 = (int64_t)blockIdx.x * chunk;
+  const int nk = (int)(min(a.T, t0 + chunk) - t0);
+  const int64_t base = (s * a.H + h) * a.pT + t0;
+  const uint8_t* cp = a.codes + base * (N / 4);
+  const uint16_t* csp = reinterpret_cast<const uint16_t*>(a.cosets) + base;
+  const uint16_t* scp = a.scales + base;
+  float* op = a.out + (s * a.Hq + hq0) * a.T + t0;
+  const uint32_t cofs = 8u * (uint32_t)kg;
+  for (int kb = 16 * U * wv; kb < nk; kb += 16 * U * nw) {
+    uint2 cw[U];
+    uint32_t cs[U], sc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t t = (uint32_t)min(kb + 16 * u + col, nk - 1);
+      cw[u] = *reinterpret_cast<const uint2*>(cp + (t * (uint32_t)(N / 4) + cofs));
+      cs[u] = CMP ? 0u : (uint32_t)csp[t];
+      sc[u] = scp[t];
+    }
+    float v[U][4];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      uint32_t w[2] = {cw[u].x, cw[u].y};
+      uint32_t cc[2];
+      if (CMP) {
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          cc[d] = (w[d] >> 14) & 0x00010001u;
+          const uint32_t p0 = (uint32_t)__builtin_popcount(w[d] & 0x00001555u) & 1u;
+          const uint32_t p1 = (uint32_t)__builtin_popcount(w[d] & 0x15550000u) & 1u;
+          w[d] = (w[d] & ~0x40004000u) | (p0 << 14) | (p1 << 30);
+        }
+      } else {
+        // coset bits of groups 4 kg .. 4 kg + 3 spread to bytes 0..3
+        const uint32_t sp = __umul24((cs[u] >> (4 * kg)) & 15u, 0x00204081u) & 0x01010101u;
+        cc[0] = cc[1] = sp;
+      }
+      nq_f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        // 16-bit halves: table entries (code byte 0 | c << 8), (code byte 1 | c << 8)
+        const uint32_t sel = CMP ? ((b & 1) ? 0x06030602u : 0x04010400u)
+                                 : (0x04010400u + 0x01000100u * (uint32_t)b +
+                                    ((b & 1) ? 0x00020002u : 0u));
+        const uint32_t ix = __builtin_amdgcn_perm(cc[b >> 1], w[b >> 1], sel);
+        const uint32_t ad = (ix << 3) & 0xfff8fff8u;
+        const uint2 e0 = *reinterpret_cast<const uint2*>(tb + (ad & 0xffffu));
+        const uint2 e1 = *reinterpret_cast<const uint2*>(tb + (ad >> 16));
+        const nq_u4 bv = {e0.x, e0.y, e1.x, e1.y};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[b], __builtin_bit_cast(nq_bf16x8, bv),
+                                                      acc, 0, 0, 0);
+      }
+      const float f = h2f((uint16_t)sc[u]) * a.inv_sqrt_n;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        // rows of 16 lanes swapped pairwise (0 <-> 1, 2 <-> 3): hi + lo parts
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[r]),
+                                                         __float_as_uint(acc[r]), false, false);
+        v[u][r] = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * f;
+      }
+    }
+    // lanes of group blocks 0 and 1 hold the same sums: each stores one of
+    // two adjacent 16-key blocks, so a store covers 32 consecutive keys
+#pragma unroll
+    for (int u = 0; u < U; u += 2) {
+      const int t = kb + 16 * u + 16 * kg + col;
+      if (kg < 2 && t < nk) {
+#pragma unroll
+        for (int r = 0; r < HPP; ++r)
+          if (r < nh) (op + r * a.T)[(uint32_t)t] = kg ? v[u + 1][r] : v[u][r];
+      }
+    }
   }
 }
 
@@ -2095,6 +2253,32 @@ constexpr int lut_max_hpp() {
   return 160 * 1024 / per_head;
 }
 
+template <int HPP, typename T>
+hipError_t score_mfma_launch(const ScoreArgs& a, int n_pass, hipStream_t s) {
+  const size_t lds = sizeof(float) * HPP * 128;
+  auto kern = a.compact ? score_mfma_kernel<HPP, T, true> : score_mfma_kernel<HPP, T, false>;
+  // two workgroups per CU: 512 (slab, head, pass, token chunk) blocks or more
+  const int64_t pairs = a.S * a.H * n_pass;
+  int64_t n_chunks = (512 + pairs - 1) / pairs;
+  const int64_t min_chunk = 4096;
+  n_chunks = max((int64_t)1, min(n_chunks, (a.T + min_chunk - 1) / min_chunk));
+  const int64_t chunk = (a.T + n_chunks - 1) / n_chunks;
+  const dim3 grid((unsigned)n_chunks, (unsigned)(a.H * n_pass), (unsigned)a.S);
+  hipLaunchKernelGGL(kern, grid, dim3(kScoreMfmaBlock), lds, s, a, n_pass, chunk);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t score_mfma(const ScoreArgs& a, hipStream_t s) {
+  const int grp = a.Hq / a.H;
+  const int n_pass = (grp + 3) / 4;
+  const int hpp = (grp + n_pass - 1) / n_pass;
+  if (hpp == 1) return score_mfma_launch<1, T>(a, n_pass, s);
+  if (hpp == 2) return score_mfma_launch<2, T>(a, n_pass, s);
+  if (hpp == 3) return score_mfma_launch<3, T>(a, n_pass, s);
+  return score_mfma_launch<4, T>(a, n_pass, s);
+}
+
 template <int BITS, int N, typename T, int NS>
 hipError_t score_lut_hpp(const ScoreArgs& a, int hpp, int n_pass, hipStream_t s) {
   constexpr int kMax = lut_max_hpp<BITS, N>();
@@ -2134,6 +2318,9 @@ hipError_t score_lut_n(const ScoreArgs& a, int max_lds, hipStream_t s) {
 
 template <int N, int BITS, typename T>
 hipError_t score_n(const ScoreArgs& a, hipStream_t s) {
+  if constexpr (N == 128 && BITS == 2) {
+    if (a.n_scales == 1 && a.T < ((int64_t)1 << 26)) return score_mfma<T>(a, s);
+  }
   if constexpr (N >= 64) {
     const bool coset_bytes_align = (a.G == N) || (a.G % 64 == 0);
     int dev = 0, max_lds = 0;

@@ -139,6 +139,38 @@ def test_score_parity(cfg, grp):
     check_scores(s.cpu().numpy(), ref, qnorm[:, :, None], kn, "score")
 
 
+@pytest.mark.parametrize("d,parity,packing,dt,grp,T,t0", [
+    (128, R_, 0, F16, 4, 4111, 0),      # 4 heads a pass, ragged last block
+    (128, S_, 0, F32, 1, 17, 0),
+    (128, S_, CP, F16, 2, 15, 0),       # fewer keys than one 16-key block
+    (128, R_, 0, F16, 3, 2048, 0),
+    (128, S_, CP, F32, 8, 1000, 0),     # two passes of 4 heads
+    (96, S_, 0, F16, 4, 777, 0),        # d < n
+    (128, R_, 0, F16, 4, 600, 13),      # window at an odd token offset
+    (128, S_, 0, F16, 12, 1, 0),        # three passes, one key
+])
+def test_score_one_scale_shapes(d, parity, packing, dt, grp, T, t0):
+    """2-bit keys with one scale per vector (the matrix-core scorer): head
+    counts, query dtypes, ragged and tiny key counts, token windows."""
+    cfg = nq.Config(d, 2, 2, 0, parity, dt, 1e4, packing=packing)
+    S, H = 2, 2
+    log(f"[score1] d={d} parity={parity} packing={packing} dt={dt} grp={grp} T={T} t0={t0}")
+    k, _ = _inputs(cfg, S, H, T, 23, pos=np.arange(t0, t0 + T))
+    pk = nq.alloc_packed(cfg, False, S, H, t0 + T + 5, DEV)
+    nq.quantize_kv(cfg, k, None, pk=pk, token_offset=t0)
+    q = synth.queries(S, H * grp, cfg.head_dim, 23, DEV, cfg.torch_dtype)
+    s = nq.score_packed_keys(cfg, pk, q, S, H, T, token_offset=t0)
+    torch.cuda.synchronize()
+    codec = oracle_codec(cfg, False)
+    codes, cosets, scales = (pl[:, :, t0:t0 + T].cpu().numpy()
+                             for pl in (pk.codes, pk.cosets, pk.scales))
+    ref = oc.score(q.cpu().numpy(), codes, cosets, scales, codec)
+    kd = oc.dequantize(codes, cosets, scales, codec, apply_rope=False)
+    kn = np.repeat(np.linalg.norm(kd, axis=-1), grp, axis=1)
+    qnorm = np.linalg.norm(q.cpu().numpy().astype(np.float64), axis=-1)
+    check_scores(s.cpu().numpy(), ref, qnorm[:, :, None], kn, "score1")
+
+
 @pytest.mark.parametrize("bits", [2, 3])
 @pytest.mark.parametrize("parity", [S_, R_])
 def test_decoder_alone(bits, parity):
