@@ -32,7 +32,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=32768,
-                    help="tokens of one slab (all 8 heads, K and V) the oracle runs on")
+                    help="tokens per slab (all 8 heads, K and V) the oracle runs on")
+    ap.add_argument("--cpu-sample-slabs", type=int, default=2,
+                    help="slabs of the cache the oracle runs on")
     return ap.parse_args()
 
 
@@ -57,16 +59,16 @@ def profiled_traffic(profile):
     return int(m_tr.group(1))
 
 
-def cpu_baseline(w, tokens):
+def cpu_baseline(w, tokens, slabs):
     """The oracle, as it stands, on a bounded sample of the same workload."""
     import numpy as np  # noqa: F401
 
     from e8_lattice_vector_amd import synth
     from oracle import codec as oc
 
-    k = synth.kv("k", 1, w.H, tokens, w.d, w.theta, 0).numpy()
-    v = synth.kv("v", 1, w.H, tokens, w.d, 0.0, 0).numpy()
-    q = synth.queries(1, 32, w.d, 0).numpy()
+    k = synth.kv("k", slabs, w.H, tokens, w.d, w.theta, 0).numpy()
+    v = synth.kv("v", slabs, w.H, tokens, w.d, 0.0, 0).numpy()
+    q = synth.queries(slabs, 32, w.d, 0).numpy()
     ck = oc.Codec(w.d, w.bits_k, w.G, w.strict, w.theta)
     cv = oc.Codec(w.d, w.bits_v, w.G, w.strict, 0.0)
     from threadpoolctl import threadpool_limits
@@ -81,13 +83,13 @@ def cpu_baseline(w, tokens):
         oc.dequantize(rv["codes"], rv["cosets"], rv["scales"], cv)
         oc.score(q, rk["codes"], rk["cosets"], rk["scales"], ck)
         dt = time.perf_counter() - t0
-    cache_tokens = tokens / w.S  # one of S slabs
+    cache_tokens = tokens * slabs / w.S  # slabs of S
     return {
         "value": cache_tokens / dt,
         "unit": "tokens/s",
         "cores": 1,
         "kind": "oracle",
-        "sample": f"1 of {w.S} slabs x {w.H} heads x {tokens} tokens, K+V quantize, "
+        "sample": f"{slabs} of {w.S} slabs x {w.H} heads x {tokens} tokens, K+V quantize, "
                   f"dequantize and 32-query scoring ({dt:.1f} s single-threaded numpy)",
     }
 
@@ -249,7 +251,7 @@ def main():
         },
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens, args.cpu_sample_slabs)
     print(json.dumps(out), flush=True)
 
 
