@@ -1872,21 +1872,24 @@ __global__ __launch_bounds__(1024) void attend_mfma4_kernel(AttendArgs a, int n_
 //   score = (s / sqrt n) sum_j q~_j p_j ,
 // a dense contraction over the coordinates j: for 16 keys at a time,
 // D[row][key] = sum_j A[row][j] B[j][key], B from the value table (exact
-// bf16) and A the rotated queries, split into bf16 hi (rows 0..3) and lo
-// (rows 4..7) parts (error below 2^-16 |q~_j| each).  Four 16x16x32 products
+// bf16) and A the rotated queries, split into bf16 hi and lo parts (error
+// below 2^-16 |q~_j| each).  Four 16x16x32 products
 // cover the 128 coordinates.  Lane (key l % 16, group block g = l / 16)
 // takes the 8-groups 4 g .. 4 g + 3 of its key (8 contiguous code bytes);
 // product b uses 8-group 4 g + b, whose two table entries are that lane's B
-// operand as they come.  D rows 0..3 + rows 4..7 are summed across lane
-// rows (v_permlane16_swap); each wave scores 32 consecutive keys per step, and two
-// workgroups share a CU.
+// operand as they come.  Up to 4 query heads a pass the rows are (head 0..3,
+// part) and rows 0..3 + 4..7 are summed across lane rows (v_permlane16_swap);
+// 5..8 heads use all 16 rows (head 0..7, part), summed across the wave's
+// halves (v_permlane32_swap).  Each wave scores 32 consecutive keys per
+// step, and two workgroups share a CU.
 // ---------------------------------------------------------------------------
 constexpr int kScoreMfmaBlock = 1024;
 
 template <int HPP, typename QT, bool CMP>
 __global__ __launch_bounds__(kScoreMfmaBlock, 8) void score_mfma_kernel(ScoreArgs a, int n_pass,
                                                                      int64_t chunk) {
-  static_assert(HPP <= 4, "rows are (head, part)");
+  static_assert(HPP <= 8, "rows are (head, part)");
+  constexpr bool W8 = HPP > 4;             // rows (head 0..7, part) instead of (head 0..3, part)
   constexpr int N = 128;
   constexpr int U = 2;                     // 16-key blocks per wave per step
   extern __shared__ float qt[];            // [HPP][N] rotated queries
@@ -1920,8 +1923,9 @@ __global__ __launch_bounds__(kScoreMfmaBlock, 8) void score_mfma_kernel(ScoreArg
   const int nw = blockDim.x >> 6;
   const int col = lane & 15;               // key of the block; A row
   const int kg = lane >> 4;                // 8-groups 4 kg .. 4 kg + 3
-  const int hh = col & 3;
-  const bool arow = col < 8 && hh < nh;
+  const int hh = W8 ? (col & 7) : (col & 3);
+  const bool part = W8 ? (col >= 8) : ((col & 4) != 0);   // the lo-part row
+  const bool arow = (W8 || col < 8) && hh < nh;
   nq_bf16x8 A[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -1933,7 +1937,7 @@ __global__ __launch_bounds__(kScoreMfmaBlock, 8) void score_mfma_kernel(ScoreArg
       for (int k = 0; k < 2; ++k) {
         const float v = arow ? qt[hh * N + 8 * (4 * kg + b) + 2 * e + k] : 0.f;
         const float hi = (float)(__bf16)v;
-        const float x = (col & 4) ? v - hi : v;
+        const float x = part ? v - hi : v;
         const uint32_t bits = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
         pr |= bits << (16 * k);
       }
@@ -1997,21 +2001,39 @@ __global__ __launch_bounds__(kScoreMfmaBlock, 8) void score_mfma_kernel(ScoreArg
       const float f = h2f((uint16_t)sc[u]) * a.inv_sqrt_n;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        // rows of 16 lanes swapped pairwise (0 <-> 1, 2 <-> 3): hi + lo parts
-        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[r]),
-                                                         __float_as_uint(acc[r]), false, false);
-        v[u][r] = (__uint_as_float(sw[0]) + __uint_as_float(sw[1])) * f;
+        // hi + lo parts: rows 0..3 + 4..7 sit 16 lanes apart (lane rows
+        // swapped pairwise), rows 0..7 + 8..15 32 lanes apart (halves swapped)
+        uint32_t s0, s1;
+        if (W8) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[r]),
+                                                           __float_as_uint(acc[r]), false, false);
+          s0 = sw[0];
+          s1 = sw[1];
+        } else {
+          const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[r]),
+                                                           __float_as_uint(acc[r]), false, false);
+          s0 = sw[0];
+          s1 = sw[1];
+        }
+        v[u][r] = (__uint_as_float(s0) + __uint_as_float(s1)) * f;
       }
     }
-    // lanes of group blocks 0 and 1 hold the same sums: each stores one of
-    // two adjacent 16-key blocks, so a store covers 32 consecutive keys
+    // Up to 4 heads: lane rows 0 and 1 hold the same sums, and each stores
+    // one of two adjacent 16-key blocks (a store covers 32 consecutive keys).
+    // 5..8 heads: lane rows 0 and 2 hold heads 0..3, rows 1 and 3 heads 4..7;
+    // rows 0, 1 store the first block, rows 2, 3 the second.
 #pragma unroll
     for (int u = 0; u < U; u += 2) {
-      const int t = kb + 16 * u + 16 * kg + col;
-      if (kg < 2 && t < nk) {
+      const int blk = W8 ? (kg >> 1) : kg;
+      const int h0 = W8 ? 4 * (kg & 1) : 0;
+      const int t = kb + 16 * (u + blk) + col;
+      const uint32_t m1 = 0u - (uint32_t)(blk & 1);      // bit select, no indexing
+      if ((W8 || kg < 2) && t < nk) {
 #pragma unroll
-        for (int r = 0; r < HPP; ++r)
-          if (r < nh) (op + r * a.T)[(uint32_t)t] = kg ? v[u + 1][r] : v[u][r];
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t x = (__float_as_uint(v[u + 1][r]) & m1) | (__float_as_uint(v[u][r]) & ~m1);
+          if (h0 + r < nh) (op + (h0 + r) * a.T)[(uint32_t)t] = __uint_as_float(x);
+        }
       }
     }
   }
@@ -2271,12 +2293,18 @@ hipError_t score_mfma_launch(const ScoreArgs& a, int n_pass, hipStream_t s) {
 template <typename T>
 hipError_t score_mfma(const ScoreArgs& a, hipStream_t s) {
   const int grp = a.Hq / a.H;
-  const int n_pass = (grp + 3) / 4;
+  const int n_pass = (grp + 7) / 8;
   const int hpp = (grp + n_pass - 1) / n_pass;
-  if (hpp == 1) return score_mfma_launch<1, T>(a, n_pass, s);
-  if (hpp == 2) return score_mfma_launch<2, T>(a, n_pass, s);
-  if (hpp == 3) return score_mfma_launch<3, T>(a, n_pass, s);
-  return score_mfma_launch<4, T>(a, n_pass, s);
+  switch (hpp) {
+    case 1: return score_mfma_launch<1, T>(a, n_pass, s);
+    case 2: return score_mfma_launch<2, T>(a, n_pass, s);
+    case 3: return score_mfma_launch<3, T>(a, n_pass, s);
+    case 4: return score_mfma_launch<4, T>(a, n_pass, s);
+    case 5: return score_mfma_launch<5, T>(a, n_pass, s);
+    case 6: return score_mfma_launch<6, T>(a, n_pass, s);
+    case 7: return score_mfma_launch<7, T>(a, n_pass, s);
+    default: return score_mfma_launch<8, T>(a, n_pass, s);
+  }
 }
 
 template <int BITS, int N, typename T, int NS>

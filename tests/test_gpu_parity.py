@@ -144,10 +144,11 @@ def test_score_parity(cfg, grp):
     (128, S_, 0, F32, 1, 17, 0),
     (128, S_, CP, F16, 2, 15, 0),       # fewer keys than one 16-key block
     (128, R_, 0, F16, 3, 2048, 0),
-    (128, S_, CP, F32, 8, 1000, 0),     # two passes of 4 heads
+    (128, S_, CP, F32, 8, 1000, 0),     # 8 heads in one pass (all 16 rows)
+    (128, R_, 0, F16, 7, 333, 3),       # 7 heads, ragged, window
     (96, S_, 0, F16, 4, 777, 0),        # d < n
     (128, R_, 0, F16, 4, 600, 13),      # window at an odd token offset
-    (128, S_, 0, F16, 12, 1, 0),        # three passes, one key
+    (128, S_, 0, F16, 12, 1, 0),        # two passes of 6 heads, one key
 ])
 def test_score_one_scale_shapes(d, parity, packing, dt, grp, T, t0):
     """2-bit keys with one scale per vector (the matrix-core scorer): head
