@@ -94,6 +94,54 @@ def cpu_baseline(w, tokens, slabs):
     }
 
 
+def qwen_decode_scores(steps, warmup, dev, stream):
+    """Packed-key scoring at the decode shape of the scoring row: 768 slabs
+    (16 sequences x 48 layers) x 8 KV heads x 16384 keys, 40 query heads (GQA
+    5). Keys come from the Llama generator and are quantized in slab batches,
+    so only the packed keys (3.6 GB) stay resident; scores are 2.0 GB."""
+    import torch
+
+    from e8_lattice_vector_amd import nq, synth, workloads
+
+    w = workloads.QWEN_DECODE
+    cfg = nq.Config(w.d, w.bits_k, w.bits_v, w.G,
+                    nq.PARITY_STRICT if w.strict else nq.PARITY_RELAXED, nq.DTYPE_F16, w.theta)
+    pk = nq.alloc_packed(cfg, False, w.S, w.H, w.T, dev)
+    ws = nq.alloc_workspace(cfg, w.T, dev)
+    batch = 32
+    for s0 in range(0, w.S, batch):
+        k = synth.kv("k", batch, w.H, w.T, w.d, w.theta, 0, dev, torch.float16, slab0=s0)
+        sub = nq.Packed(pk.codes[s0:s0 + batch], pk.cosets[s0:s0 + batch],
+                        pk.scales[s0:s0 + batch])
+        nq.quantize_kv(cfg, k, None, pk=sub, workspace=ws)
+        del k
+    q = synth.queries(w.S, w.Hq, w.d, 0, dev)
+    sc = torch.empty((w.S, w.Hq, w.T), dtype=torch.float32, device=dev)
+    for _ in range(warmup):
+        nq.score_packed_keys(cfg, pk, q, w.S, w.H, w.T, scores=sc)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(steps):
+        nq.score_packed_keys(cfg, pk, q, w.S, w.H, w.T, scores=sc)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / steps
+    keys = w.S * w.H * w.T
+    nbytes = pk.nbytes() + q.numel() * 2 + sc.numel() * 4
+    del pk, ws, q, sc
+    return {
+        "workload": w.name,
+        "ms": ms,
+        "keys_per_s": keys / (ms * 1e-3),
+        "GBps": nbytes / (ms * 1e-3) / 1e9,
+        "pct_hbm_peak": 100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "bytes": nbytes,
+        "what": "scores of 40 fp16 decode queries per slab against 768 x 8 x 16384 packed keys "
+                "(36 B/key read, 20 B/key written)",
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -250,6 +298,7 @@ def main():
             "avg_launch_ms": tq / 2,
         },
     }
+    out["score_decode_shape"] = qwen_decode_scores(args.steps, args.warmup, dev, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens, args.cpu_sample_slabs)
     print(json.dumps(out), flush=True)
