@@ -31,6 +31,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode-shape", action="store_true",
+                    help="skip the scoring run at the Qwen2.5-14B decode shape")
     ap.add_argument("--cpu-sample-tokens", type=int, default=32768,
                     help="tokens per slab (all 8 heads, K and V) the oracle runs on")
     ap.add_argument("--cpu-sample-slabs", type=int, default=2,
@@ -298,7 +300,8 @@ def main():
             "avg_launch_ms": tq / 2,
         },
     }
-    out["score_decode_shape"] = qwen_decode_scores(args.steps, args.warmup, dev, stream)
+    if not args.no_decode_shape:
+        out["score_decode_shape"] = qwen_decode_scores(args.steps, args.warmup, dev, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens, args.cpu_sample_slabs)
     print(json.dumps(out), flush=True)
