@@ -197,6 +197,10 @@ int nq_dequantize_kv(const nq_config* cfg, const nq_packed* pk,
  *  q       device [S][n_q_heads][d] queries (in_dtype)
  *  scores  device fp32 [S][n_q_heads][T]
  * n_q_heads must be a positive multiple of n_kv_heads.  workspace may be NULL.
+ * Arithmetic: fp32 sums.  For 2-bit keys with one scale per vector at
+ * n = 128 the per-coordinate products run on bf16 matrix cores, with the
+ * code values exact and each rotated query coordinate split into two bf16
+ * parts (relative error below 2^-16 per term).
  * Errors as nq_quantize_kv. */
 int nq_score_packed_keys(const nq_config* cfg, const nq_packed* pk,
                          int64_t n_slabs, int32_t n_kv_heads,
@@ -214,7 +218,11 @@ int nq_score_packed_keys(const nq_config* cfg, const nq_packed* pk,
  *  weights  device fp32 [S][n_q_heads][T] (e.g. softmax of the scores)
  *  out      device fp32 [S][n_q_heads][d]
  * n_q_heads must be a positive multiple of n_kv_heads.  The result is
- * deterministic (fixed reduction order).  Errors as nq_quantize_kv. */
+ * deterministic (fixed reduction order).  Arithmetic: fp32 sums; for 2-bit
+ * values with one scale per vector at n = 128 the per-token products run on
+ * bf16 matrix cores, with the code values exact and each weight * scale
+ * split into two bf16 parts (relative error below 2^-14 per term).
+ * Errors as nq_quantize_kv. */
 int nq_attend_packed_values(const nq_config* cfg, const nq_packed* pv,
                             int64_t n_slabs, int32_t n_kv_heads,
                             int32_t n_q_heads, int64_t n_tokens,
