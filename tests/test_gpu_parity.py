@@ -370,6 +370,42 @@ def test_attend_one_scale_shapes(d, parity, packing, grp, T, signed, t0, extra):
                   oracle_codec(cfg, True), "attend1")
 
 
+@pytest.mark.parametrize("parity", [S_, R_])
+def test_matrix_core_split_precision(parity):
+    """The matrix-core scorer and attention split the fp32 operand (rotated
+    query; weight x scale) into two bf16 parts, so their error sits far
+    below the acceptance bound: within 1e-5 |q||D0 k| per score and 2e-5
+    sum_t |w_t||V^_t| per attention output (measured ~1e-6 and ~5e-6; a
+    single bf16 part would exceed both)."""
+    cfg = nq.Config(128, 2, 2, 0, parity, F16, 1e4)
+    S, H, T, grp = 2, 2, 4096, 4
+    log(f"[split] parity={parity}")
+    k, v = _inputs(cfg, S, H, T, 31)
+    pk, pv = nq.quantize_kv(cfg, k, v)
+    q = synth.queries(S, H * grp, 128, 31, DEV, cfg.torch_dtype)
+    sc = nq.score_packed_keys(cfg, pk, q, S, H, T)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(17)
+    w = torch.softmax(torch.randn((S, H * grp, T), generator=g, device=DEV) * 3, dim=-1)
+    out = nq.attend_packed_values(cfg, pv, w.contiguous(), S, H, T)
+    torch.cuda.synchronize()
+    ck, cv = oracle_codec(cfg, False), oracle_codec(cfg, True)
+    codes, cosets, scales = to_np(pk)
+    ref = oc.score(q.cpu().numpy(), codes, cosets, scales, ck)
+    kd = oc.dequantize(codes, cosets, scales, ck, apply_rope=False)
+    kn = np.repeat(np.linalg.norm(kd, axis=-1), grp, axis=1)
+    qn = np.linalg.norm(q.cpu().numpy().astype(np.float64), axis=-1)[:, :, None]
+    e_score = np.max(np.abs(sc.cpu().numpy() - ref) / (qn * kn))
+    vplanes = to_np(pv)
+    wn = w.cpu().numpy().astype(np.float64)
+    ref_a = oc.attend(wn, *vplanes, cv)
+    vn = np.repeat(np.linalg.norm(oc.dequantize(*vplanes, cv), axis=-1), grp, axis=1)
+    e_att = np.max(np.linalg.norm(out.cpu().numpy() - ref_a, axis=-1) / (np.abs(wn) * vn).sum(-1))
+    log(f"[split] score {e_score:.2e}, attend {e_att:.2e}")
+    assert e_score <= 1e-5, e_score
+    assert e_att <= 2e-5, e_att
+
+
 def test_attend_llama_full_sampled():
     """Llama-3.1-8B 32K values, 32 query heads (GQA 4), softmax weights;
     every output of 4 sampled (slab, KV head) pairs checked against the
