@@ -1713,13 +1713,6 @@ __global__ __launch_bounds__(1024) void attend_mfma_kernel(AttendArgs a, int n_p
   }
 }
 
-// Variant for up to 4 query heads a pass: the 16 A rows are (head, hi / lo
-// part, sub) and the two bf16 of a K-slot pair are two coordinates of one
-// token (sub 0 and 1), so a lookup in a 4 KB LDS table -- entry (c, code byte)
-// holds the bf16 of idx - 2 + c/2 for the byte's 4 coordinates -- yields B
-// operand words directly.  Column g of block b holds coordinates 8 g + 2 b
-// (sub 0) and 8 g + 2 b + 1 (sub 1); the A row of sub 0 carries the weight in
-// the low bf16 of each pair and 0 in the high one, sub 1 the reverse.
 // The 2-bit code values of one byte as bf16: entry c * 256 + byte holds
 // idx - 2 + c/2 for the byte's 4 coordinates (exact in bf16), low
 // coordinate first.  Written by the whole workgroup; a barrier must follow.
@@ -1733,6 +1726,13 @@ __device__ __forceinline__ void value_table(uint2* tbl) {
   }
 }
 
+// Variant for up to 4 query heads a pass: the 16 A rows are (head, hi / lo
+// part, sub) and the two bf16 of a K-slot pair are two coordinates of one
+// token (sub 0 and 1), so a lookup in a 4 KB LDS table -- entry (c, code byte)
+// holds the bf16 of idx - 2 + c/2 for the byte's 4 coordinates -- yields B
+// operand words directly.  Column g of block b holds coordinates 8 g + 2 b
+// (sub 0) and 8 g + 2 b + 1 (sub 1); the A row of sub 0 carries the weight in
+// the low bf16 of each pair and 0 in the high one, sub 1 the reverse.
 template <bool CMP>
 __device__ __forceinline__ void att_mma4(nq_f4 (&acc)[4], const AttChunk& k,
                                          const uint2* __restrict__ tbl, int col,
