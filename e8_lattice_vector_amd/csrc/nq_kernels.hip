@@ -21,6 +21,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <algorithm>
+
 #include <type_traits>
 
 #include "nq_internal.h"
@@ -2039,6 +2041,175 @@ __global__ __launch_bounds__(kScoreMfmaBlock, 8) void score_mfma_kernel(ScoreArg
   }
 }
 
+// Pipelined form of the table variant: each wave keeps kAttStages 32-token
+// chunks in flight in LDS stages, filled by direct global -> LDS loads (no
+// registers held for data in flight).  A stage holds the chunk's codes
+// (1024 B, token t at 32 sigma(t), sigma spreading the tokens a lane group
+// reads over distinct banks), the weights of up to 4 heads (128 B each), the
+// 32 scales and the 32 coset words.  Two loads per chunk: the codes (64
+// lanes x 16 B), then weights / scales / cosets (lanes 0..39).  The wait
+// before a chunk's use counts the loads issued after it; no other vector
+// memory operation is issued inside the loop.
+// ---------------------------------------------------------------------------
+constexpr int kAttStages = 4;
+constexpr int kAttStage = 1664;           // bytes per stage
+
+// token -> 32-byte slot of the stage's code area
+__device__ __forceinline__ int att_sigma(int t) { return (t & ~7) | ((t + 2 * (t >> 3)) & 7); }
+__device__ __forceinline__ int att_sigma_inv(int p) { return (p & ~7) | ((p - 2 * (p >> 3)) & 7); }
+
+__device__ __forceinline__ void att_dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds_base), "v"(src) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void att_wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+template <int HPP, bool CMP>
+__global__ __launch_bounds__(1024) void attend_dma_kernel(AttendArgs a, int n_pass) {
+  static_assert(HPP <= 4, "rows are (head, part, sub)");
+  constexpr int N = 128;
+  constexpr int R = kAttStages;
+  extern __shared__ __align__(16) char dyn[];   // stages; reduction buffer afterwards
+  __shared__ uint2 tbl[512];
+  value_table(tbl);
+  const int64_t s = blockIdx.z;
+  const int h = blockIdx.y / n_pass;
+  const int pass = blockIdx.y % n_pass;
+  const int grp = a.Hq / a.H;
+  const int hq0 = h * grp + pass * HPP;
+  const int nh = min(HPP, h * grp + grp - hq0);
+  const int lane = threadIdx.x & 63;
+  const int wv = threadIdx.x >> 6;
+  const int nw = blockDim.x >> 6;
+  const int col = lane & 15;
+  const int kg = lane >> 4;
+  const int hh = col & 3;
+  const bool arow = hh < nh;
+  const uint32_t pmask = (col & 4) ? 0xffff0000u : 0u;
+  const uint32_t asel = (col & 8) ? 0x03020c0cu : 0x0c0c0302u;
+  const int T = (int)a.T;
+  const int64_t base = (s * a.H + h) * a.pT;
+  const float* wrow = a.w + (s * a.Hq + hq0) * a.T;
+  const uint8_t* cp = a.codes + base * (N / 4);
+  const uint16_t* csp = reinterpret_cast<const uint16_t*>(a.cosets) + base;
+  const uint16_t* scp = a.scales + base;
+  // this lane's sources for the two loads of a chunk at token c0:
+  //  codes: cp + 32 c0 + goff;   rest: src1 + c0 * eb1 (active: act1)
+  const int goff = 32 * att_sigma_inv(lane >> 1) + 16 * (lane & 1);
+  const char* src1;
+  int eb1;
+  bool act1;
+  if (lane < 32) {
+    act1 = (lane >> 3) < nh;
+    src1 = reinterpret_cast<const char*>(wrow + (int64_t)min(lane >> 3, nh - 1) * a.T + 4 * (lane & 7));
+    eb1 = 4;
+  } else if (lane < 36) {
+    act1 = true;
+    src1 = reinterpret_cast<const char*>(scp + 8 * (lane - 32));
+    eb1 = 2;
+  } else {
+    act1 = !CMP && lane < 40;
+    src1 = reinterpret_cast<const char*>(csp + 8 * (CMP ? 0 : lane - 36));
+    eb1 = 2;
+  }
+  const uint32_t dyn0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)dyn;
+  const uint32_t wbase = dyn0 + (uint32_t)(wv * R * kAttStage);
+  const char* wst = dyn + wv * R * kAttStage;        // this wave's stages
+  nq_f4 acc[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) acc[b] = nq_f4{0.f, 0.f, 0.f, 0.f};
+  __syncthreads();
+  const int nfull = T >> 5;
+  const int nk = nfull > wv ? (nfull - 1 - wv) / nw + 1 : 0;   // this wave's full chunks
+  auto issue = [&](int k) {
+    const int c0 = (wv + k * nw) * 32;
+    const uint32_t sb = wbase + (uint32_t)((k % R) * kAttStage);
+    att_dma16(cp + (int64_t)c0 * 32 + goff, __builtin_amdgcn_readfirstlane(sb));
+    if (act1) att_dma16(src1 + (int64_t)c0 * eb1, __builtin_amdgcn_readfirstlane(sb + 1024));
+  };
+#pragma unroll
+  for (int k = 0; k < R - 1; ++k)
+    if (k < nk) issue(k);
+  for (int k = 0; k < nk; ++k) {
+    if (k + R - 1 < nk) issue(k + R - 1);
+    // loads issued after chunk k's: 2 per later chunk
+    const int later = min(R - 1, nk - 1 - k);
+    if (later >= 3) att_wait_vm<6>();
+    else if (later == 2) att_wait_vm<4>();
+    else if (later == 1) att_wait_vm<2>();
+    else att_wait_vm<0>();
+    const char* st = wst + (k % R) * kAttStage;
+    AttChunk ch;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t0 = 8 * kg + 2 * j;
+      const uint32_t g0 = *reinterpret_cast<const uint16_t*>(st + 32 * att_sigma(t0) + 2 * col);
+      const uint32_t g1 = *reinterpret_cast<const uint16_t*>(st + 32 * att_sigma(t0 + 1) + 2 * col);
+      ch.cw[j] = g0 | (g1 << 16);
+    }
+    const uint4 sv = *reinterpret_cast<const uint4*>(st + 1536 + 16 * kg);
+    ch.sw[0] = sv.x; ch.sw[1] = sv.y; ch.sw[2] = sv.z; ch.sw[3] = sv.w;
+    if (!CMP) {
+      const uint4 cv = *reinterpret_cast<const uint4*>(st + 1600 + 16 * kg);
+      ch.cs[0] = cv.x; ch.cs[1] = cv.y; ch.cs[2] = cv.z; ch.cs[3] = cv.w;
+    }
+    if (arow) {
+      const float4 w0 = *reinterpret_cast<const float4*>(st + 1024 + 128 * hh + 32 * kg);
+      const float4 w1 = *reinterpret_cast<const float4*>(st + 1024 + 128 * hh + 32 * kg + 16);
+      ch.wt[0] = w0.x; ch.wt[1] = w0.y; ch.wt[2] = w0.z; ch.wt[3] = w0.w;
+      ch.wt[4] = w1.x; ch.wt[5] = w1.y; ch.wt[6] = w1.z; ch.wt[7] = w1.w;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ch.wt[i] = 0.f;
+    }
+    att_mma4<CMP>(acc, ch, tbl, col, pmask, asel);
+  }
+  // the partial chunk (T not a multiple of 32), through registers
+  if ((T & 31) != 0 && wv == nfull % nw) {
+    AttChunk ch;
+    const float* wr = wrow + (int64_t)(arow ? hh : 0) * a.T;
+    att_load<false, CMP>(ch, cp + 2 * col, csp, scp, wr, nfull * 32 + 8 * kg, T, arow);
+    att_mma4<CMP>(acc, ch, tbl, col, pmask, asel);
+  }
+  att_wait_vm<0>();
+  __syncthreads();                              // stages become the reduction buffer
+  float* red = reinterpret_cast<float*>(dyn);
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = acc[b][r] + __shfl_xor(acc[b][r], 16);
+      if ((kg & 1) == 0 && r < HPP)
+        red[(wv * HPP + r) * N + 8 * col + 2 * b + (kg >> 1)] = v;
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < HPP * N; i += blockDim.x) {
+    float sum = 0.f;
+    for (int w = 0; w < nw; ++w) sum += red[w * HPP * N + i];
+    red[i] = sum;
+  }
+  __syncthreads();
+  for (int hs = 1; hs < N; hs <<= 1) {
+    for (int i = threadIdx.x; i < HPP * (N / 2); i += blockDim.x) {
+      const int g = i / (N / 2), r = i % (N / 2);
+      const int j = (r / hs) * 2 * hs + (r % hs);
+      const float x0 = red[g * N + j], x1 = red[g * N + j + hs];
+      red[g * N + j] = x0 + x1;
+      red[g * N + j + hs] = x0 - x1;
+    }
+    __syncthreads();
+  }
+  for (int i = threadIdx.x; i < nh * a.d; i += blockDim.x) {
+    const int g = i / a.d, j = i % a.d;
+    a.out[(s * a.Hq + hq0 + g) * (int64_t)a.d + j] = red[g * N + j] * a.inv_sqrt_n;
+  }
+}
+
 // Nearest point of the whole lattice, no cube limit (the textbook
 // Conway-Sloane decoder on D8 and on D8 + 1/2 (strict) or Z^8 + 1/2
 // (relaxed)), with the same tie rules as the cube decoder: rounding ties away
@@ -2443,11 +2614,40 @@ hipError_t attend_mfma4_launch(const AttendArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int HPP>
+hipError_t attend_dma_launch(const AttendArgs& a, hipStream_t s) {
+  constexpr int kThreads = 1024;
+  const int grp = a.Hq / a.H;
+  const int n_pass = (grp + HPP - 1) / HPP;
+  const size_t lds = std::max((size_t)(kThreads / 64) * kAttStages * kAttStage,
+                              sizeof(float) * (size_t)(kThreads / 64) * HPP * 128) + 512;
+  auto kern = a.compact ? attend_dma_kernel<HPP, true> : attend_dma_kernel<HPP, false>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const dim3 grid(1u, (unsigned)(a.H * n_pass), (unsigned)a.S);
+  hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, s, a, n_pass);
+  return hipGetLastError();
+}
+// Direct-to-LDS loads move 16 aligned bytes per lane: the weight rows (T a
+// multiple of 4) and every plane's scale and coset rows (token stride a
+// multiple of 8, 16-byte aligned planes) must allow it.
+bool attend_dma_ok(const AttendArgs& a) {
+  const auto al = [](const void* p) { return ((uintptr_t)p & 15) == 0; };
+  return (a.T & 3) == 0 && (a.pT & 7) == 0 && al(a.w) && al(a.codes) && al(a.scales) &&
+         (a.compact || al(a.cosets));
+}
+
 template <int BITS, int N>
 hipError_t attend_n(const AttendArgs& a, hipStream_t s) {
   const int grp = a.Hq / a.H;
   if constexpr (BITS == 2 && N == 128) {
     if (a.n_scales == 1 && a.T < ((int64_t)1 << 26)) {
+      if (grp <= 4 && attend_dma_ok(a)) {
+        if (grp <= 1) return attend_dma_launch<1>(a, s);
+        if (grp <= 2) return attend_dma_launch<2>(a, s);
+        return attend_dma_launch<4>(a, s);
+      }
       if (grp <= 1) return attend_mfma4_launch<1>(a, s);
       if (grp <= 2) return attend_mfma4_launch<2>(a, s);
       if (grp <= 4) return attend_mfma4_launch<4>(a, s);

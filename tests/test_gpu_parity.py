@@ -342,7 +342,7 @@ def test_attend_parity(cfg, grp, signed):
     (128, R_, 0, 4, 1200, False, 5, 3),     # window at an unaligned token offset
     (128, S_, CP, 4, 2048, True, 64, 3),    # window at an aligned offset
     (128, R_, 0, 4, 1, False, 0, 3),
-    # token stride a multiple of 8 and T of 4: 16-byte loads of scales, cosets, weights
+    # token stride a multiple of 8 and T of 4: pipelined direct-to-LDS loads
     (128, R_, 0, 4, 2084, False, 0, 4),     # pipelined chunks and a tail chunk
     (128, S_, CP, 2, 64, True, 8, 0),       # aligned window; most waves idle
     (128, R_, 0, 1, 20, False, 0, 4),       # tail chunk only
@@ -351,7 +351,7 @@ def test_attend_parity(cfg, grp, signed):
 def test_attend_one_scale_shapes(d, parity, packing, grp, T, signed, t0, extra):
     """2-bit values with one scale per vector (the matrix-core contraction):
     head counts, ragged and tiny token counts, token windows, plane
-    alignments with and without 16-byte metadata loads."""
+    alignments with and without the pipelined direct-to-LDS loads."""
     cfg = nq.Config(d, 2, 2, 0, parity, F16, 0.0, packing=packing)
     S, H = 2, 2
     log(f"[attend1] d={d} parity={parity} packing={packing} grp={grp} T={T} t0={t0} "
