@@ -22,6 +22,10 @@ HIPCC_FLAGS = [
     "-ffp-contract=off",
     # keep the compiler from emitting packed fp32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core accumulators in ordinary VGPRs: the quantize kernel reads
+    # every product back into vector arithmetic, so AGPR copies would cost
+    # one extra instruction per value
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-command-line-argument",
     # per-kernel register / scratch report, checked below

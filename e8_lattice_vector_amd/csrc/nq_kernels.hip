@@ -32,6 +32,9 @@ namespace {
 
 constexpr int kBlock = 256;
 
+typedef float nq_f2 __attribute__((ext_vector_type(2)));
+typedef float nq_f4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ float h2f(uint16_t h) {
   return __half2float(__ushort_as_half(h));
 }
@@ -554,17 +557,14 @@ __device__ __forceinline__ void e8_decode2(const float g[8], uint32_t& code,
   const int c = lhs < rhs ? 1 : 0;
   cosets = __ballot(lhs < rhs);
   coset = c;
+  // both code words, then a select (no divergent branch)
   const uint32_t Bsp = spread8(~Bn);
-  uint32_t w;
-  if (c == 0) {
-    const uint32_t b = Bsp ^ (odd0 ? f0 : 0u);
-    w = b | (~((b << 1) & X) & 0xaaaau);
-  } else {
-    uint32_t x = X;
-    if (STRICT && odd1) x ^= (f1 & Bsp) | ((f1 & ~Bsp) << 1);
-    w = ((x ^ (x >> 1)) & 0x5555u) | (~x & 0xaaaau);
-  }
-  code = w;
+  const uint32_t b = Bsp ^ (odd0 ? f0 : 0u);
+  const uint32_t w0 = b | (~((b << 1) & X) & 0xaaaau);
+  uint32_t x = X;
+  if (STRICT) x ^= odd1 ? (f1 & Bsp) | ((f1 & ~Bsp) << 1) : 0u;
+  const uint32_t w1 = ((x ^ (x >> 1)) & 0x5555u) | (~x & 0xaaaau);
+  code = c ? w1 : w0;
 }
 
 // ROPE: 0 none, 1 partner through DPP (d == n >= 16), 2 partner through
@@ -737,6 +737,161 @@ __global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
         char* sb = gb + (int64_t)(it - slot) * plane_g * 2;
         *reinterpret_cast<uint16_t*>(sb + off_gb) =
             f64_to_f16_rn((double)keep * a.sigma_k);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Quantize with the rotation on the matrix cores: vectors without RoPE
+// (values, or keys when no RoPE is removed), d = n = 128, 2-bit codes, one
+// scale per vector, fp16 input.
+//
+// The Walsh-Hadamard product u = H x of 16 vectors is a 128 x 128 by
+// 128 x 16 matrix product: 8 output tiles x 4 K chunks of
+// v_mfma_f32_16x16x32_f16.  The inputs are fp16 numbers and the entries of H
+// are +-1, so every product is exact and only the fp32 sums round.  Both
+// sides are relabelled.  Lane l (v = l & 15, p = l >> 4) feeds K slot 8p + j
+// of chunk k with input coordinate j + 8k + 32p of vector v (its four chunks
+// are one 64-byte run), and row m of output tile tau is output coordinate
+//     (m & 3) + 4 (tau & 1) + 8 (tau >> 1) + 32 (m >> 2).
+// Then (-1)^popcount(out & in) splits into a per-lane pattern chosen by
+// tau & 1 times the tile-uniform sign (-1)^((tau >> 1 & 1) (k & 1) +
+// (tau >> 2) (k >> 1)), so four fragments of H (two patterns and their
+// negatives) serve all 32 products.  Lane l receives rows 4p .. 4p+3 of
+// column v of every tile: the 8-groups 4p + h (h = tau >> 1) of vector v,
+// element e of group h at tile 2h + (e >> 2), row e & 3, so each lane decodes
+// four consecutive groups and stores their 8 code bytes at once.
+//
+// Waves walk kQmChunk (slab, head) planes of one 16-token tile, and
+// neighbouring waves take neighbouring tiles of the same planes, so the
+// loads in flight at any time cover a few contiguous stretches of each plane.
+// ---------------------------------------------------------------------------
+typedef _Float16 nq_f16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kQmChunk = 8;  // (slab, head) planes per wave
+
+template <bool STRICT>
+__global__ __launch_bounds__(kBlock) void quantize_mfma_kernel(TensorArgs a, int sh_chunk) {
+  const int lane = threadIdx.x & 63;
+  const int v = lane & 15;
+  const int p = lane >> 4;
+  const int64_t n_tt = (a.T + 15) / 16;
+  const int64_t SH = a.n_vec / a.T;
+  const int64_t wave = xcd_wave_id();
+  const int64_t tt = wave % n_tt;
+  const int64_t sh0 = (wave / n_tt) * sh_chunk;
+  if (sh0 >= SH) return;
+  const int64_t sh1 = min(SH, sh0 + sh_chunk);
+  const int64_t t = tt * 16 + v;
+  const bool tvalid = t < a.T;
+  const int64_t tc = tvalid ? t : a.T - 1;
+
+  // H's fragments: the two per-lane sign patterns and their negatives
+  nq_f16x8 Ap[2], An[2];
+#pragma unroll
+  for (int t0 = 0; t0 < 2; ++t0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int par =
+          __builtin_popcount(v & j & 3) + t0 * (j >> 2) + __builtin_popcount((v >> 2) & p);
+      Ap[t0][j] = (par & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
+      An[t0][j] = (par & 1) ? (_Float16)1.0f : (_Float16)-1.0f;
+    }
+  }
+  const float kr = a.half_L * 2.f;  // the 2-bit decoder works on g = 2y
+
+  const uint32_t off_x = (uint32_t)(tc * 256) + 64u * (uint32_t)p;
+  const uint32_t off_c = (uint32_t)(tc * a.code_bytes) + 8u * (uint32_t)p;
+  const uint32_t off_s = (uint32_t)(tc * a.coset_bytes);
+  const int64_t plane_x = a.T * 256;
+  const int64_t plane_c = a.pT * a.code_bytes;
+  const int64_t plane_s = a.pT * a.coset_bytes;
+  const int64_t plane_g = a.pT;  // one fp16 scale per vector
+  const uint32_t off_gb = (uint32_t)(tc + (int64_t)p * plane_g) * 2u;
+  const int n_it = (int)(sh1 - sh0);
+  const char* xb = static_cast<const char*>(a.x) + sh0 * plane_x;
+  uint8_t* cb = a.codes + sh0 * plane_c;
+  uint8_t* qb = a.cosets + sh0 * plane_s;
+  char* gb = reinterpret_cast<char*>(a.scales) + sh0 * plane_g * 2;
+  uint32_t ox = off_x, oc = off_c, os = off_s;
+  float keep = 0.f;
+  // the next plane's input is in flight while one is decoded
+  uint4 nxt[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) nxt[k] = *reinterpret_cast<const uint4*>(xb + ox + 16 * k);
+  for (int it = 0; it < n_it; ++it, xb += plane_x, cb += plane_c, qb += plane_s) {
+    asm volatile("" : "+v"(ox), "+v"(oc), "+v"(os));
+    uint4 raw[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) raw[k] = nxt[k];
+    if (it + 1 < n_it) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        nxt[k] = *reinterpret_cast<const uint4*>(xb + plane_x + ox + 16 * k);
+    }
+    nq_f4 acc[8];
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau) acc[tau] = nq_f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const nq_f16x8 B = __builtin_bit_cast(nq_f16x8, raw[k]);
+#pragma unroll
+      for (int tau = 0; tau < 8; ++tau) {
+        const bool neg = ((((tau >> 1) & 1) * (k & 1) + ((tau >> 2) & 1) * (k >> 1)) & 1) != 0;
+        acc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(neg ? An[tau & 1] : Ap[tau & 1], B,
+                                                          acc[tau], 0, 0, 0);
+      }
+    }
+    // vector maximum of |u|: the lane's 32 values, then the 4 lanes of the
+    // vector (16 and 32 lanes apart)
+    float mx = 0.f;
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(acc[tau][r]));
+    {
+      const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                        false, false);
+      mx = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
+      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
+                                                        false, false);
+      mx = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+    }
+    float amax;
+    asm("v_max_f32 %0, %1, %2" : "=v"(amax) : "s"(a.eps), "v"(mx));
+    const float rs = __fmul_rn(rcp_rn(amax), kr);
+    uint32_t cw = 0, words[2] = {0u, 0u};
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = __fmul_rn(acc[2 * h + (e >> 2)][e & 3], rs);
+      uint32_t code;
+      uint64_t cball;
+      int c;
+      e8_decode2<STRICT>(y, code, cball, c);
+      if (STRICT && a.compact) code = Compact<2>::fold(code, c);
+      cw |= (uint32_t)c << h;
+      words[h >> 1] |= code << (16 * (h & 1));
+    }
+    if (tvalid) *reinterpret_cast<uint2*>(cb + oc) = make_uint2(words[0], words[1]);
+    // coset word of the vector: bits 4p .. 4p+3 from lane p
+    {
+      uint32_t x = cw << (4 * p);
+      const auto s16 = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+      x = s16[0] | s16[1];
+      const auto s32 = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+      x = s32[0] | s32[1];
+      if (tvalid && p == 0 && !a.compact) *reinterpret_cast<uint16_t*>(qb + os) = (uint16_t)x;
+    }
+    // scales: lane p converts and stores the scale of iteration 4q + p
+    const int slot = it & 3;
+    if (p == slot) keep = amax;
+    if (slot == 3 || it == n_it - 1) {
+      if (tvalid && p <= slot) {
+        char* sb = gb + (int64_t)(it - slot) * plane_g * 2;
+        *reinterpret_cast<uint16_t*>(sb + off_gb) = f64_to_f16_rn((double)keep * a.sigma_k);
       }
     }
   }
@@ -1183,8 +1338,6 @@ constexpr int kLutBlock = 512;
 // Table entries: HPP floats side by side.  2 and 4 heads use native vector
 // types and vector accumulation, so that each lookup stays one 8- or 16-byte
 // LDS read (per-component use lets the compiler split it into scalar reads).
-typedef float nq_f2 __attribute__((ext_vector_type(2)));
-typedef float nq_f4 __attribute__((ext_vector_type(4)));
 template <int HPP>
 struct LutVec;
 template <> struct LutVec<1> { using T = float; };
@@ -2341,13 +2494,31 @@ hipError_t quantize_fast_rope(const TensorArgs& a, hipStream_t s) {
   return quantize_fast_launch<N, BITS, STRICT, T, 2, true>(a, s);
 }
 
+// 16 tokens per wave, kQmChunk (slab, head) planes per wave, tile-fastest.
+template <bool STRICT>
+hipError_t quantize_mfma_launch(const TensorArgs& a, hipStream_t s) {
+  const int64_t SH = a.n_vec / a.T;
+  const int64_t n_tt = (a.T + 15) / 16;
+  const int chunk = (int)(SH < kQmChunk ? SH : kQmChunk);
+  const int64_t waves = n_tt * ((SH + chunk - 1) / chunk);
+  const int64_t blocks = ((waves + kBlock / 64 - 1) / (kBlock / 64) + 7) / 8 * 8;
+  hipLaunchKernelGGL((quantize_mfma_kernel<STRICT>), dim3((unsigned)blocks), dim3(kBlock), 0, s,
+                     a, chunk);
+  return hipGetLastError();
+}
+
 template <int N, int BITS, typename T>
 hipError_t quantize_n(const TensorArgs& a, hipStream_t s) {
   if constexpr (N <= 128) {
     // per-lane byte offsets are 32-bit, in the dense planes and the packed ones
-    if (max(a.T, a.pT) * a.d * (int64_t)sizeof(T) < ((int64_t)1 << 31))
+    if (max(a.T, a.pT) * a.d * (int64_t)sizeof(T) < ((int64_t)1 << 31)) {
+      if constexpr (N == 128 && BITS == 2 && std::is_same<T, __half>::value) {
+        if (a.d == 128 && a.n_scales == 1 && a.rope == nullptr)
+          return a.strict ? quantize_mfma_launch<true>(a, s) : quantize_mfma_launch<false>(a, s);
+      }
       return a.strict ? quantize_fast_rope<N, BITS, true, T>(a, s)
                       : quantize_fast_rope<N, BITS, false, T>(a, s);
+    }
   }
   constexpr int VPB = kBlock / (N / 8);
   const int64_t blocks = (a.n_vec + VPB - 1) / VPB;

@@ -3,9 +3,10 @@
 Acceptance (codes): packed code and coset bytes equal per 8-group, except
 groups where the GPU's codeword is a valid codeword whose squared distance to
 y exceeds the oracle's by less than 1e-6 (y in lattice units, fp64); such
-exempt groups must number at most 1e-6 of all groups.  Scales: equal bits.
-Dequantized vectors: |x_gpu - x_ref| <= 1e-3 |x_ref| per vector (plus 1e-6
-absolute for near-zero vectors).  Scores: |S_gpu - S_ref| <= 1e-3 |q| |D0 k|.
+exempt groups must number at most 1e-6 of all groups.  Scales: equal bits,
+or one fp16 step where the oracle's sigma lies within 1e-6 relative of an
+fp16 rounding midpoint.  Dequantized vectors: |x_gpu - x_ref| <= 1e-3
+|x_ref| per vector (plus 1e-6 absolute for near-zero vectors).  Scores: |S_gpu - S_ref| <= 1e-3 |q| |D0 k|.
 """
 
 import math
@@ -60,16 +61,30 @@ def check_codes(codes, cosets, scales, ref, codec: oc.Codec, label=""):
     rs = ref["cosets"].reshape(rc.shape[0], codec.coset_bytes)
     rsc = ref["scales"].reshape(-1, codec.n_scales)
     assert codes.shape == rc.shape, (label, codes.shape, rc.shape)
-    # scales: bit-exact (both sides round a * (1/((L/2) sqrt n)) once to fp16)
-    bad_sc = np.nonzero(scales.view(np.uint16) != rsc.view(np.uint16))
-    assert len(bad_sc[0]) == 0, f"{label}: {len(bad_sc[0])} scale mismatches, first at {bad_sc[0][:5]}"
+    # scales: equal bits (both sides round a * (1/((L/2) sqrt n)) once to
+    # fp16), except one fp16 step where the oracle's a * k lies within 1e-6
+    # relative of the midpoint of the two fp16 numbers: there a few fp32 ulps
+    # of difference in the group maximum (Hadamard sums added in another
+    # order) round it the other way
+    sg, sr = scales.view(np.uint16), rsc.view(np.uint16)
+    bad_sc = np.nonzero(sg != sr)
+    if len(bad_sc[0]):
+        k = 1.0 / ((L / 2) * math.sqrt(n))
+        a = np.asarray(ref["a"], np.float32).reshape(sr.shape).astype(np.float64)[bad_sc]
+        g16, r16 = sg[bad_sc], sr[bad_sc]
+        step = np.abs(g16.astype(np.int64) - r16.astype(np.int64)) == 1
+        mid = (g16.view(np.float16).astype(np.float64) + r16.view(np.float16).astype(np.float64)) / 2
+        near = np.abs(a * k - mid) <= 1e-6 * np.abs(a * k)
+        assert (step & near).all(), \
+            f"{label}: {int((~(step & near)).sum())} scale mismatches away from an fp16 midpoint"
+    stats_sc = int(len(bad_sc[0]))
     idx_g, c_g = unpack_planes(codes, cosets, codec)
     idx_r = ref["idx"].reshape(-1, 8)
     c_r = ref["c"].reshape(-1)
     mism = np.any(idx_g != idx_r, axis=1) | (c_g != c_r)
     n_groups = idx_r.shape[0]
     n_bad = int(mism.sum())
-    stats = {"groups": n_groups, "exempt": n_bad, "max_regret": 0.0}
+    stats = {"groups": n_groups, "exempt": n_bad, "max_regret": 0.0, "scale_steps": stats_sc}
     if n_bad:
         y = ref["y"].reshape(-1, 8)[mism].astype(np.float64)
         pg = lattice.codeword_points(idx_g[mism], c_g[mism], L)

@@ -42,6 +42,10 @@ CASES = [
     ("d80-g16-strict", nq.Config(80, 2, 2, 16, S_, F16, 1e4), 1, 2, 95, False),
     ("d16-g8", nq.Config(16, 2, 3, 8, S_, F16, 0.0), 3, 1, 50, False),
     ("single-token", nq.Config(128, 2, 2, 0, S_, F16, 5e5), 1, 1, 1, True),
+    # no RoPE removal: keys and values both take the matrix-core rotation
+    # (16-token tiles, 8 planes per wave: ragged tiles and plane chunks)
+    ("norope-relaxed", nq.Config(128, 2, 2, 0, R_, F16, 0.0), 1, 11, 45, False),
+    ("norope-strict", nq.Config(128, 2, 2, 0, S_, F16, 0.0), 2, 5, 77, False),
     # Llama-3.1 frequency scaling (factor 8, bands 1 / 4, 8192 original
     # context) at positions up to 65535; linear scaling by 4
     ("llama31-rope-scaled", nq.Config(128, 2, 2, 0, R_, F16, 5e5, nq.ROPE_SCALING_LLAMA3,
