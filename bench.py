@@ -40,25 +40,28 @@ def parse():
     return ap.parse_args()
 
 
-def profiled_traffic(profile):
-    """HBM bytes per launch from a committed rocprofv3 summary (FETCH_SIZE and
-    WRITE_SIZE, each scaled by the copy-kernel calibration), or None when the
-    kernel source has changed since the counters were taken."""
+def profiled_traffic(profiles):
+    """HBM bytes per launch from committed rocprofv3 summaries (FETCH_SIZE and
+    WRITE_SIZE, each scaled by the copy-kernel calibration), averaged over the
+    summaries (one per launch of the step), or None when any is missing or the
+    kernel source has changed since its counters were taken."""
     import hashlib
     import re
 
-    path = os.path.join(ROOT, "profiles", profile)
     src = os.path.join(ROOT, "e8_lattice_vector_amd", "csrc", "nq_kernels.hip")
-    try:
-        text = open(path).read()
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    except OSError:
-        return None
-    m_sha = re.search(r"nq_kernels.hip sha256: ([0-9a-f]{64})", text)
-    m_tr = re.search(r"traffic_bytes_per_launch: (\d+)", text)
-    if not m_sha or not m_tr or m_sha.group(1) != sha:
-        return None
-    return int(m_tr.group(1))
+    vals = []
+    for profile in profiles:
+        try:
+            text = open(os.path.join(ROOT, "profiles", profile)).read()
+            sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        except OSError:
+            return None
+        m_sha = re.search(r"nq_kernels.hip sha256: ([0-9a-f]{64})", text)
+        m_tr = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+        if not m_sha or not m_tr or m_sha.group(1) != sha:
+            return None
+        vals.append(int(m_tr.group(1)))
+    return round(sum(vals) / len(vals)) if vals else None
 
 
 def cpu_baseline(w, tokens, slabs):
@@ -294,9 +297,11 @@ def main():
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": q_gbps / HBM_PEAK_GBPS,
-            "traffic": profiled_traffic("quantize_fast_kernel-llama-3.1-8b-32k.md"),
+            "traffic": profiled_traffic(["quantize_fast_kernel-llama-3.1-8b-32k.md",
+                                         "quantize_mfma_kernel-llama-3.1-8b-32k.md"]),
             "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
-            "kernel": "quantize_kernel (K launch incl. RoPE-table build, and V launch)",
+            "kernel": "quantize: K launch quantize_fast_kernel (butterfly Hadamard, incl. "
+                      "RoPE-table build), V launch quantize_mfma_kernel (matrix-core Hadamard)",
             "avg_launch_ms": tq / 2,
         },
     }

@@ -27,11 +27,15 @@ def test_profiled_traffic_requires_matching_source(tmp_path, monkeypatch):
     prof.mkdir()
     sha = hashlib.sha256(b"kernel v1").hexdigest()
     (prof / "k.md").write_text(f"nq_kernels.hip sha256: {sha}\n\ntraffic_bytes_per_launch: 12345\n")
+    (prof / "v.md").write_text(f"nq_kernels.hip sha256: {sha}\n\ntraffic_bytes_per_launch: 10001\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    assert bench.profiled_traffic("k.md") == 12345
+    assert bench.profiled_traffic(["k.md"]) == 12345
+    # one launch per summary: the step's per-launch traffic is their mean
+    assert bench.profiled_traffic(["k.md", "v.md"]) == 11173
+    assert bench.profiled_traffic(["k.md", "missing.md"]) is None
     (src / "nq_kernels.hip").write_bytes(b"kernel v2")
-    assert bench.profiled_traffic("k.md") is None
-    assert bench.profiled_traffic("missing.md") is None
+    assert bench.profiled_traffic(["k.md"]) is None
+    assert bench.profiled_traffic(["k.md", "v.md"]) is None
 
 
 def test_cpu_baseline_leg_runs_the_oracle():
