@@ -163,6 +163,11 @@ const char* nq_status_string(int status);
  * (rope_theta > 0), the vector is zero-padded to n and rotated by the
  * Walsh-Hadamard matrix, scaled per group of G, and each 8-group is replaced
  * by its nearest codeword of the lattice restricted to b-bit coordinates.
+ * Arithmetic: fp32.  The transform runs as butterfly stages (each sum one
+ * fp32 rounding, stages in the order h = 1, 2, ..., n/2); for fp16 vectors
+ * without RoPE at d = n = 128, 2 bits, one scale per vector, as a +-1 matrix
+ * product on the matrix cores (exact products, fp32 sums in the hardware's
+ * order), whose y may differ from the stage-order one in its last bits.
  *  k, v        device [S][H][T][d] inputs; either may be NULL (then the
  *              matching packed planes are not touched)
  *  positions   device int32 [T] token positions for RoPE, or NULL for
