@@ -1104,6 +1104,167 @@ __global__ __launch_bounds__(kBlock) void dequantize_fast_kernel(TensorArgs a,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Dequantize keys with the rotation on the matrix cores (RoPE, d = n = 128,
+// 2-bit codes, one scale per vector, fp16 output).
+//
+// The B operand of chunk k holds 8-group 4p + k of vector v (lane
+// l = 16p + v) as fp16 numbers 1024 + 2 idx + c (2p + 1028 for the codeword
+// point p = idx - 2 + c/2): exact, and so is every sum of 128 of them, so
+// u' = H (2p + 1028) comes out of the matrix cores exact in fp32.  Since
+// H 1 = 128 e_0, H p = (u' - 1028 * 128 e_0) / 2, and x = (s16 / sqrt(n)) H p
+// takes one rounded product per coordinate.  Row m of output tile tau is
+// output coordinate (m & 7) + 8 (tau & 1) + 16 (tau >> 1 & 1) + 32 (m >> 3)
+// + 64 (tau >> 2), so a coordinate and its RoPE partner (+ 64) sit in tiles
+// tau and tau ^ 4 of the same lane; (-1)^popcount(out & in) splits into a
+// per-lane pattern chosen by tau >> 2 times the tile-uniform sign
+// (-1)^((tau & 1)(k & 1) + (tau >> 1 & 1)(k >> 1)).  The fp16 results pass
+// through the wave's LDS tile so that every global store writes 1 KiB of
+// contiguous output.  A wave keeps its 16-token tile (and the tile's cos /
+// sin in registers) while it walks kDmChunk (slab, head) planes; neighbouring
+// waves take neighbouring tiles.
+// ---------------------------------------------------------------------------
+constexpr int kDmChunk = 32;
+
+template <bool CMP>
+__global__ __launch_bounds__(kBlock) void dequantize_mfma_kernel(TensorArgs a, int sh_chunk) {
+  const int lane = threadIdx.x & 63;
+  const int v = lane & 15;
+  const int p = lane >> 4;
+  const int64_t n_tt = (a.T + 15) / 16;
+  const int64_t SH = a.n_vec / a.T;
+  const int64_t wave = xcd_wave_id();
+  const int64_t tt = wave % n_tt;
+  const int64_t sh0 = (wave / n_tt) * sh_chunk;
+  if (sh0 >= SH) return;
+  const int64_t sh1 = min(SH, sh0 + sh_chunk);
+  const int64_t t = tt * 16 + v;
+  const bool tvalid = t < a.T;
+  const int64_t tc = tvalid ? t : a.T - 1;
+
+  // H's fragments: the two per-lane sign patterns and their negatives
+  nq_f16x8 Ap[2], An[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int par = __builtin_popcount(v & j & 7) + ((v >> 3) & 1) * (p & 1) + q * (p >> 1);
+      Ap[q][j] = (par & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
+      An[q][j] = (par & 1) ? (_Float16)1.0f : (_Float16)-1.0f;
+    }
+  }
+  // cos / sin of angle (coordinate mod 64) r + 4 p0 + 32 p1 + 8 tau0 + 16 tau1
+  float rc[4][4], rn[4][4];
+  {
+    const float2* rp = a.rope + tc * 64 + 4 * (p & 1) + 32 * (p >> 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float2 cs = rp[8 * (q & 1) + 16 * (q >> 1) + r];
+        rc[q][r] = cs.x;
+        rn[q][r] = cs.y;
+      }
+    }
+  }
+  const float half_rs = 0.5f * a.inv_sqrt_n;
+  const uint32_t off_c = (uint32_t)(tc * a.code_bytes) + 8u * (uint32_t)p;
+  const uint32_t off_s = (uint32_t)(tc * a.coset_bytes);
+  const uint32_t off_g = (uint32_t)tc * 2u;
+  // output: the tile's 4 KiB stretch, 16 bytes per lane per store
+  const uint32_t off_y = (uint32_t)(tt * 16 * 256) + 16u * (uint32_t)lane;
+  __shared__ __align__(16) char lds_tiles[kBlock / 64][16 * 256];
+  char* tile = lds_tiles[threadIdx.x >> 6];
+  const int64_t plane_y = a.T * 256;
+  const int64_t plane_c = a.pT * a.code_bytes;
+  const int64_t plane_s = a.pT * a.coset_bytes;
+  const int64_t plane_g = a.pT * 2;
+  const int n_it = (int)(sh1 - sh0);
+  char* yb = static_cast<char*>(a.y) + sh0 * plane_y;
+  const uint8_t* cb = a.codes + sh0 * plane_c;
+  const uint8_t* qb = a.cosets + sh0 * plane_s;
+  const char* gb = reinterpret_cast<const char*>(a.scales) + sh0 * plane_g;
+  uint32_t oc = off_c, os = off_s, og = off_g, oy = off_y;
+  // the next plane's code words, coset word and scale are loaded one ahead
+  auto load_meta = [&](int q, uint2& cw, uint32_t& cs, uint32_t& sb) {
+    cw = *reinterpret_cast<const uint2*>(cb + q * plane_c + oc);
+    cs = CMP ? 0u : (uint32_t)*reinterpret_cast<const uint16_t*>(qb + q * plane_s + os);
+    sb = (uint32_t)*reinterpret_cast<const uint16_t*>(gb + q * plane_g + og);
+  };
+  uint2 cw_n;
+  uint32_t cs_n, sb_n;
+  load_meta(0, cw_n, cs_n, sb_n);
+  for (int it = 0; it < n_it;
+       ++it, yb += plane_y, cb += plane_c, qb += plane_s, gb += plane_g) {
+    asm volatile("" : "+v"(oc), "+v"(os), "+v"(og), "+v"(oy));
+    const uint2 cw = cw_n;
+    const uint32_t cs = cs_n, sbits = sb_n;
+    if (it + 1 < n_it) load_meta(1, cw_n, cs_n, sb_n);
+    nq_f4 acc[8];
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau) acc[tau] = nq_f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t w = ((k < 2 ? cw.x : cw.y) >> (16 * (k & 1))) & 0xffffu;
+      int c = (int)((cs >> (4 * p + k)) & 1u);
+      if (CMP) w = Compact<2>::unfold(w, c);
+      // fp16 1024 + 2 idx + c for the group's 8 coordinates, two per word
+      const uint32_t base = 0x64006400u | (c ? 0x00010001u : 0u);
+      uint32_t bw[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t nib = (w >> (4 * q)) & 0xfu;
+        bw[q] = (((nib | (nib << 14)) & 0x00030003u) << 1) | base;
+      }
+      const nq_f16x8 B = __builtin_bit_cast(nq_f16x8, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+#pragma unroll
+      for (int tau = 0; tau < 8; ++tau) {
+        const bool neg = (((tau & 1) * (k & 1) + ((tau >> 1) & 1) * (k >> 1)) & 1) != 0;
+        acc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(neg ? An[tau >> 2] : Ap[tau >> 2], B,
+                                                          acc[tau], 0, 0, 0);
+      }
+    }
+    // coordinate 0 (lane p = 0, tile 0, row 0) carries the 1028 * 128 offset
+    if (p == 0) acc[0][0] -= 131584.f;
+    const float f = h2f((uint16_t)sbits) * half_rs;
+    float x[8][4];
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[tau][r] = acc[tau][r] * f;
+    // RoPE forward: x_i c - x_{i+64} s (lower half), x_{i+64} c + x_i s
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float lo = x[q][r], up = x[q + 4][r];
+        x[q][r] = __fmaf_rn(lo, rc[q][r], -(up * rn[q][r]));
+        x[q + 4][r] = __fmaf_rn(up, rc[q][r], lo * rn[q][r]);
+      }
+    }
+    // fp16 results into the wave's LDS tile (16 tokens x 256 B; the 16-byte
+    // chunks of token row v rotated by v against bank conflicts)
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau) {
+      const uint32_t u0 = __builtin_bit_cast(uint32_t, __floats2half2_rn(x[tau][0], x[tau][1]));
+      const uint32_t u1 = __builtin_bit_cast(uint32_t, __floats2half2_rn(x[tau][2], x[tau][3]));
+      // byte 8 p0 + 64 p1 + 16 tau0 + 32 tau1 + 128 tau2 of row v
+      const int ch = 4 * (p >> 1) + (tau & 1) + 2 * ((tau >> 1) & 1) + 8 * (tau >> 2);
+      *reinterpret_cast<uint2*>(tile + v * 256 + ((ch ^ v) << 4) + 8 * (p & 1)) =
+          make_uint2(u0, u1);
+    }
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // store i, lane l: token row 4i + p of the tile, 16-byte chunk v
+      const int row = 4 * i + p;
+      const uint4 val = *reinterpret_cast<const uint4*>(tile + row * 256 + ((v ^ row) << 4));
+      if (tt * 16 + row < a.T) *reinterpret_cast<uint4*>(yb + oy + 1024 * i) = val;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 // Token-walking variant for tensors without RoPE (values; keys with theta =
 // 0), n = 64 or 128: wave -> ((slab, head) plane, run of kTwTiles token
 // tiles).  The wave first copies the run's packed bytes (codes, cosets,
@@ -2568,8 +2729,31 @@ hipError_t dequantize_tw_launch(const TensorArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// 16 tokens per wave, kDmChunk (slab, head) planes per wave, tile-fastest.
+inline hipError_t dequantize_mfma_launch(const TensorArgs& a, hipStream_t s) {
+  const int64_t SH = a.n_vec / a.T;
+  const int64_t n_tt = (a.T + 15) / 16;
+  const int chunk = (int)(SH < kDmChunk ? SH : kDmChunk);
+  const int64_t waves = n_tt * ((SH + chunk - 1) / chunk);
+  const int64_t blocks = ((waves + kBlock / 64 - 1) / (kBlock / 64) + 7) / 8 * 8;
+  if (a.compact)
+    hipLaunchKernelGGL((dequantize_mfma_kernel<true>), dim3((unsigned)blocks), dim3(kBlock), 0, s,
+                       a, chunk);
+  else
+    hipLaunchKernelGGL((dequantize_mfma_kernel<false>), dim3((unsigned)blocks), dim3(kBlock), 0, s,
+                       a, chunk);
+  return hipGetLastError();
+}
+
 template <int N, int BITS, typename T>
 hipError_t dequantize_n(const TensorArgs& a, hipStream_t s) {
+  if constexpr (N == 128 && BITS == 2 && std::is_same<T, __half>::value) {
+    // keys with RoPE; per-lane byte offsets are 32-bit, in the dense planes
+    // and the packed ones
+    if (a.rope != nullptr && a.d == 128 && a.n_scales == 1 &&
+        max(a.T, a.pT) * 256 < ((int64_t)1 << 31))
+      return dequantize_mfma_launch(a, s);
+  }
   if constexpr ((N == 64 || N == 128) && (N * BITS / 8) % 16 == 0) {
     if (a.rope == nullptr) return dequantize_tw_launch<N, BITS, T>(a, s);
   }

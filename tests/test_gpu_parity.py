@@ -46,6 +46,9 @@ CASES = [
     # (16-token tiles, 8 planes per wave: ragged tiles and plane chunks)
     ("norope-relaxed", nq.Config(128, 2, 2, 0, R_, F16, 0.0), 1, 11, 45, False),
     ("norope-strict", nq.Config(128, 2, 2, 0, S_, F16, 0.0), 2, 5, 77, False),
+    # RoPE keys on the matrix-core dequantize (32 planes per wave: 35 planes
+    # leave a chunk of 3; 37 tokens leave a tile of 5), explicit positions
+    ("llama-plane-chunks", nq.Config(128, 2, 2, 0, R_, F16, 5e5), 5, 7, 37, True),
     # Llama-3.1 frequency scaling (factor 8, bands 1 / 4, 8192 original
     # context) at positions up to 65535; linear scaling by 4
     ("llama31-rope-scaled", nq.Config(128, 2, 2, 0, R_, F16, 5e5, nq.ROPE_SCALING_LLAMA3,
