@@ -186,6 +186,10 @@ int nq_quantize_kv(const nq_config* cfg, const void* k, const void* v,
  * the device; [RM] "How it works": RoPE re-applied after quantization):
  * p = idx - L/2 + c/2, z = s16 * p, x = (H z / sqrt(n))[:d], keys get RoPE
  * at `positions` (rope_theta > 0), rounded to the output dtype (RNE).
+ * Arithmetic: fp32.  For fp16 keys with RoPE at d = n = 128, 2 bits, one
+ * scale per vector, H p is formed exactly on the matrix cores and scaled by
+ * s16 / sqrt(n) once; otherwise z = s16 / sqrt(n) * p goes through butterfly
+ * stages.
  *  k_out, v_out  device [S][H][T][d] outputs (either may be NULL)
  * Errors as nq_quantize_kv. */
 int nq_dequantize_kv(const nq_config* cfg, const nq_packed* pk,
