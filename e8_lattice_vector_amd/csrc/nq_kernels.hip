@@ -32,6 +32,11 @@ namespace {
 
 constexpr int kBlock = 256;
 
+// min / max of 64-bit values (HIP's unqualified min / max of two int64_t
+// resolve to the int overloads and truncate)
+__host__ __device__ constexpr int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+__host__ __device__ constexpr int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
+
 typedef float nq_f2 __attribute__((ext_vector_type(2)));
 typedef float nq_f4 __attribute__((ext_vector_type(4)));
 
@@ -586,7 +591,7 @@ __global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
   const int64_t tt = tile_major ? wave / n_shc : wave % n_tt;
   const int64_t sh0 = (tile_major ? wave % n_shc : wave / n_tt) * sh_chunk;
   if (tt >= n_tt || sh0 >= SH) return;
-  const int64_t sh1 = min(SH, sh0 + sh_chunk);
+  const int64_t sh1 = min64(SH, sh0 + sh_chunk);
   const int64_t t = tt * TPW + row;
   const bool tvalid = t < a.T;
   const int64_t tc = tvalid ? t : a.T - 1;
@@ -782,7 +787,7 @@ __global__ __launch_bounds__(kBlock) void quantize_mfma_kernel(TensorArgs a, int
   const int64_t tt = wave % n_tt;
   const int64_t sh0 = (wave / n_tt) * sh_chunk;
   if (sh0 >= SH) return;
-  const int64_t sh1 = min(SH, sh0 + sh_chunk);
+  const int64_t sh1 = min64(SH, sh0 + sh_chunk);
   const int64_t t = tt * 16 + v;
   const bool tvalid = t < a.T;
   const int64_t tc = tvalid ? t : a.T - 1;
@@ -1006,7 +1011,7 @@ __global__ __launch_bounds__(kBlock) void dequantize_fast_kernel(TensorArgs a,
   const int64_t tt = tile_major ? wave / n_shc : wave % n_tt;
   const int64_t sh0 = (tile_major ? wave % n_shc : wave / n_tt) * sh_chunk;
   if (tt >= n_tt || sh0 >= SH) return;
-  const int64_t sh1 = min(SH, sh0 + sh_chunk);
+  const int64_t sh1 = min64(SH, sh0 + sh_chunk);
   const int64_t t = tt * TPW + row;
   const bool tvalid = t < a.T;
   const int64_t tc = tvalid ? t : a.T - 1;
@@ -1137,7 +1142,7 @@ __global__ __launch_bounds__(kBlock) void dequantize_mfma_kernel(TensorArgs a, i
   const int64_t tt = wave % n_tt;
   const int64_t sh0 = (wave / n_tt) * sh_chunk;
   if (sh0 >= SH) return;
-  const int64_t sh1 = min(SH, sh0 + sh_chunk);
+  const int64_t sh1 = min64(SH, sh0 + sh_chunk);
   const int64_t t = tt * 16 + v;
   const bool tvalid = t < a.T;
   const int64_t tc = tvalid ? t : a.T - 1;
@@ -1309,7 +1314,7 @@ __global__ __launch_bounds__(kBlock) void dequantize_tw_kernel(TensorArgs a) {
   if (sh >= SH) return;                     // whole wave; no block barrier below
   const int64_t tt0 = (wave % n_run) * kTwTiles;
   const int64_t tok0 = tt0 * TPW;
-  const int nt = (int)min((int64_t)RUN, a.T - tok0);   // tokens of this run
+  const int nt = (int)min64((int64_t)RUN, a.T - tok0);   // tokens of this run
   const int64_t v0 = sh * a.pT + tok0;                 // first packed vector
   {
     // codes: nt * CB bytes, 16-byte aligned at both ends
@@ -1430,7 +1435,7 @@ __global__ __launch_bounds__(kBlock) void score_kernel(ScoreArgs a) {
     }
     __syncthreads();
   }
-  const int64_t t_end = min(a.T, (int64_t)(blockIdx.x + 1) * kScoreKeys);
+  const int64_t t_end = min64(a.T, (int64_t)(blockIdx.x + 1) * kScoreKeys);
   const int gl = a.G >> 3;
   for (int64_t t = (int64_t)blockIdx.x * kScoreKeys + threadIdx.x; t < t_end;
        t += blockDim.x) {
@@ -1633,7 +1638,7 @@ __global__ __launch_bounds__(kLutBlock) void score_lut_kernel(ScoreArgs a,
   constexpr int KG = CSB / NS;             // coset (parity) bytes per scale group
   static_assert(CB % NS == 0 && CSB % NS == 0, "scale groups must cover whole bytes");
   const int64_t t0 = (int64_t)blockIdx.x * chunk;
-  const int64_t t1 = min(a.T, t0 + chunk);
+  const int64_t t1 = min64(a.T, t0 + chunk);
   const int64_t base = (s * a.H + h) * a.pT;   // packed planes: token stride pT
   for (int64_t t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
     const int64_t vec = base + t;
@@ -2264,7 +2269,7 @@ __global__ __launch_bounds__(kScoreMfmaBlock, 8) void score_mfma_kernel(ScoreArg
   const char* tb = reinterpret_cast<const char*>(tbl);
   // this workgroup's keys t0 .. t0 + nk - 1 (nk < 2^26: 32-bit offsets)
   const int64_t t0 = (int64_t)blockIdx.x * chunk;
-  const int nk = (int)(min(a.T, t0 + chunk) - t0);
+  const int nk = (int)(min64(a.T, t0 + chunk) - t0);
   const int64_t base = (s * a.H + h) * a.pT + t0;
   const uint8_t* cp = a.codes + base * (N / 4);
   const uint16_t* csp = reinterpret_cast<const uint16_t*>(a.cosets) + base;
@@ -2672,7 +2677,7 @@ template <int N, int BITS, typename T>
 hipError_t quantize_n(const TensorArgs& a, hipStream_t s) {
   if constexpr (N <= 128) {
     // per-lane byte offsets are 32-bit, in the dense planes and the packed ones
-    if (max(a.T, a.pT) * a.d * (int64_t)sizeof(T) < ((int64_t)1 << 31)) {
+    if (max64(a.T, a.pT) * a.d * (int64_t)sizeof(T) < ((int64_t)1 << 31)) {
       if constexpr (N == 128 && BITS == 2 && std::is_same<T, __half>::value) {
         if (a.d == 128 && a.n_scales == 1 && a.rope == nullptr)
           return a.strict ? quantize_mfma_launch<true>(a, s) : quantize_mfma_launch<false>(a, s);
@@ -2751,7 +2756,7 @@ hipError_t dequantize_n(const TensorArgs& a, hipStream_t s) {
     // keys with RoPE; per-lane byte offsets are 32-bit, in the dense planes
     // and the packed ones
     if (a.rope != nullptr && a.d == 128 && a.n_scales == 1 &&
-        max(a.T, a.pT) * 256 < ((int64_t)1 << 31))
+        max64(a.T, a.pT) * 256 < ((int64_t)1 << 31))
       return dequantize_mfma_launch(a, s);
   }
   if constexpr ((N == 64 || N == 128) && (N * BITS / 8) % 16 == 0) {
@@ -2785,7 +2790,7 @@ hipError_t score_lut_launch(const ScoreArgs& a, int n_pass, hipStream_t s) {
   const int64_t pairs = a.S * a.H * n_pass;
   int64_t n_chunks = (256 + pairs - 1) / pairs;
   const int64_t min_chunk = 4 * kLutBlock;
-  n_chunks = max((int64_t)1, min(n_chunks, (a.T + min_chunk - 1) / min_chunk));
+  n_chunks = max64(1, min64(n_chunks, (a.T + min_chunk - 1) / min_chunk));
   const int64_t chunk = (a.T + n_chunks - 1) / n_chunks;
   const dim3 grid((unsigned)n_chunks, (unsigned)(a.H * n_pass), (unsigned)a.S);
   hipLaunchKernelGGL(kern, grid, dim3(kLutBlock), lds, s, a, n_pass, chunk);
@@ -2809,7 +2814,7 @@ hipError_t score_mfma_launch(const ScoreArgs& a, int n_pass, hipStream_t s) {
   const int64_t pairs = a.S * a.H * n_pass;
   int64_t n_chunks = (512 + pairs - 1) / pairs;
   const int64_t min_chunk = 4096;
-  n_chunks = max((int64_t)1, min(n_chunks, (a.T + min_chunk - 1) / min_chunk));
+  n_chunks = max64(1, min64(n_chunks, (a.T + min_chunk - 1) / min_chunk));
   const int64_t chunk = (a.T + n_chunks - 1) / n_chunks;
   const dim3 grid((unsigned)n_chunks, (unsigned)(a.H * n_pass), (unsigned)a.S);
   hipLaunchKernelGGL(kern, grid, dim3(kScoreMfmaBlock), lds, s, a, n_pass, chunk);
