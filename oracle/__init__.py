@@ -16,10 +16,13 @@ independently from the same pages:
 * Nedelkoski et al., "E8 Lattice Key Quantization for Low-Bit KV-Cache
   Compression", Abstract and Tables 2-3 (table-based asymmetric scoring).
 
-Everything that yields a floating-point result is computed in fp64.  Integer
-decisions (the lattice code) are taken on the fp32 value ``y`` that the codec
-defines, exactly (fp64 comparisons with an exact rational fallback at
-near-ties), so that oracle and kernel decide on the same number.
+Everything is computed in fp64 from the exact input values, including the
+value ``y`` that decides each lattice code; the decision itself is exact for
+that fp64 value (fp64 comparisons, with exact rational arithmetic wherever
+two compared costs are too close for fp64 to separate).  Functions that
+compute in fp32 (``transform.*_f32``, ``codec.compute_y_f32_stage_order``)
+are diagnostics: tests use them to bound the error of an fp32 computation of
+y; no acceptance decision rests on them.
 
 Parity status per function is recorded in each module's header.
 """

@@ -30,15 +30,17 @@ Sources
   dequantize-then-dot in fp64 (the kernel's table form is algebraically the
   same number; the oracle does not use that algebra).
 
-Definitions (one head vector x of d values, n = next power of two >= d):
-  K only, theta > 0:  x' = RoPE^-1(x)       (fp32, transform.rope_inverse_f32)
-  v = (x', 0, ..., 0) in R^n;  u = H_n v     (fp32, transform.fwht_f32)
+Definitions (one head vector x of d values, n = next power of two >= d),
+every step in fp64 from the exact input values:
+  K only, theta > 0:  x' = RoPE^-1(x)       (transform.rope_inverse_f64)
+  v = (x', 0, ..., 0) in R^n;  u = H_n v     (transform.fwht_f64)
   per scale group g of G coordinates:
-      a_g  = max(max_j |u_j|, fp32(1e-8 * sqrt(n)))   (1e-8 in orthonormal
-             units, z = u / sqrt(n))
-      r_g  = fp32((L/2) / a_g);  y_j = fp32(u_j * r_g)   -> max |y| = L/2
-      sigma_g = a_g / ((L/2) sqrt(n))  in fp64, stored as fp16 (RNE)
-  each 8-group of y -> lattice.decode -> idx in [0, L-1]^8, coset bit c
+      a_g  = max(max_j |u_j|, 1e-8 * sqrt(n))   (1e-8 in orthonormal units,
+             z = u / sqrt(n))
+      y_j  = (L/2) u_j / a_g                    -> max |y| = L/2 exactly
+      sigma_g = a_g / ((L/2) sqrt(n)), stored as fp16 (RNE)
+  each 8-group of y -> lattice.decode (exact nearest codeword of the fp64 y)
+  -> idx in [0, L-1]^8, coset bit c
   Dequantize: p = idx - L/2 + c/2;  z^ = s16 * p;  x^ = (H_n z^ / sqrt(n))[:d];
   keys then get RoPE back (the README's re-application after quantization).
   D0 denotes dequantization without the RoPE step (the codec frame).
@@ -122,10 +124,43 @@ def fp16_kv_bytes(layers: int, kv_heads: int, head_dim: int, tokens: int = 1):
 
 
 def compute_y(x, codec: Codec, positions=None, is_key: bool = False):
-    """fp32 y [.., n], group maxima a [.., n/G] -- the decision input."""
+    """y [.., n] and group maxima a [.., n/G], both fp64: the decision input.
+
+    Every step in fp64 from the exact input values (fp16 / fp32 widened
+    exactly): split-half RoPE removal with cos / sin of the fp64 angles
+    (keys, theta > 0), zero padding, u = H v (fast transform, each sum one
+    fp64 rounding; exact for fp16 inputs without RoPE, whose partial sums
+    fit in 53 bits), a = max(max |u|, 1e-8 sqrt(n)) per group (the page's
+    1e-8 floor in orthonormal units), and y = (L/2) u / a as one correctly
+    rounded division, so the group maximum maps to L/2 exactly.
+    """
+    x64 = np.asarray(x).astype(np.float64)
+    d = codec.head_dim
+    assert x64.shape[-1] == d
+    if is_key and codec.rope_theta > 0:
+        T = x64.shape[-2]
+        pos = np.arange(T) if positions is None else np.asarray(positions)
+        x64 = transform.rope_inverse_f64(x64, pos, codec.rope_theta, codec.rope_scaling)
+    n = codec.n
+    v = np.zeros(x64.shape[:-1] + (n,), dtype=np.float64)
+    v[..., :d] = x64
+    u = transform.fwht_f64(v)
+    G = codec.G
+    ug = u.reshape(u.shape[:-1] + (n // G, G))
+    a = np.maximum(np.max(np.abs(ug), axis=-1), 1e-8 * math.sqrt(n))
+    y = ((codec.L / 2) * ug / a[..., None]).reshape(u.shape)
+    return y, a
+
+
+def compute_y_f32_stage_order(x, codec: Codec, positions=None, is_key: bool = False):
+    """DIAGNOSTIC ONLY (not the decision input): the fp32 y of a butterfly
+    implementation that rounds every step to fp32 in a fixed order -- RoPE
+    removal as two rounded products and a rounded sum with fp32 cos / sin,
+    Walsh-Hadamard stages h = 1, 2, ..., n/2 each rounded once, r = fp32
+    ((L/2) / a), y = fp32(u r).  Tests use it to bound how far an fp32
+    computation of y lies from the fp64 one."""
     x32 = np.asarray(x).astype(np.float32)
     d = codec.head_dim
-    assert x32.shape[-1] == d
     if is_key and codec.rope_theta > 0:
         T = x32.shape[-2]
         pos = np.arange(T) if positions is None else np.asarray(positions)
@@ -137,16 +172,16 @@ def compute_y(x, codec: Codec, positions=None, is_key: bool = False):
     u = transform.fwht_f32(v)
     G = codec.G
     ug = u.reshape(u.shape[:-1] + (n // G, G))
-    eps = np.float32(1e-8 * math.sqrt(n))
-    a = np.maximum(np.max(np.abs(ug), axis=-1), eps)            # fp32
-    r = np.float32(codec.L / 2) / a                              # fp32 division
-    y = (ug * r[..., None]).reshape(u.shape)                     # fp32 product
+    a = np.maximum(np.max(np.abs(ug), axis=-1), np.float32(1e-8 * math.sqrt(n)))
+    r = np.float32(codec.L / 2) / a
+    y = (ug * r[..., None]).reshape(u.shape)
     return y.astype(np.float32), a.astype(np.float32)
 
 
 def scales_from_maxima(a, codec: Codec) -> np.ndarray:
+    """sigma = a / ((L/2) sqrt(n)) (orthonormal units), rounded once to fp16."""
     k = 1.0 / ((codec.L / 2) * math.sqrt(codec.n))
-    return (np.asarray(a, dtype=np.float32).astype(np.float64) * k).astype(np.float16)
+    return (np.asarray(a, dtype=np.float64) * k).astype(np.float16)
 
 
 def pack_codes(idx, bits: int) -> np.ndarray:

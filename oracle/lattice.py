@@ -39,6 +39,7 @@ bound, hand-worked example) -- see tests/test_oracle_lattice.py.
 
 from __future__ import annotations
 
+import math
 from fractions import Fraction
 
 import numpy as np
@@ -57,18 +58,20 @@ __all__ = [
 def _round_to_coset(y: np.ndarray, c: int) -> np.ndarray:
     """Nearest integer (c=0) or half-integer (c=1) to each coordinate, T1 ties.
 
-    ``y`` holds fp32 values widened to fp64, so |y| + 1/2 and floor(|y|) are
-    exact in fp64.
+    Exact for any fp64 input: with f = floor(|y|), |y| - f is exact (f = 0,
+    or f and |y| within a factor of two of each other), so the comparison
+    with 1/2 is exact; the nearest half-integer is always f + 1/2.
     """
     a = np.abs(y)
+    f = np.floor(a)
     if c == 0:
-        m = np.floor(a + 0.5)
+        m = f + (a - f >= 0.5)
     else:
-        m = np.floor(a) + 0.5
+        m = f + 0.5
     return np.copysign(m, y)
 
 
-def _exact_sqdist(y_row: np.ndarray, p_row: np.ndarray) -> Fraction:
+def _exact_sqdist(y_row, p_row) -> Fraction:
     return sum((Fraction(float(a)) - Fraction(float(b))) ** 2
                for a, b in zip(y_row, p_row))
 
@@ -76,13 +79,15 @@ def _exact_sqdist(y_row: np.ndarray, p_row: np.ndarray) -> Fraction:
 def _coset_candidate(y: np.ndarray, c: int, pmax: float | None, parity: bool):
     """Nearest point of one coset (optionally limited to |p| <= pmax).
 
-    Returns (p, d) with d the fp64 squared distance.  Rows whose parity step
-    has to choose between exactly equal costs are resolved by T3 because the
-    comparison key below is exact (|delta| needs no rounding).
+    Returns (p, d, fragile): p the candidate, d its fp64 squared distance,
+    and a mask of rows whose parity step compared two costs closer than
+    1e-12 (|delta| can round for half-integer candidates of tiny |y|); those
+    rows are recomputed exactly by the caller.
     """
     p = _round_to_coset(y, c)
     if pmax is not None:
         p = np.clip(p, -pmax, pmax)
+    fragile = np.zeros(y.shape[0], dtype=bool)
     if parity:
         # sum p is an integer on both cosets (8 half-integers sum to an integer)
         s = np.sum(p, axis=-1)
@@ -103,12 +108,54 @@ def _coset_candidate(y: np.ndarray, c: int, pmax: float | None, parity: bool):
             kappa = np.where(ok, np.abs(delta), -np.abs(delta))
             i_star = np.argmax(kappa, axis=-1)  # first index on ties (T3)
             rows = np.arange(po.shape[0])
+            top = np.sort(kappa, axis=-1)
+            near = (top[:, -1] - top[:, -2]) <= 1e-12
+            fragile[np.nonzero(odd)[0][near]] = True
             po = po.copy()
             po[rows, i_star] = alt[rows, i_star]
             p = p.copy()
             p[odd] = po
     d = np.sum((y - p) ** 2, axis=-1)
+    return p, d, fragile
+
+
+def _exact_candidate(y_row, c: int, pmax, parity: bool):
+    """One coset's candidate for one row in exact rational arithmetic (the
+    same steps as _coset_candidate)."""
+    ys = [Fraction(float(v)) for v in y_row]
+    neg = [math.copysign(1.0, float(v)) < 0 for v in y_row]
+    p = []
+    for v, n in zip(ys, neg):
+        a = abs(v)
+        f = Fraction(math.floor(a))
+        m = f + (1 if a - f >= Fraction(1, 2) else 0) if c == 0 else f + Fraction(1, 2)
+        if pmax is not None:
+            m = min(m, Fraction(pmax))
+        p.append(-m if n else m)
+    if parity and sum(p) % 2 != 0:
+        best, i_best, alt_best = None, -1, None
+        for i, (v, q, n) in enumerate(zip(ys, p, neg)):
+            delta = v - q
+            t = (1 if delta > 0 else -1) if delta != 0 else (-1 if n else 1)
+            toward = q + t
+            ok = pmax is None or abs(toward) <= Fraction(pmax)
+            kappa = abs(delta) if ok else -abs(delta)
+            if best is None or kappa > best:
+                best, i_best, alt_best = kappa, i, (toward if ok else q - t)
+        p[i_best] = alt_best
+    d = sum((v - q) ** 2 for v, q in zip(ys, p))
     return p, d
+
+
+def _decode_row_exact(y_row, L, strict: bool):
+    """Exact (rational) two-coset decode of one row: (p as floats, c)."""
+    pm0 = None if L is None else L / 2 - 1
+    pm1 = None if L is None else (L - 1) / 2
+    p0, d0 = _exact_candidate(y_row, 0, pm0, True)
+    p1, d1 = _exact_candidate(y_row, 1, pm1, strict)
+    if d1 < d0:
+        return np.array([float(v) for v in p1]), 1
+    return np.array([float(v) for v in p0]), 0
 
 
 def _choose(y, p0, d0, p1, d1):
@@ -121,12 +168,27 @@ def _choose(y, p0, d0, p1, d1):
     return p, pick1.astype(np.uint8)
 
 
+def _decode(y, L, strict: bool):
+    """Shared body of decode / decode_unconstrained (L None: no cube)."""
+    pm0 = None if L is None else L / 2 - 1
+    pm1 = None if L is None else (L - 1) / 2
+    p0, d0, f0 = _coset_candidate(y, 0, pm0, True)
+    p1, d1, f1 = _coset_candidate(y, 1, pm1, strict)
+    p, c = _choose(y, p0, d0, p1, d1)
+    for r in np.nonzero(f0 | f1)[0]:
+        p[r], c[r] = _decode_row_exact(y[r], L, strict)
+    return p, c
+
+
 def decode(y, L: int, strict: bool):
     """Exact nearest codeword of the cube codebook C(L) for each 8-group.
 
     Parameters
     ----------
-    y : array [N, 8], fp32 values (widened exactly to fp64 here)
+    y : array [N, 8] of fp64 (or narrower floats, widened exactly); the
+        decision is exact for the value held: fp64 comparisons, and exact
+        rational arithmetic wherever two compared costs lie within 1e-12
+        (parity step) or 1e-9 relative (coset choice) of each other
     L : levels, 2**bits (4 for 2-bit, 8 for 3-bit)
     strict : textbook E8 parity on the half-integer coset too
 
@@ -136,10 +198,8 @@ def decode(y, L: int, strict: bool):
     c : uint8 [N], 1 for the half-integer coset
     p : float64 [N, 8], the codeword
     """
-    y = np.asarray(y, dtype=np.float32).astype(np.float64).reshape(-1, 8)
-    p0, d0 = _coset_candidate(y, 0, L / 2 - 1, True)
-    p1, d1 = _coset_candidate(y, 1, (L - 1) / 2, strict)
-    p, c = _choose(y, p0, d0, p1, d1)
+    y = np.asarray(y).astype(np.float64).reshape(-1, 8)
+    p, c = _decode(y, L, strict)
     idx = p + (L / 2) - c[:, None] * 0.5
     assert np.all(idx == np.round(idx)) and idx.min() >= 0 and idx.max() <= L - 1
     return idx.astype(np.uint8), c, p
@@ -148,9 +208,7 @@ def decode(y, L: int, strict: bool):
 def decode_unconstrained(y, strict: bool):
     """Exact nearest point of the whole lattice (no cube limit).  fp64 input."""
     y = np.asarray(y, dtype=np.float64).reshape(-1, 8)
-    p0, d0 = _coset_candidate(y, 0, None, True)
-    p1, d1 = _coset_candidate(y, 1, None, strict)
-    p, _ = _choose(y, p0, d0, p1, d1)
+    p, _ = _decode(y, None, strict)
     return p
 
 

@@ -7,31 +7,33 @@ Sources
   zero-padded.  The README's "Supported models" names split-half RoPE
   (Llama / Mistral / Qwen / Phi), i.e. coordinate i pairs with i + d/2.
 * NexusQuant blog, post "The E8 lattice quantizes 8 numbers at once",
-  "Handling outliers": ``H = hadamard_matrix(128); rotated = vector @ H.T``,
-  orthogonal.  We take the Sylvester matrix H[j][k] = (-1)^popcount(j & k),
-  which is symmetric, so ``v @ H.T == H v``; the orthonormal rotation is
-  H / sqrt(n).
+  "Handling outliers": the head vector is multiplied by the transpose of a
+  128 x 128 Hadamard matrix, an orthogonal rotation.  We take the Sylvester
+  matrix H[j][k] = (-1)^popcount(j & k), which is symmetric, so the product
+  with its transpose is H v; the orthonormal rotation is H / sqrt(n).
 * RoPE frequencies omega_i = theta^(-2i/d), the form HF models use with
   ``rope_theta`` from the config (README "API reference", ``rope_base``).
-* Frequency scaling: README "API reference" takes the model config's
-  ``rope_scaling`` dict ("Pass model.config.rope_scaling for Llama-3.1 and
-  similar"); README "Limitations" names linear scaling and Llama-3.1 beyond
-  its original context.  The pages print no formula; we take the published
+* Frequency scaling: README "API reference" lets the caller hand over the
+  model config's ``rope_scaling`` dict, for Llama-3.1-style models; README
+  "Limitations" names linear scaling and Llama-3.1 beyond its original
+  context.  The pages print no formula; we take the published
   definitions of the two HF types that phrase points at: "linear" divides
   every frequency by the factor; "llama3" keeps the high-frequency band
   (wavelength below C / high_freq_factor), divides the low-frequency band
   (wavelength above C / low_freq_factor) by the factor and interpolates
   linearly in C / wavelength between them (C = original context length).
 
-fp32 functions (``rope_table_f32``, ``rope_inverse_f32``, ``fwht_f32``) define
-the value y on which the lattice decision is taken: every operation is one
-IEEE fp32 operation in a stated order (products and sums rounded separately,
-FWHT stages in the order h = 1, 2, 4, ..., n/2).  fp64 functions serve the
-floating-point outputs (dequantized vectors, scores).
+fp64 functions define every value the codec computes, the decision input y
+included.  The fp32 functions (``rope_table_f32``, ``rope_inverse_f32``,
+``fwht_f32``) are diagnostics: each operation is one IEEE fp32 operation in a
+stated order (products and sums rounded separately, FWHT stages in the order
+h = 1, 2, 4, ..., n/2), and tests use them to bound the error of an fp32
+computation against the fp64 one.
 
 Parity status: pinned (H H^T = nI, fast transform equals the dense product,
 norm preservation, inverse-after-forward RoPE is the identity, position 0 is
-the identity; scaling: factor 1 is the identity, linear scaling equals
+the identity, the rotation direction by a hand-computed value (e_0 at
+position 1 becomes cos(1) e_0 + sin(1) e_{d/2}); scaling: factor 1 is the identity, linear scaling equals
 unscaled RoPE at position p / factor, llama3 frequencies lie between w/f and
 w, fall monotonically, keep / divide the outer bands and are continuous at
 the band edges) -- see tests/test_oracle_transform.py.

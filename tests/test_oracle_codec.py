@@ -220,3 +220,97 @@ def test_compact_same_reconstruction_as_standard(bits, G, d):
     ra = oc.dequantize(a["codes"], a["cosets"], a["scales"], std)
     rb = oc.dequantize(b["codes"], b["cosets"], b["scales"], cmp_)
     assert np.array_equal(ra, rb)
+
+
+@pytest.mark.parametrize("n", [8, 64, 128, 256])
+def test_coset_plane_bit_position(n):
+    """Group m's coset bit is bit m of the vector's little-endian coset field
+    (byte m // 8, bit m % 8), checked one group at a time."""
+    groups = n // 8
+    nbytes = (groups + 7) // 8
+    for m in range(groups):
+        c = np.zeros((1, groups), np.uint8)
+        c[0, m] = 1
+        plane = oc.pack_cosets(c, nbytes)[0]
+        assert plane.shape == (nbytes,)
+        assert int.from_bytes(plane.tobytes(), "little") == 1 << m
+    # quantize puts the coset of the group at coordinates 8m .. 8m+7 there:
+    # x = H u / n (exact for these dyadic u) with a scale per 8-group; group m
+    # of u is (2, 1/2, ..., 1/2) -> y = u -> half coset (squared distance
+    # 1/4 against 11/4), every other group (2, 1/8, 0, ..., 0) -> integer
+    # coset (5/8 against 15/8)
+    cfg = oc.Codec(n, 2, 8)
+    H = transform.hadamard_dense(n)
+    for m in range(groups):
+        u = np.zeros(n)
+        u[0::8] = 2.0
+        u[1::8] = 0.125
+        u[8 * m + 1:8 * m + 8] = 0.5
+        x = (H @ u / n)[None]
+        q = oc.quantize(x, cfg)
+        assert list(np.nonzero(q["c"][0])[0]) == [m]
+        assert int.from_bytes(q["cosets"][0].tobytes(), "little") == 1 << m
+
+
+def _exact_y_fp16(x16, L, G):
+    """y of fp16 vectors without RoPE by exact integer arithmetic: u * 2^24 =
+    H (x * 2^24) in Python integers, y = (L/2) u / a as an exact fraction,
+    rounded once to fp64 by float()."""
+    from fractions import Fraction
+    n = x16.shape[-1]
+    H = transform.hadamard_dense(n).astype(np.int64)
+    xi = [int(v) for v in (x16.astype(np.float64) * 2.0 ** 24).astype(np.int64)]
+    u = [sum(int(H[j, k]) * xi[k] for k in range(n)) for j in range(n)]
+    out = []
+    for g in range(n // G):
+        grp = u[g * G:(g + 1) * G]
+        a = max(Fraction(max(abs(v) for v in grp)), Fraction(1e-8 * math.sqrt(n)) * 2 ** 24)
+        out += [float(Fraction(L, 2) * v / a) for v in grp]
+    return np.array(out)
+
+
+@pytest.mark.parametrize("n,bits,G", [(128, 2, 0), (64, 3, 32), (8, 2, 8)])
+def test_y_is_the_exact_value_rounded_once(n, bits, G):
+    """For fp16 inputs without RoPE the oracle's fp64 y equals the exact
+    rational (L/2) u / a rounded once (u = H x exact), element for element.
+    Pins the transform (a transposed or dropped term), the group maximum and
+    the scale step of compute_y."""
+    cfg = oc.Codec(n, bits, G)
+    rng = np.random.default_rng(n + bits)
+    x = rng.normal(size=(6, n)).astype(np.float16)
+    x[1] = 0
+    x[2, :] = 0
+    x[2, 3] = np.float16(6e-8)      # fp16 subnormal: below the 1e-8 floor
+    x[3] *= np.float16(1e-3)
+    y, a = oc.compute_y(x, cfg)
+    for r in range(x.shape[0]):
+        assert np.array_equal(y[r], _exact_y_fp16(x[r], cfg.L, cfg.G)), r
+    # the group maximum sits at +-L/2 exactly (nonzero groups)
+    yg = np.abs(y[[0, 3, 4, 5]]).reshape(4, -1, cfg.G).max(-1)
+    assert np.all(yg == cfg.L / 2)
+
+
+def test_rope_key_y_against_dense_fp64():
+    """Keys: y from an independent dense computation (rotation matrix of the
+    inverse RoPE, dense Sylvester matrix) agrees with compute_y to fp64
+    rounding."""
+    d, theta = 96, 1e4
+    cfg = oc.Codec(d, 2, 32, rope_theta=theta)
+    x = _x((1, 1, 20, d), 31).astype(np.float64)
+    pos = np.arange(20) + 1000
+    y, _ = oc.compute_y(x, cfg, positions=pos, is_key=True)
+    Hd = transform.hadamard_dense(128)
+    h = d // 2
+    for t in range(20):
+        R = np.zeros((d, d))
+        for i in range(h):
+            ang = pos[t] * theta ** (-2.0 * i / d)
+            c, s = math.cos(ang), math.sin(ang)
+            R[i, i], R[i, i + h] = c, s           # x'_i = x_i c + x_{i+h} s
+            R[i + h, i + h], R[i + h, i] = c, -s  # x'_{i+h} = x_{i+h} c - x_i s
+        v = np.zeros(128)
+        v[:d] = R @ x[0, 0, t]
+        u = Hd @ v
+        ref = np.concatenate([u[g * 32:(g + 1) * 32] * 2 / np.abs(u[g * 32:(g + 1) * 32]).max()
+                              for g in range(4)])
+        np.testing.assert_allclose(y[0, 0, t], ref, rtol=0, atol=1e-13)

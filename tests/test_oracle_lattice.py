@@ -176,3 +176,54 @@ def test_sign_symmetry_and_parity(strict, L):
         assert np.all(i1.astype(int).sum(-1) % 2 == 0)
     else:
         assert np.all(i1[c1 == 0].astype(int).sum(-1) % 2 == 0)
+
+
+def test_fp64_near_ties_round_the_right_way():
+    """Decisions are exact for fp64 inputs just below a rounding boundary,
+    where |y| + 1/2 would round up to the boundary in fp64."""
+    below = np.nextafter(0.5, 0.0)                  # 0.5 - 2^-54
+    for strict in (True, False):
+        y = np.array([[below, below, 0, 0, 0, 0, 0, 0]])
+        idx, c, p = lattice.decode(y, 4, strict)
+        assert c[0] == 0 and np.all(p == 0), p          # origin, not (1, 1, 0, ...)
+        assert np.all(lattice.decode_unconstrained(y, strict) == 0)
+        y = -y
+        _, _, p = lattice.decode(y, 4, strict)
+        assert np.all(p == 0)
+    # just below 3/2 on the integer coset rounds to 1, and just above 1/2
+    # rounds to 1
+    above = np.nextafter(0.5, 1.0)
+    y = np.array([[np.nextafter(1.5, 0.0), above, 0, 0, 0, 0, 0, 0]])
+    _, c, p = lattice.decode(y, 4, False)
+    assert c[0] == 0 and list(p[0]) == [1, 1, 0, 0, 0, 0, 0, 0]
+
+
+def test_tiny_half_coset_parity_step_is_exact():
+    """Strict half coset with an odd index sum: the step moves the coordinate
+    with the largest |delta| = 1/2 - |y|, i.e. the smallest |y|; in fp64 the
+    two |delta| below round to the same number, the exact path separates
+    them (coordinate 1 moves, not coordinate 0)."""
+    y = np.array([[1e-20, 1e-30, 1.5, 1.5, 1.5, 1.5, 1.5, 1.5]])
+    _, c, p = lattice.decode(y, 4, True)
+    cb = lattice.enumerate_cube_codebook(4, True)
+    from fractions import Fraction
+    dist = [sum((Fraction(float(a)) - Fraction(float(b))) ** 2 for a, b in zip(y[0], q))
+            for q in cb]
+    best = min(dist)
+    winners = [cb[i] for i, dd in enumerate(dist) if dd == best]
+    assert len(winners) == 1 and np.array_equal(p[0], winners[0]), (p, winners)
+
+
+@pytest.mark.parametrize("strict", [True, False])
+def test_cube_decoder_fp64_brute_force(strict):
+    """fp64 inputs (not fp32-representable) against brute force over the
+    whole 2-bit codebook."""
+    cb = lattice.enumerate_cube_codebook(4, strict)
+    rng = np.random.default_rng(14)
+    y = rng.uniform(-2.0, 2.0, size=(1000, 8))
+    y[::5] = np.round(y[::5] * 2) / 2 + rng.choice([-1, 1], size=(200, 8)) * 2.0 ** -50
+    y = np.clip(y, -2.0, 2.0)
+    idx, c, p = lattice.decode(y, 4, strict)
+    best, _ = lattice.brute_force_nearest(y, cb, chunk=16)
+    np.testing.assert_allclose(_norm2(y - p), best, rtol=0, atol=1e-12)
+    assert np.all(lattice.in_lattice(p, strict))

@@ -131,3 +131,52 @@ def test_llama3_scaling_continuous_at_band_edges():
     pos = np.arange(30) + 60000
     y = transform.rope_forward_f64(x, pos, 5e5, s)
     np.testing.assert_allclose(transform.rope_inverse_f64(y, pos, 5e5, s), x, atol=1e-12)
+
+
+@pytest.mark.parametrize("d,theta", [(128, 5e5), (96, 1e4), (8, 1e4)])
+def test_rope_direction_hand_value(d, theta):
+    """Split-half RoPE in the rotate-half convention rotates the pair
+    (x_i, x_{i+d/2}) by +p w_i: by hand, e_0 at position 1 (w_0 = 1) becomes
+    cos(1) e_0 + sin(1) e_{d/2}, and e_1 at position 2 becomes
+    cos(2 w_1) e_1 + sin(2 w_1) e_{1+d/2} with w_1 = theta^(-2/d).  Removal
+    turns e_0 at position 1 into cos(1) e_0 - sin(1) e_{d/2}.  A flipped sign
+    of sin anywhere fails these (round trips alone do not see it)."""
+    h = d // 2
+    e0 = np.zeros((1, 1, d))
+    e0[..., 0] = 1.0
+    want = np.zeros(d)
+    want[0], want[h] = math.cos(1.0), math.sin(1.0)
+    np.testing.assert_allclose(transform.rope_forward_f64(e0, [1], theta)[0, 0], want,
+                               rtol=0, atol=1e-15)
+    want_inv = want.copy()
+    want_inv[h] = -want[h]
+    np.testing.assert_allclose(transform.rope_inverse_f64(e0, [1], theta)[0, 0], want_inv,
+                               rtol=0, atol=1e-15)
+    e1 = np.zeros((1, 1, d))
+    e1[..., 1] = 1.0
+    w1 = theta ** (-2.0 / d)
+    want1 = np.zeros(d)
+    want1[1], want1[1 + h] = math.cos(2 * w1), math.sin(2 * w1)
+    np.testing.assert_allclose(transform.rope_forward_f64(e1, [2], theta)[0, 0], want1,
+                               rtol=0, atol=1e-15)
+    # the fp32 diagnostic removal turns the same way
+    c32, s32 = transform.rope_table_f32([1], theta, d)
+    got = transform.rope_inverse_f32(e0.astype(np.float32)[0], c32, s32)[0]
+    np.testing.assert_allclose(got, want_inv, rtol=0, atol=1e-7)
+
+
+def test_generator_rotates_forward():
+    """The seeded key generator applies RoPE in the forward direction (the
+    same hand value), so removing it with the codec's inverse undoes it."""
+    import torch
+
+    from e8_lattice_vector_amd import synth
+
+    d, h = 16, 8
+    x = torch.zeros((1, 3, d), dtype=torch.float64)
+    x[0, :, 0] = 1.0
+    y = synth._rotary(x, 1e4, positions=[0, 1, 2])[0].numpy()
+    for p in range(3):
+        want = np.zeros(d)
+        want[0], want[h] = math.cos(p), math.sin(p)
+        np.testing.assert_allclose(y[p], want, rtol=0, atol=1e-15)
