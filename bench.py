@@ -112,8 +112,8 @@ def qwen_decode_scores(steps, warmup, dev, stream):
     cfg = nq.Config(w.d, w.bits_k, w.bits_v, w.G,
                     nq.PARITY_STRICT if w.strict else nq.PARITY_RELAXED, nq.DTYPE_F16, w.theta)
     pk = nq.alloc_packed(cfg, False, w.S, w.H, w.T, dev)
-    ws = nq.alloc_workspace(cfg, w.T, dev)
     batch = 32
+    ws = nq.alloc_workspace(cfg, batch, w.H, w.T, dev)
     for s0 in range(0, w.S, batch):
         k = synth.kv("k", batch, w.H, w.T, w.d, w.theta, 0, dev, torch.float16, slab0=s0)
         sub = nq.Packed(pk.codes[s0:s0 + batch], pk.cosets[s0:s0 + batch],
@@ -169,7 +169,7 @@ def main():
     q = synth.queries(w.S, Hq, w.d, 0, dev)
     pk = nq.alloc_packed(cfg, False, w.S, w.H, w.T, dev)
     pv = nq.alloc_packed(cfg, True, w.S, w.H, w.T, dev)
-    ws = nq.alloc_workspace(cfg, w.T, dev)
+    ws = nq.alloc_workspace(cfg, w.S, w.H, w.T, dev)
     kd = torch.empty_like(k)
     vd = torch.empty_like(v)
     scores = torch.empty((w.S, Hq, w.T), dtype=torch.float32, device=dev)
@@ -181,7 +181,7 @@ def main():
         nq.quantize_kv(cfg, k, None, pk=pk, workspace=ws)
         if ev is not None:
             ev[1].record(stream)
-        nq.quantize_kv(cfg, None, v, pv=pv)
+        nq.quantize_kv(cfg, None, v, pv=pv, workspace=ws)
         if ev is not None:
             ev[2].record(stream)
         nq.dequantize_kv(cfg, pk, pv, w.S, w.H, w.T, k_out=kd, v_out=vd, workspace=ws)

@@ -35,7 +35,9 @@ class PackedKVCache:
         shape = (S, H, block, cfg.head_dim)
         self.rk = torch.empty(shape, dtype=cfg.torch_dtype, device=device)
         self.rv = torch.empty(shape, dtype=cfg.torch_dtype, device=device)
-        self.ws = nq.alloc_workspace(cfg, block, device)
+        # sized for the larger of a decode block and nothing else: a prefill
+        # allocates its own workspace
+        self.ws = nq.alloc_workspace(cfg, S, H, block, device)
         self.n_packed = 0   # tokens 0 .. n_packed - 1 are in the packed planes
         self.n_res = 0      # the next n_res tokens wait in the fp16 residual
 
@@ -62,11 +64,20 @@ class PackedKVCache:
         every full block of it is quantized into the planes."""
         t = k.shape[2]
         self._room(t)
+        # the residual copies run on the same stream as the quantization that
+        # reads them, so they are ordered before it
+        if stream is None:
+            ts = torch.cuda.current_stream()
+        elif isinstance(stream, torch.cuda.Stream):
+            ts = stream
+        else:   # a raw hipStream_t handle
+            ts = torch.cuda.ExternalStream(int(stream))
         i = 0
         while i < t:
             n = min(self.block - self.n_res, t - i)
-            self.rk[:, :, self.n_res:self.n_res + n].copy_(k[:, :, i:i + n])
-            self.rv[:, :, self.n_res:self.n_res + n].copy_(v[:, :, i:i + n])
+            with torch.cuda.stream(ts):
+                self.rk[:, :, self.n_res:self.n_res + n].copy_(k[:, :, i:i + n])
+                self.rv[:, :, self.n_res:self.n_res + n].copy_(v[:, :, i:i + n])
             self.n_res += n
             i += n
             if self.n_res == self.block:

@@ -43,6 +43,7 @@ int check_config(const nq_config* c) {
     return NQ_ERR_INVALID_ARG;
   if (c->packing == NQ_PACKING_COMPACT && c->parity != NQ_PARITY_STRICT)
     return NQ_ERR_INVALID_ARG;
+  if (c->exact != 0 && c->exact != 1) return NQ_ERR_INVALID_ARG;
   if (c->rope_scaling == NQ_ROPE_SCALING_LLAMA3) {
     if (!(c->rope_low_freq_factor > 0.0) || !isfinite(c->rope_high_freq_factor) ||
         !(c->rope_high_freq_factor > c->rope_low_freq_factor) || c->rope_original_max <= 0)
@@ -68,10 +69,45 @@ Layout layout(const nq_config* c, int is_value) {
   return l;
 }
 
+size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
+
+// Workspace of a call on S x H x T vectors, in this order (each part
+// 256-byte aligned): the fp32 RoPE table [T][d/2] (cos, sin) -- the only part
+// dequantize uses --, the same table in fp64, two queue counters (keys,
+// values) and the key and value queues of the fp64 pass.
+struct WsLayout {
+  size_t rope32, rope64, counters, queue_k, queue_v, total;
+  int64_t queue_cap;
+};
+
+int64_t queue_capacity(int64_t n_vec) {
+  // ~1e-3 of random vectors have a near-tie group; a queue of 1/32 of the
+  // vectors (at least 1024) leaves a wide margin, and a full queue makes the
+  // fp64 pass recompute every vector instead
+  int64_t cap = n_vec / 32;
+  if (cap < 1024) cap = 1024;
+  if (cap > n_vec) cap = n_vec;
+  return cap;
+}
+
+WsLayout ws_layout(const nq_config* c, int64_t S, int64_t H, int64_t T) {
+  WsLayout w;
+  const bool rope = c->rope_theta > 0.0;
+  const size_t th = (size_t)T * (size_t)(c->head_dim / 2);
+  w.rope32 = 0;
+  w.rope64 = round256(rope ? th * sizeof(float2) : 0);
+  w.counters = w.rope64 + round256(rope ? th * sizeof(double2) : 0);
+  w.queue_k = w.counters + 256;
+  w.queue_cap = queue_capacity(S * H * T);
+  const size_t qb = round256((size_t)w.queue_cap * sizeof(int64_t));
+  w.queue_v = w.queue_k + qb;
+  w.total = w.queue_v + qb;
+  return w;
+}
+
 size_t rope_bytes(const nq_config* c, int64_t T) {
   if (c->rope_theta <= 0.0) return 0;
-  const size_t b = (size_t)T * (size_t)(c->head_dim / 2) * sizeof(float2);
-  return (b + 255) & ~(size_t)255;
+  return round256((size_t)T * (size_t)(c->head_dim / 2) * sizeof(float2));
 }
 
 constexpr int64_t kMaxTokens = (int64_t)1 << 40;
@@ -144,6 +180,8 @@ nq::TensorArgs tensor_args(const nq_config* c, const Layout& l, int64_t S,
   a.half_L = (float)(l.L / 2);
   a.sigma_k = 1.0 / ((l.L / 2.0) * sqrt((double)l.n));
   a.inv_sqrt_n = (float)(1.0 / sqrt((double)l.n));
+  a.eps64 = 1e-8 * sqrt((double)l.n);
+  a.half_L64 = l.L / 2.0;
   return a;
 }
 
@@ -163,19 +201,19 @@ double rope_freq(const nq_config* c, int i) {
   return (1.0 - a) * w / c->rope_factor + a * w;
 }
 
-// Builds the cos/sin table in the workspace when keys need RoPE.
+// Builds the cos/sin table(s) in the workspace when keys need RoPE: fp32 at
+// the start of the workspace, and (table64 != null) the fp64 one; clears the
+// n_counters queue counters at `counters` in the same launch.
 int prepare_rope(const nq_config* c, int64_t T, const int32_t* positions, int64_t pos0,
-                 void* ws, size_t ws_bytes, hipStream_t s, const float2** out) {
+                 void* ws, double2* table64, unsigned long long* counters, int n_counters,
+                 hipStream_t s, const float2** out) {
   *out = nullptr;
-  const size_t need = rope_bytes(c, T);
-  if (need == 0) return NQ_OK;
-  if (ws == nullptr || ws_bytes < need) return NQ_ERR_WORKSPACE;
-  if (!aligned16(ws)) return NQ_ERR_INVALID_ARG;
   nq::RopeFreqs f;
   const int d = c->head_dim;
   for (int i = 0; i < d / 2; ++i) f.omega[i] = rope_freq(c, i);
   float2* table = static_cast<float2*>(ws);
-  if (nq::launch_rope_table(positions, pos0, T, d, f, table, s) != hipSuccess)
+  if (nq::launch_rope_table(positions, pos0, T, d, f, table, table64, counters, n_counters, s) !=
+      hipSuccess)
     return NQ_ERR_HIP;
   *out = table;
   return NQ_OK;
@@ -197,9 +235,10 @@ size_t nq_packed_bytes(const nq_config* cfg, int is_value, int64_t n_vectors,
   }
 }
 
-size_t nq_workspace_bytes(const nq_config* cfg, int64_t n_tokens) {
-  if (check_config(cfg) != NQ_OK || n_tokens < 0) return 0;
-  return rope_bytes(cfg, n_tokens);
+size_t nq_workspace_bytes(const nq_config* cfg, int64_t n_slabs, int32_t n_kv_heads,
+                          int64_t n_tokens) {
+  if (check_config(cfg) != NQ_OK || check_shape(n_slabs, n_kv_heads, n_tokens) != NQ_OK) return 0;
+  return ws_layout(cfg, n_slabs, n_kv_heads, n_tokens).total;
 }
 
 const char* nq_status_string(int status) {
@@ -226,20 +265,36 @@ int nq_quantize_kv(const nq_config* cfg, const void* k, const void* v,
   if (v != nullptr && (!aligned16(v) || (st = check_packed(pv, T, cfg)) != NQ_OK))
     return st != NQ_OK ? st : NQ_ERR_INVALID_ARG;
   if (positions != nullptr && !aligned16(positions)) return NQ_ERR_INVALID_ARG;
+  const WsLayout w = ws_layout(cfg, S, H, T);
+  if (ws == nullptr || ws_bytes < w.total) return NQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return NQ_ERR_INVALID_ARG;
+  char* wb = static_cast<char*>(ws);
+  auto* counters = reinterpret_cast<unsigned long long*>(wb + w.counters);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float2* rope = nullptr;
-  if (k != nullptr) {
-    if ((st = prepare_rope(cfg, T, positions, pk->token_offset, ws, ws_bytes, s, &rope)) != NQ_OK)
+  double2* rope64 = nullptr;
+  if (k != nullptr && cfg->rope_theta > 0.0) {
+    rope64 = reinterpret_cast<double2*>(wb + w.rope64);
+    if ((st = prepare_rope(cfg, T, positions, pk->token_offset, ws, rope64, counters, 2, s,
+                           &rope)) != NQ_OK)
       return st;
-    nq::TensorArgs a = tensor_args(cfg, layout(cfg, 0), S, H, T, pk);
-    a.x = k;
-    a.rope = rope;
-    if (nq::launch_quantize(a, cfg->in_dtype, s) != hipSuccess) return NQ_ERR_HIP;
+  } else if (nq::launch_clear_counters(counters, 2, s) != hipSuccess) {
+    return NQ_ERR_HIP;
   }
-  if (v != nullptr) {
-    nq::TensorArgs a = tensor_args(cfg, layout(cfg, 1), S, H, T, pv);
-    a.x = v;
-    if (nq::launch_quantize(a, cfg->in_dtype, s) != hipSuccess) return NQ_ERR_HIP;
+  // each tensor: the fp32 kernel (which queues near-tie vectors), then the
+  // fp64 pass over the queue; with cfg->exact every vector takes the fp64 pass
+  for (int is_v = 0; is_v < 2; ++is_v) {
+    const void* x = is_v ? v : k;
+    if (x == nullptr) continue;
+    nq::TensorArgs a = tensor_args(cfg, layout(cfg, is_v), S, H, T, is_v ? pv : pk);
+    a.x = x;
+    a.rope = is_v ? nullptr : rope;
+    a.rope64 = is_v ? nullptr : rope64;
+    a.queue_count = counters + is_v;
+    a.queue = reinterpret_cast<int64_t*>(wb + (is_v ? w.queue_v : w.queue_k));
+    a.queue_cap = w.queue_cap;
+    if (!cfg->exact && nq::launch_quantize(a, cfg->in_dtype, s) != hipSuccess) return NQ_ERR_HIP;
+    if (nq::launch_exact(a, cfg->in_dtype, cfg->exact, s) != hipSuccess) return NQ_ERR_HIP;
   }
   return NQ_OK;
 }
@@ -260,8 +315,13 @@ int nq_dequantize_kv(const nq_config* cfg, const nq_packed* pk,
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (k_out != nullptr) {
     const float2* rope = nullptr;
-    if ((st = prepare_rope(cfg, T, positions, pk->token_offset, ws, ws_bytes, s, &rope)) != NQ_OK)
-      return st;
+    if (rope_bytes(cfg, T) != 0) {
+      if (ws == nullptr || ws_bytes < rope_bytes(cfg, T)) return NQ_ERR_WORKSPACE;
+      if (!aligned16(ws)) return NQ_ERR_INVALID_ARG;
+      if ((st = prepare_rope(cfg, T, positions, pk->token_offset, ws, nullptr, nullptr, 0, s,
+                             &rope)) != NQ_OK)
+        return st;
+    }
     nq::TensorArgs a = tensor_args(cfg, layout(cfg, 0), S, H, T, pk);
     a.y = k_out;
     a.rope = rope;

@@ -25,6 +25,13 @@ struct TensorArgs {
   float half_L;         // L / 2
   double sigma_k;       // 1 / ((L/2) * sqrt(n)): stored scale = a * sigma_k
   float inv_sqrt_n;     // fp32(1 / sqrt(n))
+  // quantize only: the fp64 pass
+  const double2* rope64;           // [T][d/2] (cos, sin) in fp64, or nullptr
+  unsigned long long* queue_count; // vectors queued for the fp64 pass
+  int64_t* queue;                  // their indices (slab * H + head) * T + t
+  int64_t queue_cap;               // entries the queue holds
+  double eps64;                    // 1e-8 * sqrt(n)
+  double half_L64;                 // L / 2
 };
 
 struct ScoreArgs {
@@ -60,10 +67,16 @@ struct RopeFreqs {
   double omega[kMaxHalfDim];  // theta^(-2i/d), computed on the host
 };
 
-// positions[t], or pos0 + t when positions is null
+// cos / sin of positions[t] (or pos0 + t when positions is null) times
+// omega_i: `table` in fp32, `table64` (if not null) in fp64.  Also clears
+// the n_counters queue counters (if not null).
 hipError_t launch_rope_table(const int32_t* positions, int64_t pos0, int64_t T,
                              int d, const RopeFreqs& f, float2* table,
-                             hipStream_t stream);
+                             double2* table64, unsigned long long* counters,
+                             int n_counters, hipStream_t stream);
+hipError_t launch_clear_counters(unsigned long long* counters, int n, hipStream_t s);
+// The fp64 pass: the queued vectors (all = 0) or every vector (all = 1).
+hipError_t launch_exact(const TensorArgs& a, int in_dtype, int all, hipStream_t s);
 hipError_t launch_quantize(const TensorArgs& a, int in_dtype, hipStream_t s);
 hipError_t launch_dequantize(const TensorArgs& a, int out_dtype, hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, int in_dtype, hipStream_t s);

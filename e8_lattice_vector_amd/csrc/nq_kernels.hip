@@ -26,6 +26,7 @@
 #include <type_traits>
 
 #include "nq_internal.h"
+#include "nq_device.h"
 
 namespace nq {
 namespace {
@@ -39,27 +40,6 @@ __host__ __device__ constexpr int64_t max64(int64_t a, int64_t b) { return a > b
 
 typedef float nq_f2 __attribute__((ext_vector_type(2)));
 typedef float nq_f4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ float h2f(uint16_t h) {
-  return __half2float(__ushort_as_half(h));
-}
-__device__ __forceinline__ uint16_t f2h_rn(float f) {
-  return __half_as_ushort(__float2half_rn(f));
-}
-
-// fp64 -> fp16 with a single rounding to nearest-even: round to odd into
-// fp32 first (24 bits >= 11 + 2), then round to nearest-even into fp16.
-__device__ __forceinline__ uint16_t f64_to_f16_rn(double x) {
-  float f = (float)x;
-  const double back = (double)f;
-  if (back != x) {
-    uint32_t b = __float_as_uint(f);
-    if (fabs(back) > fabs(x)) b -= 1u;
-    b |= 1u;
-    f = __uint_as_float(b);
-  }
-  return f2h_rn(f);
-}
 
 template <typename T>
 struct Io;
@@ -229,79 +209,6 @@ __device__ __forceinline__ void rope_lane(float v[8], int m, int d,
   }
 }
 
-// Nearest codeword of the b-bit cube codebook for one 8-group.
-//
-// Works on g = 2y (exact) and a = |g|: with f = floor(a), the nearest even
-// integer to a is f + (f & 1) and the nearest odd one is f | 1 (ties away
-// from zero), clamped to the cube (L-2 resp. L-1 in these doubled units).
-// The parity step moves the coordinate with the largest "kappa" (|delta| if
-// the step toward y stays in the cube, -|delta| if it has to go away) by two;
-// its extra squared cost is 4 - 4 kappa.  The closer coset wins, the integer
-// coset on ties.  Output: b-bit codes idx = p + L/2 - c/2 packed little
-// endian, and the coset bit c.
-template <int BITS, bool STRICT>
-__device__ __forceinline__ void e8_decode(const float y[8], uint32_t& code,
-                                          int& coset) {
-  constexpr int L = 1 << BITS;
-  int P0[8], P1[8];
-  float d0[8], d1[8];
-  int neg[8];
-  float D0 = 0.f, D1 = 0.f;
-  int S0 = 0, S1 = 0, NS = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const float g = __fadd_rn(y[k], y[k]);
-    neg[k] = signbit(g) ? 1 : 0;
-    const float a = fabsf(g);
-    const int fi = (int)floorf(a);
-    P0[k] = min(fi + (fi & 1), L - 2);
-    P1[k] = min(fi | 1, L - 1);
-    d0[k] = __fsub_rn(a, (float)P0[k]);
-    d1[k] = __fsub_rn(a, (float)P1[k]);
-    D0 = __fmaf_rn(d0[k], d0[k], D0);
-    D1 = __fmaf_rn(d1[k], d1[k], D1);
-    S0 += P0[k];
-    S1 += P1[k];
-    NS += neg[k];
-  }
-  const int odd0 = (S0 >> 1) & 1;
-  const int odd1 = STRICT ? (((S1 + 2 * NS) >> 1) & 1) : 0;
-  float b0 = -INFINITY, b1 = -INFINITY;
-  int i0 = 0, i1 = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const bool ok0 = (d0[k] < 0.f) || (P0[k] <= L - 4);
-    const float k0 = ok0 ? fabsf(d0[k]) : -fabsf(d0[k]);
-    if (k0 > b0) { b0 = k0; i0 = k; }
-    if (STRICT) {
-      const bool ok1 = (d1[k] < 0.f) || (P1[k] <= L - 3);
-      const float k1 = ok1 ? fabsf(d1[k]) : -fabsf(d1[k]);
-      if (k1 > b1) { b1 = k1; i1 = k; }
-    }
-  }
-  if (odd0) D0 = __fadd_rn(D0, __fmaf_rn(-4.f, b0, 4.f));
-  if (STRICT && odd1) D1 = __fadd_rn(D1, __fmaf_rn(-4.f, b1, 4.f));
-  const int c = (D1 < D0) ? 1 : 0;
-  const int odd = c ? odd1 : odd0;
-  const int is = c ? i1 : i0;
-  uint32_t w = 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    int P = c ? P1[k] : P0[k];
-    if (odd && k == is) {
-      const float dd = c ? d1[k] : d0[k];
-      const bool ok = (dd < 0.f) || (P <= L - 4 + c);
-      const int t = (dd >= 0.f) ? 2 : -2;
-      P = ok ? P + t : P - t;
-    }
-    const int p2 = neg[k] ? -P : P;
-    const int idx = (p2 + L - c) >> 1;
-    w |= (uint32_t)idx << (BITS * k);
-  }
-  code = w;
-  coset = c;
-}
-
 // ---------------------------------------------------------------------------
 // Fast path for n <= 128 (one 16-lane DPP row or less per vector).
 //
@@ -429,15 +336,6 @@ __device__ __forceinline__ uint32_t row_or(uint32_t x) {
   return x;
 }
 
-// Spread the low 8 bits of x to the even bits of a 16-bit word.
-__device__ __forceinline__ uint32_t spread8(uint32_t x) {
-  x &= 0xffu;
-  x = (x | (x << 4)) & 0x0f0fu;
-  x = (x | (x << 2)) & 0x3333u;
-  x = (x | (x << 1)) & 0x5555u;
-  return x;
-}
-
 // fl(1/a): the hardware reciprocal estimate refined by one Newton step whose
 // residual 1 - a*r0 is formed by a fused multiply-add.  On gfx950 this equals
 // the correctly rounded quotient 1/a for every normal a below 2^126, i.e.
@@ -489,11 +387,6 @@ struct Compact {
   }
 };
 
-// (x << n) | (the top n bits of w): v_alignbit_b32
-__device__ __forceinline__ uint32_t shift_in(uint32_t x, float w, int n) {
-  return __builtin_amdgcn_alignbit(x, __float_as_uint(w), (uint32_t)(32 - n));
-}
-
 // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
 // that consecutive logical workgroups share an XCD and its L2.  The wave
 // order is then either tile-fastest (neighbouring waves stream neighbouring
@@ -509,67 +402,22 @@ __device__ __forceinline__ int64_t xcd_wave_id() {
   return (int64_t)lb * (kBlock / 64) + w;
 }
 
-// 2-bit decoder (L = 4) on g = 2y.  With a = |g| and t = a - 1:
-//  integer coset: p = 0 if a < 1 else sign(g) (bit B = a >= 1);
-//  half coset:    |p| = 1/2 if a < 2 else 3/2 (bit E = a >= 2), sign S;
-//  D1 - D0 = sum_k 2 min(|t_k|, 3 - a_k) - 8        (doubled units);
-//  integer-coset parity step: the coordinate with the smallest |t| toggles
-//  B, extra cost 4 |t|;  strict half-coset step: kappa = |t| (a < 2) or
-//  3 - a (a >= 2), extra cost 4 - 4 kappa, toggles E (a >= 1) or S (a < 1).
-// The two top bits of g's fp32 pattern are (S, E), so shifting them in for
-// k = 7 .. 0 builds the half-coset code word with (S_k, E_k) at bits
-// (2k+1, 2k); the sign bit of t gives not-B.  Scanning k downward also makes
-// the lowest index win ties.  Code word: 2-bit idx_k = p_k + 2 - c/2 at bits
-// [2k, 2k+2): integer coset bit0 = B, bit1 = ~(B & S); half coset
-// bit0 = E ^ S, bit1 = ~S.
-// `cosets` receives the wave-wide ballot of the coset bit (every lane of the
-// wave must be active).
-template <bool STRICT>
-__device__ __forceinline__ void e8_decode2(const float g[8], uint32_t& code,
-                                           uint64_t& cosets, int& coset) {
-  // With e = |t| - 1: min(|t|, 3 - a) = 1 - |e| and kappa = 1 - |e| exactly
-  // (|t| is a multiple of 2^-24 in [0, 3]), so D1 - D0 = 8 - 2 sum |e|, the
-  // strict step takes the smallest |e| (lowest index on ties) and costs
-  // 4 |e|.  |.| comes free as a source modifier.
-  uint32_t X = 0, Bn = 0, f0 = 1u << 14, f1 = 0;
-  float acc = 0.f, best0, best1 = INFINITY;
-#pragma unroll
-  for (int k = 7; k >= 0; --k) {
-    const float t = fabsf(g[k]) - 1.0f;
-    const float at = fabsf(t);
-    const float ae = fabsf(at - 1.0f);
-    X = shift_in(X, g[k], 2);
-    Bn = shift_in(Bn, t, 1);
-    acc = acc + ae;
-    if (k == 7) {
-      best0 = at;
-    } else if (at <= best0) {
-      best0 = at;
-      f0 = 1u << (2 * k);
-    }
-    if (STRICT) {
-      if (ae <= best1) { best1 = ae; f1 = 1u << (2 * k); }
-    }
+// Appends vector `vec` of every lane with `push` set to the call's queue of
+// vectors whose lattice decisions are re-taken in fp64 (one atomic add per
+// wave; entries past the queue's capacity are dropped, and the fp64 pass then
+// recomputes every vector).  All lanes of the wave must call this.
+__device__ __forceinline__ void queue_push(const TensorArgs& a, bool push, int64_t vec) {
+  const uint64_t b = __ballot(push);
+  if (b == 0) return;
+  const int lane = threadIdx.x & 63;
+  const int first = __builtin_ctzll(b);
+  unsigned long long base = 0;
+  if (lane == first) base = atomicAdd(a.queue_count, (unsigned long long)__popcll(b));
+  base = __shfl(base, first);
+  if (push) {
+    const unsigned long long r = base + (unsigned long long)__popcll(b & ((1ull << lane) - 1ull));
+    if (r < (unsigned long long)a.queue_cap) a.queue[r] = vec;
   }
-  const uint32_t odd0 = __builtin_popcount(Bn) & 1u;
-  float lhs = __fmaf_rn(-2.f, acc, 8.f);
-  uint32_t odd1 = 0;
-  if (STRICT) {
-    odd1 = __builtin_popcount(X) & 1u;
-    if (odd1) lhs = lhs + 4.f * best1;
-  }
-  const float rhs = odd0 ? 4.f * best0 : 0.f;
-  const int c = lhs < rhs ? 1 : 0;
-  cosets = __ballot(lhs < rhs);
-  coset = c;
-  // both code words, then a select (no divergent branch)
-  const uint32_t Bsp = spread8(~Bn);
-  const uint32_t b = Bsp ^ (odd0 ? f0 : 0u);
-  const uint32_t w0 = b | (~((b << 1) & X) & 0xaaaau);
-  uint32_t x = X;
-  if (STRICT) x ^= odd1 ? (f1 & Bsp) | ((f1 & ~Bsp) << 1) : 0u;
-  const uint32_t w1 = ((x ^ (x >> 1)) & 0x5555u) | (~x & 0xaaaau);
-  code = c ? w1 : w0;
 }
 
 // ROPE: 0 none, 1 partner through DPP (d == n >= 16), 2 partner through
@@ -711,11 +559,22 @@ __global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
 #pragma unroll
     for (int k = 0; k < 8; ++k) y[k] = __fmul_rn(v[k], rs);
     int c;
+    bool near;
     if (BITS == 2) {
-      e8_decode2<STRICT>(y, code, cball, c);
+      e8_decode2<STRICT>(y, code, cball, c, near);
     } else {
-      e8_decode<BITS, STRICT>(y, code, c);
+      float mgn;
+      e8_decode<BITS, STRICT, float>(y, code, c, &mgn);
+      near = mgn < kNearTie;
       cball = __ballot(c);
+    }
+    {
+      // a vector with any near-tie group goes to the fp64 pass
+      const uint64_t nb = __ballot(near);
+      if (nb != 0) {
+        const bool lead = l == 0 && tvalid && ((nb >> row_shift) & kRowMask) != 0;
+        queue_push(a, lead, (sh0 + it) * a.T + t);
+      }
     }
     if (STRICT && a.compact) code = Compact<BITS>::fold(code, c);
     const uint64_t cmask = coset_rows<VL>(cball);
@@ -867,6 +726,7 @@ __global__ __launch_bounds__(kBlock) void quantize_mfma_kernel(TensorArgs a, int
     asm("v_max_f32 %0, %1, %2" : "=v"(amax) : "s"(a.eps), "v"(mx));
     const float rs = __fmul_rn(rcp_rn(amax), kr);
     uint32_t cw = 0, words[2] = {0u, 0u};
+    bool near_any = false;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       float y[8];
@@ -875,10 +735,21 @@ __global__ __launch_bounds__(kBlock) void quantize_mfma_kernel(TensorArgs a, int
       uint32_t code;
       uint64_t cball;
       int c;
-      e8_decode2<STRICT>(y, code, cball, c);
+      bool near;
+      e8_decode2<STRICT>(y, code, cball, c, near);
+      near_any = near_any || near;
       if (STRICT && a.compact) code = Compact<2>::fold(code, c);
       cw |= (uint32_t)c << h;
       words[h >> 1] |= code << (16 * (h & 1));
+    }
+    {
+      // token v's groups sit in lanes v, v + 16, v + 32, v + 48
+      const uint64_t nb = __ballot(near_any);
+      if (nb != 0) {
+        const uint64_t f = nb | (nb >> 16) | (nb >> 32) | (nb >> 48);
+        const bool lead = p == 0 && tvalid && ((f >> v) & 1u) != 0;
+        queue_push(a, lead, (sh0 + it) * a.T + t);
+      }
     }
     if (tvalid) *reinterpret_cast<uint2*>(cb + oc) = make_uint2(words[0], words[1]);
     // coset word of the vector: bits 4p .. 4p+3 from lane p
@@ -935,8 +806,19 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(TensorArgs a) {
   for (int k = 0; k < 8; ++k) y[k] = __fmul_rn(v[k], r);
   uint32_t code;
   int c;
-  e8_decode<BITS, STRICT>(y, code, c);
+  float mgn;
+  e8_decode<BITS, STRICT, float>(y, code, c, &mgn);
   const uint64_t bal = __ballot(c);
+  {
+    const uint64_t nb = __ballot(mgn < kNearTie);
+    if (nb != 0) {
+      const int lane = threadIdx.x & 63;
+      const uint64_t rows = nb >> (lane - m);
+      const bool lead = m == 0 && live &&
+                        (rows & (VL >= 64 ? ~0ull : ((1ull << VL) - 1ull))) != 0;
+      queue_push(a, lead, vv);
+    }
+  }
   if (!live) return;
   if (STRICT && a.compact) code = Compact<BITS>::fold(code, c);
   uint8_t* cp = a.codes + pvec * a.code_bytes + m * BITS;
@@ -2529,103 +2411,6 @@ __global__ __launch_bounds__(1024) void attend_dma_kernel(AttendArgs a, int n_pa
   }
 }
 
-// Nearest point of the whole lattice, no cube limit (the textbook
-// Conway-Sloane decoder on D8 and on D8 + 1/2 (strict) or Z^8 + 1/2
-// (relaxed)), with the same tie rules as the cube decoder: rounding ties away
-// from zero, a parity step toward y (away from zero when y is on the point),
-// the lowest index among equal |delta|, the integer coset on equal distance.
-// Distances in fp64 (exact for fp32 y).  q = 2p.
-template <bool STRICT>
-__device__ void e8_nearest_free(const float y[8], int q[8], int& coset) {
-  int qc[2][8];
-  double dist[2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    float dl[8];
-    int s = 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const float a = fabsf(y[k]);
-      const float m = c == 0 ? floorf(a + 0.5f) : floorf(a) + 0.5f;
-      const float p = copysignf(m, y[k]);
-      dl[k] = y[k] - p;
-      qc[c][k] = (int)(2.f * p);
-      s += qc[c][k];
-    }
-    if ((c == 0 || STRICT) && ((s >> 1) & 1)) {   // sum p = s / 2 is odd
-      int is = 0;
-      float best = -1.f;
-#pragma unroll
-      for (int k = 0; k < 8; ++k)
-        if (fabsf(dl[k]) > best) { best = fabsf(dl[k]); is = k; }
-      int t = dl[is] > 0.f ? 1 : -1;
-      if (dl[is] == 0.f) t = signbit(y[is]) ? -1 : 1;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) if (k == is) qc[c][k] += 2 * t;
-    }
-    double d = 0.0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const double e = (double)y[k] - 0.5 * (double)qc[c][k];
-      d += e * e;
-    }
-    dist[c] = d;
-  }
-  coset = dist[1] < dist[0] ? 1 : 0;
-#pragma unroll
-  for (int k = 0; k < 8; ++k) q[k] = coset ? qc[1][k] : qc[0][k];
-}
-
-// Decoder alone.  constrained: the cube decoder the quantize kernels use (the
-// 2-bit one on g = 2y for b = 2); otherwise the unconstrained nearest point,
-// idx = p - c/2 + L/2 stored as a two's-complement int8.
-template <int BITS, bool STRICT>
-__global__ __launch_bounds__(kBlock) void decode_debug_kernel(
-    const float* y, int64_t n, int constrained, uint8_t* idx, uint8_t* coset) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n) return;
-  float v[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) v[k] = y[i * 8 + k];
-  int c;
-  if (!constrained) {
-    int q[8];
-    e8_nearest_free<STRICT>(v, q, c);
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      idx[i * 8 + k] = (uint8_t)(int8_t)((q[k] - c + (1 << BITS)) / 2);
-    coset[i] = (uint8_t)c;
-    return;
-  }
-  uint32_t code;
-  if (BITS == 2) {
-    float g[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) g[k] = v[k] + v[k];
-    uint64_t ball;
-    e8_decode2<STRICT>(g, code, ball, c);
-  } else {
-    e8_decode<BITS, STRICT>(v, code, c);
-  }
-#pragma unroll
-  for (int k = 0; k < 8; ++k)
-    idx[i * 8 + k] = (uint8_t)((code >> (BITS * k)) & ((1u << BITS) - 1u));
-  coset[i] = (uint8_t)c;
-}
-
-__global__ __launch_bounds__(kBlock) void rope_table_kernel(
-    const int32_t* pos, int64_t pos0, int64_t T, int h, RopeFreqs f, float2* table) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= T * h) return;
-  const int64_t t = i / h;
-  const int k = (int)(i % h);
-  const double p = pos ? (double)pos[t] : (double)(pos0 + t);
-  const double ang = p * f.omega[k];
-  double sn, cs;
-  sincos(ang, &sn, &cs);
-  table[i] = make_float2((float)cs, (float)sn);
-}
-
 // (slab, head) pairs per wave: about 8192 waves in all (32 per CU, the
 // resident limit at <= 64 VGPRs), so that on long caches each wave walks all
 // pairs of its token tile and reads its RoPE rows once.
@@ -3044,17 +2829,6 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
 namespace {
 }  // namespace
 
-hipError_t launch_rope_table(const int32_t* positions, int64_t pos0, int64_t T,
-                             int d, const RopeFreqs& f, float2* table,
-                             hipStream_t stream) {
-  const int h = d / 2;
-  const int64_t total = T * h;
-  const int64_t blocks = (total + kBlock - 1) / kBlock;
-  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(kBlock), 0,
-                     stream, positions, pos0, T, h, f, table);
-  return hipGetLastError();
-}
-
 hipError_t launch_quantize(const TensorArgs& a, int in_dtype, hipStream_t s) {
   return in_dtype == 0 ? quantize_t<__half>(a, s) : quantize_t<float>(a, s);
 }
@@ -3065,18 +2839,6 @@ hipError_t launch_dequantize(const TensorArgs& a, int out_dtype, hipStream_t s) 
 
 hipError_t launch_score(const ScoreArgs& a, int in_dtype, hipStream_t s) {
   return in_dtype == 0 ? score_t<__half>(a, s) : score_t<float>(a, s);
-}
-
-hipError_t launch_decode_debug(const float* y, int64_t n, int bits, int strict, int constrained,
-                               uint8_t* idx, uint8_t* coset, hipStream_t s) {
-  const int64_t blocks = (n + kBlock - 1) / kBlock;
-  const dim3 g((unsigned)blocks), b(kBlock);
-  if (bits == 2 && strict) hipLaunchKernelGGL((decode_debug_kernel<2, true>), g, b, 0, s, y, n, constrained, idx, coset);
-  else if (bits == 2) hipLaunchKernelGGL((decode_debug_kernel<2, false>), g, b, 0, s, y, n, constrained, idx, coset);
-  else if (bits == 3 && strict) hipLaunchKernelGGL((decode_debug_kernel<3, true>), g, b, 0, s, y, n, constrained, idx, coset);
-  else if (bits == 3) hipLaunchKernelGGL((decode_debug_kernel<3, false>), g, b, 0, s, y, n, constrained, idx, coset);
-  else return hipErrorInvalidValue;
-  return hipGetLastError();
 }
 
 }  // namespace nq

@@ -41,7 +41,8 @@ class _Config(ctypes.Structure):
                 ("rope_theta", ctypes.c_double),
                 ("rope_scaling", ctypes.c_int32), ("rope_original_max", ctypes.c_int32),
                 ("rope_factor", ctypes.c_double), ("rope_low_freq_factor", ctypes.c_double),
-                ("rope_high_freq_factor", ctypes.c_double), ("packing", ctypes.c_int32)]
+                ("rope_high_freq_factor", ctypes.c_double), ("packing", ctypes.c_int32),
+                ("exact", ctypes.c_int32)]
 
 
 class _Packed(ctypes.Structure):
@@ -72,7 +73,7 @@ def load(path: str = LIB_PATH):
     cfgp, pkp = ctypes.POINTER(_Config), ctypes.POINTER(_Packed)
     lib.nq_packed_bytes.argtypes = [cfgp, ctypes.c_int, i64, ctypes.c_int]
     lib.nq_packed_bytes.restype = sz
-    lib.nq_workspace_bytes.argtypes = [cfgp, i64]
+    lib.nq_workspace_bytes.argtypes = [cfgp, i64, i32, i64]
     lib.nq_workspace_bytes.restype = sz
     lib.nq_status_string.argtypes = [ctypes.c_int]
     lib.nq_status_string.restype = ctypes.c_char_p
@@ -110,13 +111,14 @@ class Config:
     rope_low_freq_factor: float = 1.0
     rope_high_freq_factor: float = 4.0
     packing: int = PACKING_STANDARD
+    exact: int = 0
 
     def c(self) -> _Config:
         return _Config(self.head_dim, self.bits_k, self.bits_v, self.scale_group,
                        self.parity, self.in_dtype, float(self.rope_theta),
                        self.rope_scaling, self.rope_original_max, float(self.rope_factor),
                        float(self.rope_low_freq_factor), float(self.rope_high_freq_factor),
-                       self.packing)
+                       self.packing, self.exact)
 
     @staticmethod
     def scaling_from_hf(rope_scaling) -> dict:
@@ -185,14 +187,51 @@ def _check(status: int, what: str):
         raise NQError(status, what)
 
 
+def _bad(what: str):
+    raise NQError(NQ_ERR_INVALID_ARG, what)
+
+
+def _check_tensor(t, dtype, shape, what: str):
+    """A caller-supplied device tensor must have this dtype and shape and be
+    contiguous (the library writes it as a dense row-major array)."""
+    if (t.dtype != dtype or not t.is_contiguous() or tuple(t.shape) != tuple(shape)
+            or t.device.type != "cuda"):
+        _bad(f"{what}: need a contiguous {dtype} device tensor of shape {tuple(shape)}, "
+             f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def _check_positions(positions, T: int, what: str):
+    if positions is not None and (positions.dtype != torch.int32 or positions.numel() != T
+                                  or not positions.is_contiguous()):
+        _bad(f"{what} positions: need {T} contiguous int32 values")
+
+
+def _check_packed(cfg: Config, p: Packed, is_value: bool, S: int, H: int, T: int,
+                  token_offset: int, what: str):
+    """Planes [S][H][capacity][bytes per vector] with the config's byte counts
+    and room for tokens [token_offset, token_offset + T)."""
+    if token_offset < 0 or p.codes.dim() != 4:
+        _bad(f"{what}: planes must be [S][H][capacity][bytes]")
+    cap = p.capacity
+    if cap < token_offset + T:
+        _bad(f"{what}: capacity {cap} < token window end {token_offset + T}")
+    nb = [packed_bytes(cfg, is_value, 1, pl) for pl in (PLANE_CODES, PLANE_COSETS, PLANE_SCALES)]
+    for t, dt, per, name in ((p.codes, torch.uint8, nb[0], "codes"),
+                             (p.cosets, torch.uint8, nb[1], "cosets"),
+                             (p.scales, torch.float16, nb[2] // 2, "scales")):
+        if t.dtype != dt or not t.is_contiguous() or tuple(t.shape) != (S, H, cap, per):
+            _bad(f"{what} {name}: need a contiguous {dt} tensor of shape {(S, H, cap, per)}, "
+                 f"got {t.dtype} {tuple(t.shape)}")
+
+
 def packed_bytes(cfg: Config, is_value: bool, n_vectors: int, plane: int) -> int:
     cc = cfg.c()
     return int(load().nq_packed_bytes(ctypes.byref(cc), int(is_value), int(n_vectors), plane))
 
 
-def workspace_bytes(cfg: Config, n_tokens: int) -> int:
+def workspace_bytes(cfg: Config, S: int, H: int, T: int) -> int:
     cc = cfg.c()
-    return int(load().nq_workspace_bytes(ctypes.byref(cc), int(n_tokens)))
+    return int(load().nq_workspace_bytes(ctypes.byref(cc), int(S), int(H), int(T)))
 
 
 def alloc_packed(cfg: Config, is_value: bool, S: int, H: int, T: int, device) -> Packed:
@@ -210,9 +249,12 @@ def alloc_packed(cfg: Config, is_value: bool, S: int, H: int, T: int, device) ->
                   scales.view(torch.float16).view(S, H, T, -1))
 
 
-def alloc_workspace(cfg: Config, T: int, device):
-    nb = workspace_bytes(cfg, T)
-    return None if nb == 0 else torch.empty(nb, dtype=torch.uint8, device=device)
+def alloc_workspace(cfg: Config, S: int, H: int, T: int, device):
+    """Workspace for quantize (and dequantize) calls on S x H x T vectors."""
+    nb = workspace_bytes(cfg, S, H, T)
+    if nb == 0:
+        raise NQError(NQ_ERR_INVALID_ARG, "workspace_bytes")
+    return torch.empty(nb, dtype=torch.uint8, device=device)
 
 
 def quantize_kv(cfg: Config, k, v, positions=None, pk: Packed | None = None,
@@ -231,10 +273,13 @@ def quantize_kv(cfg: Config, k, v, positions=None, pk: Packed | None = None,
         pk = alloc_packed(cfg, False, S, H, token_offset + T, k.device)
     if v is not None and pv is None:
         pv = alloc_packed(cfg, True, S, H, token_offset + T, v.device)
-    if workspace is None and k is not None:
-        workspace = alloc_workspace(cfg, T, ref.device)
-    if positions is not None and (positions.dtype != torch.int32 or positions.numel() != T):
-        raise NQError(NQ_ERR_INVALID_ARG, "quantize_kv positions")
+    if k is not None:
+        _check_packed(cfg, pk, False, S, H, T, token_offset, "quantize_kv pk")
+    if v is not None:
+        _check_packed(cfg, pv, True, S, H, T, token_offset, "quantize_kv pv")
+    if workspace is None:
+        workspace = alloc_workspace(cfg, S, H, T, ref.device)
+    _check_positions(positions, T, "quantize_kv")
     cc = cfg.c()
     ck = pk.c(token_offset) if k is not None else None
     cv = pv.c(token_offset) if v is not None else None
@@ -251,14 +296,23 @@ def dequantize_kv(cfg: Config, pk: Packed | None, pv: Packed | None, S: int, H: 
                   T: int, positions=None, k_out=None, v_out=None, workspace=None,
                   stream=None, token_offset: int = 0):
     """Dequantize tokens [token_offset, token_offset + T) -> [S][H][T][d]."""
+    if pk is None and pv is None:
+        _bad("dequantize_kv: neither pk nor pv")
     dev = (pk if pk is not None else pv).codes.device
     shape = (S, H, T, cfg.head_dim)
-    if pk is not None and k_out is None:
-        k_out = torch.empty(shape, dtype=cfg.torch_dtype, device=dev)
-    if pv is not None and v_out is None:
-        v_out = torch.empty(shape, dtype=cfg.torch_dtype, device=dev)
-    if workspace is None and pk is not None:
-        workspace = alloc_workspace(cfg, T, dev)
+    if pk is not None:
+        _check_packed(cfg, pk, False, S, H, T, token_offset, "dequantize_kv pk")
+        if k_out is None:
+            k_out = torch.empty(shape, dtype=cfg.torch_dtype, device=dev)
+        _check_tensor(k_out, cfg.torch_dtype, shape, "dequantize_kv k_out")
+    if pv is not None:
+        _check_packed(cfg, pv, True, S, H, T, token_offset, "dequantize_kv pv")
+        if v_out is None:
+            v_out = torch.empty(shape, dtype=cfg.torch_dtype, device=dev)
+        _check_tensor(v_out, cfg.torch_dtype, shape, "dequantize_kv v_out")
+    _check_positions(positions, T, "dequantize_kv")
+    if workspace is None and pk is not None and cfg.rope_theta > 0:
+        workspace = alloc_workspace(cfg, S, H, T, dev)
     cc = cfg.c()
     ck = pk.c(token_offset) if pk is not None else None
     cv = pv.c(token_offset) if pv is not None else None
@@ -278,8 +332,10 @@ def score_packed_keys(cfg: Config, pk: Packed, q, S: int, H: int, T: int,
     Hq = q.shape[1]
     if q.dtype != cfg.torch_dtype or not q.is_contiguous() or q.shape != (S, Hq, cfg.head_dim):
         raise NQError(NQ_ERR_INVALID_ARG, "score_packed_keys q")
+    _check_packed(cfg, pk, False, S, H, T, token_offset, "score_packed_keys pk")
     if scores is None:
         scores = torch.empty((S, Hq, T), dtype=torch.float32, device=q.device)
+    _check_tensor(scores, torch.float32, (S, Hq, T), "score_packed_keys scores")
     cc = cfg.c()
     ck = pk.c(token_offset)
     st = load().nq_score_packed_keys(ctypes.byref(cc), ctypes.byref(ck), S, H, Hq, T,
@@ -297,8 +353,10 @@ def attend_packed_values(cfg: Config, pv: Packed, weights, S: int, H: int, T: in
     if (weights.dtype != torch.float32 or not weights.is_contiguous()
             or tuple(weights.shape) != (S, Hq, T)):
         raise NQError(NQ_ERR_INVALID_ARG, "attend_packed_values weights")
+    _check_packed(cfg, pv, True, S, H, T, token_offset, "attend_packed_values pv")
     if out is None:
         out = torch.empty((S, Hq, cfg.head_dim), dtype=torch.float32, device=weights.device)
+    _check_tensor(out, torch.float32, (S, Hq, cfg.head_dim), "attend_packed_values out")
     cc = cfg.c()
     cv = pv.c(token_offset)
     st = load().nq_attend_packed_values(ctypes.byref(cc), ctypes.byref(cv), S, H, Hq, T,

@@ -99,6 +99,17 @@ enum { NQ_PLANE_CODES = 0, NQ_PLANE_COSETS = 1, NQ_PLANE_SCALES = 2 };
  *      parity of the low bits of idx_0..idx_6; that bit position stores the
  *      coset bit instead.  Exactly 8b bits per group; the coset plane has 0
  *      bytes and its pointer may be NULL.
+ *
+ * exact ([Walk] "The Conway-Sloane Nearest-Point Algorithm": the code of a
+ * group is the nearest lattice point of its scaled coordinates y; the pages
+ * fix no precision for y, read here as fp64 from the exact input values)
+ *  0  y and the decisions in fp32; every vector with a group whose decision
+ *     margin (squared-distance gap to the next best codeword) is below
+ *     1.6e-5 in units of y is recomputed in fp64 -- RoPE removal, transform,
+ *     group maximum, y = (L/2) u / a correctly rounded -- and decided there.
+ *     The result equals the fp64 definition except where fp64 itself cannot
+ *     separate two codewords.
+ *  1  every vector takes the fp64 path (a reference mode, many times slower).
  */
 typedef struct {
   int32_t head_dim;
@@ -114,6 +125,7 @@ typedef struct {
   double rope_low_freq_factor;   /* LLAMA3                                  */
   double rope_high_freq_factor;  /* LLAMA3                                  */
   int32_t packing;               /* NQ_PACKING_*                            */
+  int32_t exact;                 /* 0 or 1, see above                       */
 } nq_config;
 
 /* Packed form of one KV tensor: three device planes, each row-major over
@@ -150,10 +162,16 @@ typedef struct {
 size_t nq_packed_bytes(const nq_config* cfg, int is_value, int64_t n_vectors,
                        int plane);
 
-/* Host.  Workspace bytes that quantize / dequantize need for n_tokens tokens
- * (the per-call RoPE cos/sin table, T * d/2 * 8 bytes rounded up to 256; 0
- * when rope_theta == 0).  Scoring needs no workspace. */
-size_t nq_workspace_bytes(const nq_config* cfg, int64_t n_tokens);
+/* Host.  Workspace bytes that quantize needs for a call on n_slabs x
+ * n_kv_heads x n_tokens vectors; dequantize takes the same workspace (it uses
+ * its first part only).  In order, each part rounded up to 256 bytes: the
+ * RoPE cos/sin table in fp32 (T * d/2 * 8 bytes) and in fp64 (T * d/2 * 16
+ * bytes), both only when rope_theta > 0; 256 bytes of queue counters; two
+ * queues (keys, values) of the vectors that take the fp64 path, 8 bytes per
+ * entry, min(S*H*T, max(1024, S*H*T / 32)) entries each.  Returns 0 for an
+ * invalid config or shape.  Scoring and attention need no workspace. */
+size_t nq_workspace_bytes(const nq_config* cfg, int64_t n_slabs, int32_t n_kv_heads,
+                          int64_t n_tokens);
 
 /* Host.  Static text for a status code. */
 const char* nq_status_string(int status);
@@ -163,17 +181,21 @@ const char* nq_status_string(int status);
  * (rope_theta > 0), the vector is zero-padded to n and rotated by the
  * Walsh-Hadamard matrix, scaled per group of G, and each 8-group is replaced
  * by its nearest codeword of the lattice restricted to b-bit coordinates.
- * Arithmetic: fp32.  The transform runs as butterfly stages (each sum one
- * fp32 rounding, stages in the order h = 1, 2, ..., n/2); for fp16 vectors
- * without RoPE at d = n = 128, 2 bits, one scale per vector, as a +-1 matrix
- * product on the matrix cores (exact products, fp32 sums in the hardware's
- * order), whose y may differ from the stage-order one in its last bits.
+ * Arithmetic: fp32, with the fp64 pass of cfg->exact for near-ties, so that
+ * codes, coset bits and scales are those of the fp64 definition (y = (L/2)
+ * u / a, u = H pad(RoPE^-1(x)), a the group maximum of |u| floored at
+ * 1e-8 sqrt(n)), up to codeword pairs fp64 cannot separate.  The fp32
+ * transform runs as butterfly stages, or for fp16 vectors without RoPE at
+ * d = n = 128, 2 bits, one scale per vector, as a +-1 matrix product on the
+ * matrix cores (exact products, fp32 sums).
  *  k, v        device [S][H][T][d] inputs; either may be NULL (then the
  *              matching packed planes are not touched)
  *  positions   device int32 [T] token positions for RoPE, or NULL for
  *              token_offset + (0..T-1); values must be >= 0
  *  pk, pv      host structs holding device plane pointers (outputs)
- *  workspace   device scratch of nq_workspace_bytes(cfg, T) bytes
+ *  workspace   device scratch of nq_workspace_bytes(cfg, S, H, T) bytes; its
+ *              contents on entry do not matter, and calls that share one
+ *              workspace must not overlap in time
  * Errors: NQ_ERR_INVALID_ARG (sizes <= 0, null config, misalignment),
  * NQ_ERR_UNSUPPORTED (see nq_config), NQ_ERR_WORKSPACE, NQ_ERR_HIP. */
 int nq_quantize_kv(const nq_config* cfg, const void* k, const void* v,
@@ -191,6 +213,9 @@ int nq_quantize_kv(const nq_config* cfg, const void* k, const void* v,
  * s16 / sqrt(n) once; otherwise z = s16 / sqrt(n) * p goes through butterfly
  * stages.
  *  k_out, v_out  device [S][H][T][d] outputs (either may be NULL)
+ *  workspace     with keys and rope_theta > 0: at least the fp32 RoPE table
+ *                (T * d/2 * 8 bytes, e.g. a workspace of nq_workspace_bytes);
+ *                otherwise unused (may be NULL)
  * Errors as nq_quantize_kv. */
 int nq_dequantize_kv(const nq_config* cfg, const nq_packed* pk,
                      const nq_packed* pv, int64_t n_slabs, int32_t n_kv_heads,

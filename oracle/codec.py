@@ -39,8 +39,9 @@ every step in fp64 from the exact input values:
              z = u / sqrt(n))
       y_j  = (L/2) u_j / a_g                    -> max |y| = L/2 exactly
       sigma_g = a_g / ((L/2) sqrt(n)), stored as fp16 (RNE)
-  each 8-group of y -> lattice.decode (exact nearest codeword of the fp64 y)
-  -> idx in [0, L-1]^8, coset bit c
+  each 8-group of y -> lattice.decode (exact nearest codeword of the quotient
+  y, settled in exact arithmetic where fp64 cannot) -> idx in [0, L-1]^8,
+  coset bit c
   Dequantize: p = idx - L/2 + c/2;  z^ = s16 * p;  x^ = (H_n z^ / sqrt(n))[:d];
   keys then get RoPE back (the README's re-application after quantization).
   D0 denotes dequantization without the RoPE step (the codec frame).
@@ -123,16 +124,19 @@ def fp16_kv_bytes(layers: int, kv_heads: int, head_dim: int, tokens: int = 1):
     return 2 * layers * kv_heads * head_dim * tokens * 2
 
 
-def compute_y(x, codec: Codec, positions=None, is_key: bool = False):
-    """y [.., n] and group maxima a [.., n/G], both fp64: the decision input.
+def compute_y(x, codec: Codec, positions=None, is_key: bool = False, with_u: bool = False):
+    """y [.., n] and group maxima a [.., n/G], both fp64: the decision input
+    (with_u: also u [.., n]).
 
     Every step in fp64 from the exact input values (fp16 / fp32 widened
     exactly): split-half RoPE removal with cos / sin of the fp64 angles
     (keys, theta > 0), zero padding, u = H v (fast transform, each sum one
     fp64 rounding; exact for fp16 inputs without RoPE, whose partial sums
     fit in 53 bits), a = max(max |u|, 1e-8 sqrt(n)) per group (the page's
-    1e-8 floor in orthonormal units), and y = (L/2) u / a as one correctly
-    rounded division, so the group maximum maps to L/2 exactly.
+    1e-8 floor in orthonormal units).  The decision input is the quotient
+    y = (L/2) u / a of those fp64 numbers; the array returned holds it
+    rounded once to fp64 (the group maximum maps to L/2 exactly), and the
+    decoder settles close calls on the exact quotient.
     """
     x64 = np.asarray(x).astype(np.float64)
     d = codec.head_dim
@@ -149,6 +153,8 @@ def compute_y(x, codec: Codec, positions=None, is_key: bool = False):
     ug = u.reshape(u.shape[:-1] + (n // G, G))
     a = np.maximum(np.max(np.abs(ug), axis=-1), 1e-8 * math.sqrt(n))
     y = ((codec.L / 2) * ug / a[..., None]).reshape(u.shape)
+    if with_u:
+        return y, a, u
     return y, a
 
 
@@ -235,9 +241,13 @@ def unfold_cosets(idx_c):
 
 def quantize(x, codec: Codec, positions=None, is_key: bool = False):
     """Quantize vectors x [.., d] -> dict of planes plus the decision data."""
-    y, a = compute_y(x, codec, positions, is_key)
+    y, a, u = compute_y(x, codec, positions, is_key, with_u=True)
     lead = y.shape[:-1]
-    idx, c, _ = lattice.decode(y.reshape(-1, 8), codec.L, codec.strict)
+    # exact quotient of every coordinate: (L/2) u (exact: L/2 is a power of
+    # two) over its group's maximum
+    den = np.repeat(a, codec.G, axis=-1)
+    idx, c, _ = lattice.decode(y.reshape(-1, 8), codec.L, codec.strict,
+                               exact=((codec.L / 2) * u, den))
     ng = codec.n // 8
     stored = fold_cosets(idx, c) if codec.compact else idx
     idx = idx.reshape(lead + (codec.n,))

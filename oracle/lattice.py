@@ -119,11 +119,9 @@ def _coset_candidate(y: np.ndarray, c: int, pmax: float | None, parity: bool):
     return p, d, fragile
 
 
-def _exact_candidate(y_row, c: int, pmax, parity: bool):
+def _exact_candidate(ys, neg, c: int, pmax, parity: bool):
     """One coset's candidate for one row in exact rational arithmetic (the
-    same steps as _coset_candidate)."""
-    ys = [Fraction(float(v)) for v in y_row]
-    neg = [math.copysign(1.0, float(v)) < 0 for v in y_row]
+    same steps as _coset_candidate); ys exact values, neg their sign bits."""
     p = []
     for v, n in zip(ys, neg):
         a = abs(v)
@@ -147,40 +145,68 @@ def _exact_candidate(y_row, c: int, pmax, parity: bool):
     return p, d
 
 
-def _decode_row_exact(y_row, L, strict: bool):
+def _decode_row_exact(ys, neg, L, strict: bool):
     """Exact (rational) two-coset decode of one row: (p as floats, c)."""
     pm0 = None if L is None else L / 2 - 1
     pm1 = None if L is None else (L - 1) / 2
-    p0, d0 = _exact_candidate(y_row, 0, pm0, True)
-    p1, d1 = _exact_candidate(y_row, 1, pm1, strict)
+    p0, d0 = _exact_candidate(ys, neg, 0, pm0, True)
+    p1, d1 = _exact_candidate(ys, neg, 1, pm1, strict)
     if d1 < d0:
         return np.array([float(v) for v in p1]), 1
     return np.array([float(v) for v in p0]), 0
 
 
-def _choose(y, p0, d0, p1, d1):
-    """T4 coset choice with an exact check of near-ties."""
+def _choose(p0, d0, p1, d1):
+    """T4 coset choice in fp64; rows whose two distances lie within 1e-9
+    (relative) of each other are returned for an exact re-decision."""
     pick1 = d1 < d0
     near = np.abs(d1 - d0) <= 1e-9 * np.maximum(1.0, np.maximum(d0, d1))
-    for r in np.nonzero(near)[0]:
-        pick1[r] = _exact_sqdist(y[r], p1[r]) < _exact_sqdist(y[r], p0[r])
     p = np.where(pick1[:, None], p1, p0)
-    return p, pick1.astype(np.uint8)
+    return p, pick1.astype(np.uint8), near
 
 
-def _decode(y, L, strict: bool):
-    """Shared body of decode / decode_unconstrained (L None: no cube)."""
+def _near_boundary(y, L):
+    """Rows with a coordinate within 1e-12 of a rounding boundary of either
+    coset: a half-integer below L/2 - 1/2 for the integer coset, a nonzero
+    integer below L/2 for the half coset (past those the cube clamps the
+    rounding; at 0 the sign bit decides, and it is exact)."""
+    a = np.abs(y)
+    top0 = np.inf if L is None else L / 2 - 0.5
+    top1 = np.inf if L is None else L / 2
+    h = np.floor(a) + 0.5                      # nearest half-integer boundary below a + 1/2
+    h = np.where(a - (h - 1) < h - a, h - 1, h)
+    near0 = (np.abs(a - h) <= 1e-12) & (h < top0)
+    k = np.round(a)                            # nearest integer
+    near1 = (np.abs(a - k) <= 1e-12) & (k >= 1) & (k < top1)
+    return np.any(near0 | near1, axis=-1)
+
+
+def _decode(y, L, strict: bool, exact=None):
+    """Shared body of decode / decode_unconstrained (L None: no cube).
+
+    exact: None, or (num, den) arrays [N, 8] with y = num / den exactly; rows
+    where fp64 cannot settle a decision are then decided on num / den instead
+    of on the fp64 y."""
     pm0 = None if L is None else L / 2 - 1
     pm1 = None if L is None else (L - 1) / 2
     p0, d0, f0 = _coset_candidate(y, 0, pm0, True)
     p1, d1, f1 = _coset_candidate(y, 1, pm1, strict)
-    p, c = _choose(y, p0, d0, p1, d1)
-    for r in np.nonzero(f0 | f1)[0]:
-        p[r], c[r] = _decode_row_exact(y[r], L, strict)
+    p, c, near = _choose(p0, d0, p1, d1)
+    redo = f0 | f1 | near
+    if exact is not None:
+        redo |= _near_boundary(y, L)
+    for r in np.nonzero(redo)[0]:
+        if exact is None:
+            ys = [Fraction(float(v)) for v in y[r]]
+        else:
+            ys = [Fraction(float(nu)) / Fraction(float(de))
+                  for nu, de in zip(exact[0][r], exact[1][r])]
+        neg = [math.copysign(1.0, float(v)) < 0 for v in y[r]]
+        p[r], c[r] = _decode_row_exact(ys, neg, L, strict)
     return p, c
 
 
-def decode(y, L: int, strict: bool):
+def decode(y, L: int, strict: bool, exact=None):
     """Exact nearest codeword of the cube codebook C(L) for each 8-group.
 
     Parameters
@@ -191,6 +217,11 @@ def decode(y, L: int, strict: bool):
         (parity step) or 1e-9 relative (coset choice) of each other
     L : levels, 2**bits (4 for 2-bit, 8 for 3-bit)
     strict : textbook E8 parity on the half-integer coset too
+    exact : optional (num, den), arrays [N, 8] of fp64 with y = num / den
+        exactly (y itself then being that quotient rounded to fp64): rows
+        where a decision is not settled in fp64 -- the costs above, or a
+        coordinate within 1e-12 of a rounding boundary -- are decided on the
+        exact quotient
 
     Returns
     -------
@@ -199,7 +230,10 @@ def decode(y, L: int, strict: bool):
     p : float64 [N, 8], the codeword
     """
     y = np.asarray(y).astype(np.float64).reshape(-1, 8)
-    p, c = _decode(y, L, strict)
+    if exact is not None:
+        exact = (np.asarray(exact[0], np.float64).reshape(-1, 8),
+                 np.asarray(exact[1], np.float64).reshape(-1, 8))
+    p, c = _decode(y, L, strict, exact)
     idx = p + (L / 2) - c[:, None] * 0.5
     assert np.all(idx == np.round(idx)) and idx.min() >= 0 and idx.max() <= L - 1
     return idx.astype(np.uint8), c, p

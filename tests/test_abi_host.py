@@ -35,11 +35,28 @@ def test_plane_sizes_and_workspace():
     assert [nq.packed_bytes(c96, 0, 1, p) for p in range(3)] == [32, 2, 2]
     c8 = nq.Config(8, 2, 2, 8, nq.PARITY_STRICT, nq.DTYPE_F32, 0.0)
     assert [nq.packed_bytes(c8, 0, 64, p) for p in range(3)] == [128, 64, 128]
-    assert nq.workspace_bytes(c, 32768) == 32768 * 64 * 8
-    assert nq.workspace_bytes(c, 3) == 1536
-    assert nq.workspace_bytes(nq.Config(8, 2, 2, 8, 0, 0, 1e4), 3) == 256
-    assert nq.workspace_bytes(c8, 64) == 0
+    # fp32 and fp64 RoPE tables (keys with theta > 0), 256 bytes of counters,
+    # two queues of min(n, max(1024, n / 32)) 8-byte entries, each part
+    # rounded up to 256 bytes
+    def r(b):
+        return (b + 255) // 256 * 256
+
+    def ws(cfg, S, H, T, rope):
+        n = S * H * T
+        cap = min(n, max(1024, n // 32))
+        th = T * cfg.head_dim // 2
+        return (r(th * 8) + r(th * 16) if rope else 0) + 256 + 2 * r(cap * 8)
+
+    assert nq.workspace_bytes(c, 1, 1, 32768) == ws(c, 1, 1, 32768, True) == \
+        32768 * 64 * 24 + 256 + 2 * 8192
+    assert nq.workspace_bytes(c, 32, 8, 32768) == 32768 * 64 * 24 + 256 + 2 * (1 << 21)
+    assert nq.workspace_bytes(c, 1, 1, 3) == 1536 + 3072 + 256 + 512
+    c8r = nq.Config(8, 2, 2, 8, 0, 0, 1e4)
+    assert nq.workspace_bytes(c8r, 1, 1, 3) == ws(c8r, 1, 1, 3, True) == 1280
+    assert nq.workspace_bytes(c8, 1, 1, 64) == ws(c8, 1, 1, 64, False) == 1280
+    assert nq.workspace_bytes(c, 0, 1, 3) == 0 and nq.workspace_bytes(c, 1, 1, 0) == 0
     assert nq.packed_bytes(c, 0, 1, 7) == 0
+    assert nq.packed_bytes(nq.Config(exact=2), 0, 1, 0) == 0      # exact must be 0 or 1
 
 
 @pytest.mark.parametrize("kw", [dict(head_dim=7), dict(head_dim=264), dict(bits_k=4),
@@ -75,6 +92,14 @@ def test_invalid_arguments_rejected_before_launch():
     # keys with RoPE need the workspace table
     assert q(ctypes.byref(c), 0x10000, None, 1, 1, 4, None, ctypes.byref(pk), None, None, 0, None) == -3
     assert q(ctypes.byref(c), 0x10000, None, 1, 1, 4, None, ctypes.byref(pk), None, 0x8000, 128, None) == -3
+    # values need the workspace too (the queue of the fp64 pass); a misaligned
+    # workspace is rejected
+    nb = nq.workspace_bytes(nq.Config(128, 2, 2, 0, 1, 0, 5e5), 1, 1, 4)
+    assert q(ctypes.byref(c), None, 0x10000, 1, 1, 4, None, None, ctypes.byref(pk), None, 0, None) == -3
+    assert q(ctypes.byref(c), None, 0x10000, 1, 1, 4, None, None, ctypes.byref(pk), 0x8000, nb - 1,
+             None) == -3
+    assert q(ctypes.byref(c), None, 0x10000, 1, 1, 4, None, None, ctypes.byref(pk), 0x8008, nb,
+             None) == -1
     dq = lib.nq_dequantize_kv
     assert dq(ctypes.byref(c), ctypes.byref(pk), None, 1, 1, 4, None, None, None, None, 0, None) == -1
     assert dq(ctypes.byref(c), ctypes.byref(pk), None, 1, 1, 4, None, 0x10000, None, None, 0, None) == -3

@@ -1,0 +1,97 @@
+"""Exemption accounting over whole caches: every group of the Llama-3.1-8B
+32K cache (K and V, 2^28 groups), the Mistral-7B cache (K3 / V2, G = 64) and
+the Phi-3-mini cache (strict, d = 96 padded to 128), quantized in the launch
+configuration bench.py times, compared with the oracle (fp64 y, exact
+nearest codeword) over the host's cores.  Exempt groups (a different codeword
+within 1e-6 of the oracle's distance) must number at most 1e-6 of the
+cache's groups; no group may have a larger regret."""
+
+import math
+import multiprocessing as mp
+import os
+import uuid
+from multiprocessing import shared_memory
+
+import numpy as np
+import pytest
+import torch
+
+from e8_lattice_vector_amd import nq, synth, workloads
+
+import fullcache
+from parity import oracle_codec
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DEV = "cuda"
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def _to_shm(t, keep):
+    a = t.cpu().numpy()
+    shm = shared_memory.SharedMemory(create=True, size=max(a.nbytes, 1),
+                                     name=f"nqx_{uuid.uuid4().hex[:12]}")
+    keep.append(shm)
+    np.ndarray(a.shape, a.dtype, buffer=shm.buf)[...] = a
+    return (shm.name, a.shape, a.dtype.str)
+
+
+def _queued(ws, cfg, T):
+    """Vectors the two quantize passes queued for the fp64 pass (the
+    counters that follow the RoPE tables in the workspace)."""
+    off = 0
+    if cfg.rope_theta > 0:
+        th = T * cfg.head_dim // 2
+        off = (th * 8 + 255) // 256 * 256 + (th * 16 + 255) // 256 * 256
+    return ws[off:off + 16].view(torch.int64).cpu().tolist()
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("wname,heads_per_job", [("llama-3.1-8b-32k", 2), ("mistral-7b", 8),
+                                                 ("phi-3-mini", 8)])
+def test_whole_cache_exemptions(wname, heads_per_job):
+    w = workloads.ALL[wname]
+    cfg = nq.Config(w.d, w.bits_k, w.bits_v, w.G,
+                    nq.PARITY_STRICT if w.strict else nq.PARITY_RELAXED, nq.DTYPE_F16, w.theta)
+    log(f"[whole] {wname}: S={w.S} H={w.H} T={w.T} d={w.d}")
+    k, v = synth.workload_inputs(w, seed=0, device=DEV)
+    ws = nq.alloc_workspace(cfg, w.S, w.H, w.T, DEV)
+    pk, pv = nq.quantize_kv(cfg, k, v, workspace=ws)
+    torch.cuda.synchronize()
+    queued = _queued(ws, cfg, w.T)
+    n_vec = w.S * w.H * w.T
+    log(f"[whole] {wname}: quantized; fp64 pass took K {queued[0]} / V {queued[1]} of "
+        f"{n_vec} vectors")
+    nproc = max(1, min(16, os.cpu_count() or 1))
+    for is_v, x, p in ((False, k, pk), (True, v, pv)):
+        keep = []
+        try:
+            specs = {"x": _to_shm(x, keep), "codes": _to_shm(p.codes, keep),
+                     "cosets": _to_shm(p.cosets, keep), "scales": _to_shm(p.scales, keep)}
+            codec = oracle_codec(cfg, is_v)
+            kw = dict(head_dim=codec.head_dim, bits=codec.bits, scale_group=codec.scale_group,
+                      strict=codec.strict, rope_theta=codec.rope_theta, compact=codec.compact)
+            jobs = [(specs, kw, not is_v, s, h0, min(w.H, h0 + heads_per_job))
+                    for s in range(w.S) for h0 in range(0, w.H, heads_per_job)]
+            with mp.get_context("spawn").Pool(nproc) as pool:
+                res = pool.map(fullcache.check_chunk, jobs, chunksize=1)
+        finally:
+            for shm in keep:
+                shm.close()
+                shm.unlink()
+        tot = {key: sum(r[key] for r in res) for key in res[0] if key != "max_regret"}
+        tot["max_regret"] = max(r["max_regret"] for r in res)
+        label = f"{wname}/{'V' if is_v else 'K'}"
+        log(f"[whole] {label}: {tot['exempt']} exempt of {tot['groups']} groups "
+            f"(budget {math.floor(1e-6 * tot['groups'])}), max regret {tot['max_regret']:.3e}, "
+            f"scale steps {tot['scale_steps']} ({nproc} processes)")
+        assert tot["groups"] == n_vec * (cfg.n // 8)
+        assert tot["invalid"] == 0 and tot["bad_regret"] == 0, tot
+        assert tot["scale_bad"] == 0, tot
+        assert tot["exempt"] <= math.floor(1e-6 * tot["groups"]), tot
+    del k, v, pk, pv, ws
+    torch.cuda.empty_cache()

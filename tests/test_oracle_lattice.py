@@ -227,3 +227,50 @@ def test_cube_decoder_fp64_brute_force(strict):
     best, _ = lattice.brute_force_nearest(y, cb, chunk=16)
     np.testing.assert_allclose(_norm2(y - p), best, rtol=0, atol=1e-12)
     assert np.all(lattice.in_lattice(p, strict))
+
+
+def _exact_min_codewords(yq, cb):
+    """All codewords at the exact minimum squared distance from the rational
+    vector yq (fp64 prefilter, then exact arithmetic on the close ones)."""
+    from fractions import Fraction
+    yf = np.array([float(v) for v in yq])
+    d = ((cb - yf) ** 2).sum(-1)
+    cand = cb[d <= d.min() + 1e-9]
+    ex = [sum((v - Fraction(float(q))) ** 2 for v, q in zip(yq, row)) for row in cand]
+    m = min(ex)
+    return [cand[i] for i, e in enumerate(ex) if e == m], m
+
+
+@pytest.mark.parametrize("strict", [True, False])
+def test_decisions_on_the_exact_quotient(strict):
+    """y = (L/2) u / a is decided as the exact quotient: on small-integer u
+    with non-power-of-two a (exact ties are common there), rows whose fp64
+    rounding of y would tip a tie come out as an exact nearest codeword of
+    the quotient, and on exact distance ties the integer coset (tie rule T4);
+    checked against exact brute force over the 2-bit codebook."""
+    from fractions import Fraction
+    rng = np.random.default_rng(21 + strict)
+    u = rng.integers(-6, 7, size=(20000, 8)).astype(np.float64)
+    a = np.abs(u).max(-1, keepdims=True)
+    a[a == 0] = 1.0
+    u[:, 0] = np.where(rng.random(20000) < 0.5, a[:, 0], -a[:, 0])
+    num, den = 2.0 * u, np.repeat(a, 8, axis=1)
+    y = num / den
+    _, c1, p1 = lattice.decode(y, 4, strict)
+    _, c2, p2 = lattice.decode(y, 4, strict, exact=(num, den))
+    rows = np.nonzero(np.any(p1 != p2, axis=1))[0]
+    assert len(rows) > 0
+    cb = lattice.enumerate_cube_codebook(4, strict)
+    for r in rows[:25]:
+        yq = [Fraction(int(nu)) / Fraction(int(de)) for nu, de in zip(num[r], den[r])]
+        winners, m = _exact_min_codewords(yq, cb)
+        assert any(np.array_equal(p2[r], w) for w in winners), (y[r], p2[r], winners)
+        d1 = sum((v - Fraction(float(q))) ** 2 for v, q in zip(yq, p1[r]))
+        assert d1 >= m
+        if d1 == m and c1[r] != c2[r]:      # a coset tie the fp64 rounding tipped: T4
+            assert c2[r] == 0
+        elif d1 == m:                         # a parity-step tie: T3, the lower index moves
+            i = int(np.nonzero(p1[r] != p2[r])[0][0])
+            yi = yq[i]
+            rnd = lattice._round_to_coset(np.array([float(yi)]), int(c2[r]))[0]
+            assert p2[r][i] != rnd and p1[r][i] == rnd
