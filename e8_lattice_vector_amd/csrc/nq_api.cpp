@@ -73,10 +73,10 @@ size_t round256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 // Workspace of a call on S x H x T vectors, in this order (each part
 // 256-byte aligned): the fp32 RoPE table [T][d/2] (cos, sin) -- the only part
-// dequantize uses --, the same table in fp64, two queue counters (keys,
-// values) and the key and value queues of the fp64 pass.
+// dequantize uses --, the fp64 RoPE frequencies [d/2], two queue counters
+// (keys, values) and the key and value queues of the fp64 pass.
 struct WsLayout {
-  size_t rope32, rope64, counters, queue_k, queue_v, total;
+  size_t rope32, omega, counters, queue_k, queue_v, total;
   int64_t queue_cap;
 };
 
@@ -95,8 +95,8 @@ WsLayout ws_layout(const nq_config* c, int64_t S, int64_t H, int64_t T) {
   const bool rope = c->rope_theta > 0.0;
   const size_t th = (size_t)T * (size_t)(c->head_dim / 2);
   w.rope32 = 0;
-  w.rope64 = round256(rope ? th * sizeof(float2) : 0);
-  w.counters = w.rope64 + round256(rope ? th * sizeof(double2) : 0);
+  w.omega = round256(rope ? th * sizeof(float2) : 0);
+  w.counters = w.omega + round256(rope ? (size_t)(c->head_dim / 2) * sizeof(double) : 0);
   w.queue_k = w.counters + 256;
   w.queue_cap = queue_capacity(S * H * T);
   const size_t qb = round256((size_t)w.queue_cap * sizeof(int64_t));
@@ -201,18 +201,18 @@ double rope_freq(const nq_config* c, int i) {
   return (1.0 - a) * w / c->rope_factor + a * w;
 }
 
-// Builds the cos/sin table(s) in the workspace when keys need RoPE: fp32 at
-// the start of the workspace, and (table64 != null) the fp64 one; clears the
-// n_counters queue counters at `counters` in the same launch.
+// Builds the fp32 cos/sin table at the start of the workspace when keys need
+// RoPE; in the same launch copies the fp64 frequencies to `omega` and clears
+// the n_counters queue counters at `counters` (each when not null).
 int prepare_rope(const nq_config* c, int64_t T, const int32_t* positions, int64_t pos0,
-                 void* ws, double2* table64, unsigned long long* counters, int n_counters,
+                 void* ws, double* omega, unsigned long long* counters, int n_counters,
                  hipStream_t s, const float2** out) {
   *out = nullptr;
   nq::RopeFreqs f;
   const int d = c->head_dim;
   for (int i = 0; i < d / 2; ++i) f.omega[i] = rope_freq(c, i);
   float2* table = static_cast<float2*>(ws);
-  if (nq::launch_rope_table(positions, pos0, T, d, f, table, table64, counters, n_counters, s) !=
+  if (nq::launch_rope_table(positions, pos0, T, d, f, table, omega, counters, n_counters, s) !=
       hipSuccess)
     return NQ_ERR_HIP;
   *out = table;
@@ -272,10 +272,10 @@ int nq_quantize_kv(const nq_config* cfg, const void* k, const void* v,
   auto* counters = reinterpret_cast<unsigned long long*>(wb + w.counters);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const float2* rope = nullptr;
-  double2* rope64 = nullptr;
+  double* omega = nullptr;
   if (k != nullptr && cfg->rope_theta > 0.0) {
-    rope64 = reinterpret_cast<double2*>(wb + w.rope64);
-    if ((st = prepare_rope(cfg, T, positions, pk->token_offset, ws, rope64, counters, 2, s,
+    omega = reinterpret_cast<double*>(wb + w.omega);
+    if ((st = prepare_rope(cfg, T, positions, pk->token_offset, ws, omega, counters, 2, s,
                            &rope)) != NQ_OK)
       return st;
   } else if (nq::launch_clear_counters(counters, 2, s) != hipSuccess) {
@@ -289,7 +289,9 @@ int nq_quantize_kv(const nq_config* cfg, const void* k, const void* v,
     nq::TensorArgs a = tensor_args(cfg, layout(cfg, is_v), S, H, T, is_v ? pv : pk);
     a.x = x;
     a.rope = is_v ? nullptr : rope;
-    a.rope64 = is_v ? nullptr : rope64;
+    a.omega = is_v ? nullptr : omega;
+    a.positions = positions;
+    a.pos0 = (is_v ? pv : pk)->token_offset;
     a.queue_count = counters + is_v;
     a.queue = reinterpret_cast<int64_t*>(wb + (is_v ? w.queue_v : w.queue_k));
     a.queue_cap = w.queue_cap;

@@ -3,8 +3,8 @@
 // The quantize kernels compute y in fp32 and take each lattice decision in
 // fp32.  Every vector with a group whose decision margin falls below
 // kNearTie is appended to a queue; exact_kernel then recomputes those
-// vectors from their input in fp64 -- RoPE removal with the fp64 cos / sin
-// table, Walsh-Hadamard stages h = 1, 2, ..., n/2, the group maximum, y =
+// vectors from their input in fp64 -- RoPE removal with fp64 cos / sin,
+// Walsh-Hadamard stages h = 1, 2, ..., n/2, the group maximum, y =
 // (L/2) u / a as one correctly rounded division -- decodes them with the same
 // two-coset decoder in fp64 and overwrites their codes, coset bits and
 // scales.  For fp16 inputs without RoPE, u is exact and the decision is
@@ -134,9 +134,10 @@ __global__ __launch_bounds__(kExBlock) void exact_kernel(TensorArgs a, int all) 
     double v[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) v[k] = j0 < a.d ? load_in(x, vec * a.d + j0 + k) : 0.0;
-    if (a.rope64 != nullptr) {
+    if (a.omega != nullptr) {
       // x'_i = x_i c + x_{i+h} s, x'_{i+h} = x_{i+h} c - x_i s: two rounded
-      // products and a rounded sum each
+      // products and a rounded sum each; c, s from the same fp64 angle and
+      // sincos as the fp32 table of the fp32 kernels
       double xp[8];
       if (a.d == 8) {
 #pragma unroll
@@ -149,13 +150,16 @@ __global__ __launch_bounds__(kExBlock) void exact_kernel(TensorArgs a, int all) 
         for (int k = 0; k < 8; ++k) xp[k] = __shfl(v[k], src);
       }
       if (j0 < a.d) {
+        const double pos =
+            a.positions != nullptr ? (double)a.positions[t] : (double)(a.pos0 + t);
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const int j = j0 + k;
           const bool up = j >= h;
-          const double2 cs = a.rope64[t * h + (up ? j - h : j)];
-          const double p1 = __dmul_rn(v[k], cs.x);
-          const double p2 = __dmul_rn(xp[k], cs.y);
+          double sn, cs;
+          sincos(pos * a.omega[up ? j - h : j], &sn, &cs);
+          const double p1 = __dmul_rn(v[k], cs);
+          const double p2 = __dmul_rn(xp[k], sn);
           v[k] = up ? __dsub_rn(p1, p2) : __dadd_rn(p1, p2);
         }
       }
@@ -189,7 +193,7 @@ __global__ __launch_bounds__(kExBlock) void exact_kernel(TensorArgs a, int all) 
     const double am = fmax(mx, a.eps64);
     uint32_t code;
     int c;
-    if (std::is_same<InT, __half>::value && a.rope64 == nullptr && mx > a.eps64) {
+    if (std::is_same<InT, __half>::value && a.omega == nullptr && mx > a.eps64) {
       // fp16 inputs without RoPE: u and a are exact multiples of 2^-24
       // below 2^23, so g = 2y = L u / a is decided on exact integers
       int64_t num[8];
@@ -269,9 +273,10 @@ hipError_t exact_t(const TensorArgs& a, int all, hipStream_t s) {
 
 __global__ __launch_bounds__(kExBlock) void rope_table_kernel(
     const int32_t* pos, int64_t pos0, int64_t T, int h, RopeFreqs f, float2* table,
-    double2* table64, unsigned long long* counters, int n_counters) {
+    double* omega, unsigned long long* counters, int n_counters) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (counters != nullptr && i < n_counters) counters[i] = 0ull;
+  if (omega != nullptr && i < h) omega[i] = f.omega[i];
   if (i >= T * h) return;
   const int64_t t = i / h;
   const int k = (int)(i % h);
@@ -280,7 +285,6 @@ __global__ __launch_bounds__(kExBlock) void rope_table_kernel(
   double sn, cs;
   sincos(ang, &sn, &cs);
   table[i] = make_float2((float)cs, (float)sn);
-  if (table64 != nullptr) table64[i] = make_double2(cs, sn);
 }
 
 __global__ void clear_counters_kernel(unsigned long long* counters, int n) {
@@ -393,7 +397,7 @@ hipError_t launch_exact(const TensorArgs& a, int in_dtype, int all, hipStream_t 
 }
 
 hipError_t launch_rope_table(const int32_t* positions, int64_t pos0, int64_t T, int d,
-                             const RopeFreqs& f, float2* table, double2* table64,
+                             const RopeFreqs& f, float2* table, double* omega,
                              unsigned long long* counters, int n_counters,
                              hipStream_t stream) {
   const int h = d / 2;
@@ -401,7 +405,7 @@ hipError_t launch_rope_table(const int32_t* positions, int64_t pos0, int64_t T, 
   if (total < n_counters) total = n_counters;
   const int64_t blocks = (total + kExBlock - 1) / kExBlock;
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(kExBlock), 0, stream,
-                     positions, pos0, T, h, f, table, table64, counters, n_counters);
+                     positions, pos0, T, h, f, table, omega, counters, n_counters);
   return hipGetLastError();
 }
 

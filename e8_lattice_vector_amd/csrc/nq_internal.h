@@ -26,7 +26,9 @@ struct TensorArgs {
   double sigma_k;       // 1 / ((L/2) * sqrt(n)): stored scale = a * sigma_k
   float inv_sqrt_n;     // fp32(1 / sqrt(n))
   // quantize only: the fp64 pass
-  const double2* rope64;           // [T][d/2] (cos, sin) in fp64, or nullptr
+  const double* omega;             // RoPE frequencies [d/2] in fp64, or nullptr
+  const int32_t* positions;        // RoPE positions [T], or nullptr: pos0 + t
+  int64_t pos0;
   unsigned long long* queue_count; // vectors queued for the fp64 pass
   int64_t* queue;                  // their indices (slab * H + head) * T + t
   int64_t queue_cap;               // entries the queue holds
@@ -68,11 +70,11 @@ struct RopeFreqs {
 };
 
 // cos / sin of positions[t] (or pos0 + t when positions is null) times
-// omega_i: `table` in fp32, `table64` (if not null) in fp64.  Also clears
-// the n_counters queue counters (if not null).
+// omega_i, rounded once to fp32, into `table`.  Also copies the frequencies
+// to `omega` and clears the n_counters queue counters (each if not null).
 hipError_t launch_rope_table(const int32_t* positions, int64_t pos0, int64_t T,
                              int d, const RopeFreqs& f, float2* table,
-                             double2* table64, unsigned long long* counters,
+                             double* omega, unsigned long long* counters,
                              int n_counters, hipStream_t stream);
 hipError_t launch_clear_counters(unsigned long long* counters, int n, hipStream_t s);
 // The fp64 pass: the queued vectors (all = 0) or every vector (all = 1).

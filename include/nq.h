@@ -165,8 +165,9 @@ size_t nq_packed_bytes(const nq_config* cfg, int is_value, int64_t n_vectors,
 /* Host.  Workspace bytes that quantize needs for a call on n_slabs x
  * n_kv_heads x n_tokens vectors; dequantize takes the same workspace (it uses
  * its first part only).  In order, each part rounded up to 256 bytes: the
- * RoPE cos/sin table in fp32 (T * d/2 * 8 bytes) and in fp64 (T * d/2 * 16
- * bytes), both only when rope_theta > 0; 256 bytes of queue counters; two
+ * RoPE cos/sin table in fp32 (T * d/2 * 8 bytes) and the fp64 frequencies
+ * (d/2 * 8 bytes), both only when rope_theta > 0; 256 bytes of queue
+ * counters; two
  * queues (keys, values) of the vectors that take the fp64 path, 8 bytes per
  * entry, min(S*H*T, max(1024, S*H*T / 32)) entries each.  Returns 0 for an
  * invalid config or shape.  Scoring and attention need no workspace. */

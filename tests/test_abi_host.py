@@ -45,12 +45,12 @@ def test_plane_sizes_and_workspace():
         n = S * H * T
         cap = min(n, max(1024, n // 32))
         th = T * cfg.head_dim // 2
-        return (r(th * 8) + r(th * 16) if rope else 0) + 256 + 2 * r(cap * 8)
+        return (r(th * 8) + r(cfg.head_dim // 2 * 8) if rope else 0) + 256 + 2 * r(cap * 8)
 
     assert nq.workspace_bytes(c, 1, 1, 32768) == ws(c, 1, 1, 32768, True) == \
-        32768 * 64 * 24 + 256 + 2 * 8192
-    assert nq.workspace_bytes(c, 32, 8, 32768) == 32768 * 64 * 24 + 256 + 2 * (1 << 21)
-    assert nq.workspace_bytes(c, 1, 1, 3) == 1536 + 3072 + 256 + 512
+        32768 * 64 * 8 + 512 + 256 + 2 * 8192
+    assert nq.workspace_bytes(c, 32, 8, 32768) == 32768 * 64 * 8 + 512 + 256 + 2 * (1 << 21)
+    assert nq.workspace_bytes(c, 1, 1, 3) == 1536 + 512 + 256 + 512
     c8r = nq.Config(8, 2, 2, 8, 0, 0, 1e4)
     assert nq.workspace_bytes(c8r, 1, 1, 3) == ws(c8r, 1, 1, 3, True) == 1280
     assert nq.workspace_bytes(c8, 1, 1, 64) == ws(c8, 1, 1, 64, False) == 1280

@@ -46,7 +46,7 @@ def _queued(ws, cfg, T):
     off = 0
     if cfg.rope_theta > 0:
         th = T * cfg.head_dim // 2
-        off = (th * 8 + 255) // 256 * 256 + (th * 16 + 255) // 256 * 256
+        off = (th * 8 + 255) // 256 * 256 + (cfg.head_dim // 2 * 8 + 255) // 256 * 256
     return ws[off:off + 16].view(torch.int64).cpu().tolist()
 
 

@@ -233,7 +233,17 @@ def test_unconstrained_decoder(parity):
     rng = np.random.default_rng(30 + parity)
     y = rng.uniform(-3, 3, size=(100000, 8))
     y[:20000] = np.round(y[:20000] * 2) / 2                               # exact ties
-    y = np.concatenate([mins, -mins, y]).astype(np.float32)
+    # just below a rounding boundary in fp32: 0.5 - 2^-25 (where fl(a + 0.5)
+    # would round up to 1) and 1.5 - 2^-23, either sign, at every position
+    below = [float(np.nextafter(np.float32(0.5), np.float32(0))),
+             float(np.nextafter(np.float32(1.5), np.float32(0)))]
+    assert below == [0.5 - 2.0 ** -25, 1.5 - 2.0 ** -23]
+    edge = np.zeros((32, 8))
+    for r in range(32):
+        v = below[r % 2]
+        edge[r, (r // 2) % 8] = v * (1 if (r // 16) == 0 else -1)
+        edge[r, (r // 2 + 3) % 8] = 0.25
+    y = np.concatenate([mins, -mins, edge, y]).astype(np.float32)
     log(f"[decoder-free] parity={parity} groups={len(y)}")
     idx, c = nq.e8_decode_debug(torch.from_numpy(y).to(DEV), 2, parity, constrained=False)
     torch.cuda.synchronize()
