@@ -50,7 +50,7 @@ def spilling_kernels(remarks: str):
 
 def build(verbose: bool = False) -> str:
     hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    srcs = [os.path.join(CSRC, f) for f in ("nq_api.cpp", "nq_kernels.hip", "nq_exact.hip")]
+    srcs = [os.path.join(CSRC, f) for f in ("nq_api.cpp", "nq_kernels.hip", "nq_exact.hip", "nq_noalloc.hip")]
     tmp = LIB + ".tmp"
     cmd = [hipcc] + HIPCC_FLAGS + ["-o", tmp] + srcs
     if verbose:

@@ -221,41 +221,12 @@ int prepare_rope(const nq_config* c, int64_t T, const int32_t* positions, int64_
 
 }  // namespace
 
-extern "C" {
+namespace nq {
 
-size_t nq_packed_bytes(const nq_config* cfg, int is_value, int64_t n_vectors,
-                       int plane) {
-  if (check_config(cfg) != NQ_OK || n_vectors < 0) return 0;
-  const Layout l = layout(cfg, is_value);
-  switch (plane) {
-    case NQ_PLANE_CODES: return (size_t)n_vectors * l.code_bytes;
-    case NQ_PLANE_COSETS: return (size_t)n_vectors * l.coset_bytes;
-    case NQ_PLANE_SCALES: return (size_t)n_vectors * l.n_scales * 2;
-    default: return 0;
-  }
-}
-
-size_t nq_workspace_bytes(const nq_config* cfg, int64_t n_slabs, int32_t n_kv_heads,
-                          int64_t n_tokens) {
-  if (check_config(cfg) != NQ_OK || check_shape(n_slabs, n_kv_heads, n_tokens) != NQ_OK) return 0;
-  return ws_layout(cfg, n_slabs, n_kv_heads, n_tokens).total;
-}
-
-const char* nq_status_string(int status) {
-  switch (status) {
-    case NQ_OK: return "ok";
-    case NQ_ERR_INVALID_ARG: return "invalid argument";
-    case NQ_ERR_UNSUPPORTED: return "unsupported configuration";
-    case NQ_ERR_WORKSPACE: return "workspace missing or too small";
-    case NQ_ERR_HIP: return "HIP launch failed";
-    default: return "unknown status";
-  }
-}
-
-int nq_quantize_kv(const nq_config* cfg, const void* k, const void* v,
-                   int64_t S, int32_t H, int64_t T, const int32_t* positions,
-                   const nq_packed* pk, const nq_packed* pv, void* ws,
-                   size_t ws_bytes, void* stream) {
+// nq_quantize_kv with the workspace supplied by the entry point.
+int quantize_impl(const nq_config* cfg, const void* k, const void* v, int64_t S, int32_t H,
+                  int64_t T, const int32_t* positions, const nq_packed* pk, const nq_packed* pv,
+                  void* ws, size_t ws_bytes, void* stream) {
   int st = check_config(cfg);
   if (st != NQ_OK) return st;
   if ((st = check_shape(S, H, T)) != NQ_OK) return st;
@@ -299,6 +270,46 @@ int nq_quantize_kv(const nq_config* cfg, const void* k, const void* v,
     if (nq::launch_exact(a, cfg->in_dtype, cfg->exact, s) != hipSuccess) return NQ_ERR_HIP;
   }
   return NQ_OK;
+}
+
+}  // namespace nq
+
+extern "C" {
+
+size_t nq_packed_bytes(const nq_config* cfg, int is_value, int64_t n_vectors,
+                       int plane) {
+  if (check_config(cfg) != NQ_OK || n_vectors < 0) return 0;
+  const Layout l = layout(cfg, is_value);
+  switch (plane) {
+    case NQ_PLANE_CODES: return (size_t)n_vectors * l.code_bytes;
+    case NQ_PLANE_COSETS: return (size_t)n_vectors * l.coset_bytes;
+    case NQ_PLANE_SCALES: return (size_t)n_vectors * l.n_scales * 2;
+    default: return 0;
+  }
+}
+
+size_t nq_workspace_bytes(const nq_config* cfg, int64_t n_slabs, int32_t n_kv_heads,
+                          int64_t n_tokens) {
+  if (check_config(cfg) != NQ_OK || check_shape(n_slabs, n_kv_heads, n_tokens) != NQ_OK) return 0;
+  return ws_layout(cfg, n_slabs, n_kv_heads, n_tokens).total;
+}
+
+const char* nq_status_string(int status) {
+  switch (status) {
+    case NQ_OK: return "ok";
+    case NQ_ERR_INVALID_ARG: return "invalid argument";
+    case NQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case NQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case NQ_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int nq_quantize_kv(const nq_config* cfg, const void* k, const void* v,
+                   int64_t S, int32_t H, int64_t T, const int32_t* positions,
+                   const nq_packed* pk, const nq_packed* pv, void* ws,
+                   size_t ws_bytes, void* stream) {
+  return nq::quantize_impl(cfg, k, v, S, H, T, positions, pk, pv, ws, ws_bytes, stream);
 }
 
 int nq_dequantize_kv(const nq_config* cfg, const nq_packed* pk,

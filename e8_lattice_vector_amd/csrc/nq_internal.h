@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/nq.h"
+
 namespace nq {
 
 // One KV tensor pass (quantize or dequantize).
@@ -80,6 +82,10 @@ hipError_t launch_clear_counters(unsigned long long* counters, int n, hipStream_
 // The fp64 pass: the queued vectors (all = 0) or every vector (all = 1).
 hipError_t launch_exact(const TensorArgs& a, int in_dtype, int all, hipStream_t s);
 hipError_t launch_quantize(const TensorArgs& a, int in_dtype, hipStream_t s);
+// The body of nq_quantize_kv (argument checks, launches) on a given workspace.
+int quantize_impl(const nq_config* cfg, const void* k, const void* v, int64_t S, int32_t H,
+                  int64_t T, const int32_t* positions, const nq_packed* pk, const nq_packed* pv,
+                  void* ws, size_t ws_bytes, void* stream);
 hipError_t launch_dequantize(const TensorArgs& a, int out_dtype, hipStream_t s);
 hipError_t launch_score(const ScoreArgs& a, int in_dtype, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);

@@ -31,7 +31,7 @@ PACKING_STANDARD, PACKING_COMPACT = 0, 1
 
 EXPORTED = ("nq_packed_bytes", "nq_workspace_bytes", "nq_status_string",
             "nq_quantize_kv", "nq_dequantize_kv", "nq_score_packed_keys",
-            "nq_attend_packed_values", "nq_e8_decode_debug")
+            "nq_attend_packed_values", "nq_e8_decode_debug", "nq_quantize_kv_noalloc")
 
 
 class _Config(ctypes.Structure):
@@ -79,6 +79,8 @@ def load(path: str = LIB_PATH):
     lib.nq_status_string.restype = ctypes.c_char_p
     lib.nq_quantize_kv.argtypes = [cfgp, vp, vp, i64, i32, i64, vp, pkp, pkp, vp, sz, vp]
     lib.nq_quantize_kv.restype = ctypes.c_int
+    lib.nq_quantize_kv_noalloc.argtypes = [cfgp, vp, vp, i64, i32, i64, vp, pkp, pkp, vp]
+    lib.nq_quantize_kv_noalloc.restype = ctypes.c_int
     lib.nq_dequantize_kv.argtypes = [cfgp, pkp, pkp, i64, i32, i64, vp, vp, vp, vp, sz, vp]
     lib.nq_dequantize_kv.restype = ctypes.c_int
     lib.nq_score_packed_keys.argtypes = [cfgp, pkp, i64, i32, i32, i64, vp, vp, vp, sz, vp]
@@ -289,6 +291,34 @@ def quantize_kv(cfg: Config, k, v, positions=None, pk: Packed | None = None,
         ctypes.byref(cv) if cv is not None else None,
         _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream(stream))
     _check(st, "nq_quantize_kv")
+    return pk, pv
+
+
+def quantize_kv_noalloc(cfg: Config, k, v, pk: Packed | None, pv: Packed | None,
+                        positions=None, stream=None, token_offset: int = 0):
+    """quantize_kv through nq_quantize_kv_noalloc: the library's own static
+    workspace; the caller supplies the packed planes (nothing is allocated)."""
+    ref = k if k is not None else v
+    S, H, T, d = ref.shape
+    if d != cfg.head_dim:
+        _bad("quantize_kv_noalloc head_dim")
+    for t, p, is_v in ((k, pk, False), (v, pv, True)):
+        if t is None:
+            continue
+        if t.dtype != cfg.torch_dtype or not t.is_contiguous() or tuple(t.shape) != (S, H, T, d):
+            _bad("quantize_kv_noalloc tensor")
+        if p is None:
+            _bad("quantize_kv_noalloc needs the packed planes")
+        _check_packed(cfg, p, is_v, S, H, T, token_offset, "quantize_kv_noalloc")
+    _check_positions(positions, T, "quantize_kv_noalloc")
+    cc = cfg.c()
+    ck = pk.c(token_offset) if k is not None else None
+    cv = pv.c(token_offset) if v is not None else None
+    st = load().nq_quantize_kv_noalloc(
+        ctypes.byref(cc), _ptr(k), _ptr(v), S, H, T, _ptr(positions),
+        ctypes.byref(ck) if ck is not None else None,
+        ctypes.byref(cv) if cv is not None else None, _stream(stream))
+    _check(st, "nq_quantize_kv_noalloc")
     return pk, pv
 
 

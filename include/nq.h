@@ -205,6 +205,24 @@ int nq_quantize_kv(const nq_config* cfg, const void* k, const void* v,
                    const nq_packed* pv, void* workspace, size_t ws_bytes,
                    void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * operation, arguments and results as nq_quantize_kv, with no workspace
+ * argument.  Its workspace is a library-owned device array of 32 MiB per
+ * GPU (allocated when the library's code is loaded on that GPU and held until
+ * the process ends), so calls that need more -- nq_workspace_bytes(cfg, S, H,
+ * T) > 32 MiB, e.g. more than about 55K tokens at d = 128 with RoPE --
+ * return NQ_ERR_WORKSPACE before anything is enqueued.  It calls no
+ * allocating routine.  Every call on one GPU shares that array: calls whose
+ * work overlaps in time on one GPU (other streams, other host threads) race
+ * and give undefined results; calls in one stream are ordered and safe.
+ * The array's contents between calls do not matter (each call clears what it
+ * counts). */
+int nq_quantize_kv_noalloc(const nq_config* cfg, const void* k, const void* v,
+                           int64_t n_slabs, int32_t n_kv_heads, int64_t n_tokens,
+                           const int32_t* positions, const nq_packed* pk,
+                           const nq_packed* pv, void* stream);
+
 /* Inverse path ([Walk] "What Makes This Hard in Practice", item 3: unpack on
  * the device; [RM] "How it works": RoPE re-applied after quantization):
  * p = idx - L/2 + c/2, z = s16 * p, x = (H z / sqrt(n))[:d], keys get RoPE

@@ -203,3 +203,22 @@ def test_build_spill_check_parses_remarks():
            "x.hip:9:1: remark: Function Name: _Z2k2v [-Rpass-analysis=kernel-resource-usage]\n"
            "x.hip:9:1: remark:     ScratchSize [bytes/lane]: 12 [-Rpass-analysis=kernel-resource-usage]\n")
     assert build.spilling_kernels(txt) == [("_Z2k2v", 12)]
+
+
+def test_no_alloc_checks_before_launch():
+    """nq_quantize_kv_noalloc refuses, on the host and before anything is
+    enqueued, calls whose workspace exceeds its 32 MiB array, and reports
+    config errors like nq_quantize_kv (no GPU needed)."""
+    lib = nq.load()
+    c = nq.Config(128, 2, 2, 0, nq.PARITY_RELAXED, nq.DTYPE_F16, 5e5)
+    cc = c.c()
+    pk = nq._Packed(0x1000, 0x2000, 0x3000)
+    f = lib.nq_quantize_kv_noalloc
+    assert nq.workspace_bytes(c, 1, 1, 131072) > 32 << 20
+    assert f(ctypes.byref(cc), 0x10000, None, 1, 1, 131072, None, ctypes.byref(pk), None,
+             None) == nq.NQ_ERR_WORKSPACE
+    bad = nq.Config(128, 4, 2, 0, nq.PARITY_RELAXED, nq.DTYPE_F16, 5e5).c()
+    assert f(ctypes.byref(bad), 0x10000, None, 1, 1, 4, None, ctypes.byref(pk), None,
+             None) == nq.NQ_ERR_UNSUPPORTED
+    assert f(ctypes.byref(cc), 0x10000, None, 0, 1, 4, None, ctypes.byref(pk), None,
+             None) == nq.NQ_ERR_INVALID_ARG
