@@ -1,14 +1,20 @@
 """Benchmark of the E8 KV-cache hot path on one MI355X.
 
-One step = the whole path over the Llama-3.1-8B 32K-token cache (32 layers x
-8 KV heads x 32768 tokens x head_dim 128, fp16 K and V, k2v2 relaxed, one
-scale per head vector):
+Headline (the metric): quantize + pack of the Llama-3.1-8B 32K-token cache
+(32 layers x 8 KV heads x 32768 tokens x head_dim 128, fp16 K and V, k2v2
+relaxed, one scale per head vector); `value` = tokens of the cache / median
+time of the K and V quantize calls (HIP events on the kernels' stream).
+
+One step = the whole path over that cache:
   1. quantize + pack K (RoPE removed, theta 5e5) and V      nq_quantize_kv
   2. dequantize K (RoPE re-applied) and V                   nq_dequantize_kv
   3. score one decode query per query head (32 heads, GQA 4) against the
      packed keys                                            nq_score_packed_keys
-Inputs are synthetic (e8_lattice_vector_amd.synth) and resident in HBM
-before timing starts.  Prints one JSON line.
+Also timed on their own: packed-value attention, the Mistral-7B (K3V2) and
+Phi-3-mini (d = 96, strict) caches, scoring at the Qwen2.5-14B decode shape,
+and the CPU oracle on a sample (cpu_baseline).  Inputs are synthetic
+(e8_lattice_vector_amd.synth) and resident in HBM before timing starts.
+Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -33,30 +39,43 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-shape", action="store_true",
                     help="skip the scoring run at the Qwen2.5-14B decode shape")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=32768,
-                    help="tokens per slab (all 8 heads, K and V) the oracle runs on")
-    ap.add_argument("--cpu-sample-slabs", type=int, default=2,
-                    help="slabs of the cache the oracle runs on")
+    ap.add_argument("--no-other-shapes", action="store_true",
+                    help="skip the Mistral-7B and Phi-3-mini caches")
+    ap.add_argument("--cpu-sample-slabs", type=int, default=1,
+                    help="slabs of the cache (all heads and tokens, K and V) the oracle runs on")
     return ap.parse_args()
+
+
+SOURCES = ("nq_kernels.hip", "nq_device.h", "nq_exact.hip")
+
+
+def source_sha() -> str:
+    """sha256 of the quantize kernels' sources (the files whose code the
+    committed counters measured), concatenated in a fixed order."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in SOURCES:
+        with open(os.path.join(ROOT, "e8_lattice_vector_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def profiled_traffic(profiles):
     """HBM bytes per launch from committed rocprofv3 summaries (FETCH_SIZE and
     WRITE_SIZE, each scaled by the copy-kernel calibration), averaged over the
     summaries (one per launch of the step), or None when any is missing or the
-    kernel source has changed since its counters were taken."""
-    import hashlib
+    kernel sources have changed since its counters were taken."""
     import re
 
-    src = os.path.join(ROOT, "e8_lattice_vector_amd", "csrc", "nq_kernels.hip")
     vals = []
     for profile in profiles:
         try:
             text = open(os.path.join(ROOT, "profiles", profile)).read()
-            sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+            sha = source_sha()
         except OSError:
             return None
-        m_sha = re.search(r"nq_kernels.hip sha256: ([0-9a-f]{64})", text)
+        m_sha = re.search(r"kernel sources sha256: ([0-9a-f]{64})", text)
         m_tr = re.search(r"traffic_bytes_per_launch: (\d+)", text)
         if not m_sha or not m_tr or m_sha.group(1) != sha:
             return None
@@ -64,39 +83,139 @@ def profiled_traffic(profiles):
     return round(sum(vals) / len(vals)) if vals else None
 
 
-def cpu_baseline(w, tokens, slabs):
-    """The oracle, as it stands, on a bounded sample of the same workload."""
-    import numpy as np  # noqa: F401
+def median(xs):
+    xs = sorted(xs)
+    n = len(xs)
+    return xs[n // 2] if n % 2 else 0.5 * (xs[n // 2 - 1] + xs[n // 2])
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_job(job):
+    """Worker: the oracle's quantize + pack of heads [h0, h1) of one slab of
+    the cache (K with RoPE removal, or V), single-threaded; returns the
+    oracle's seconds (input generation excluded)."""
+    kind, w, slab, h0, h1 = job
+    import torch
+    from threadpoolctl import threadpool_limits
 
     from e8_lattice_vector_amd import synth
     from oracle import codec as oc
 
-    k = synth.kv("k", slabs, w.H, tokens, w.d, w.theta, 0).numpy()
-    v = synth.kv("v", slabs, w.H, tokens, w.d, 0.0, 0).numpy()
-    q = synth.queries(slabs, 32, w.d, 0).numpy()
-    ck = oc.Codec(w.d, w.bits_k, w.G, w.strict, w.theta)
-    cv = oc.Codec(w.d, w.bits_v, w.G, w.strict, 0.0)
-    from threadpoolctl import threadpool_limits
-
-    # one thread, so that "cores" is what the run used (numpy's BLAS would
-    # otherwise spread the scoring products over the host's cores)
+    torch.set_num_threads(1)
+    x = synth.kv(kind, 1, w.H, w.T, w.d, w.theta if kind == "k" else 0.0, 0,
+                 slab0=slab).numpy()[:, h0:h1]
+    cdc = oc.Codec(w.d, w.bits_k if kind == "k" else w.bits_v, w.G, w.strict,
+                   w.theta if kind == "k" else 0.0)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        rk = oc.quantize(k, ck, is_key=True)
-        rv = oc.quantize(v, cv)
-        oc.dequantize(rk["codes"], rk["cosets"], rk["scales"], ck, is_key=True)
-        oc.dequantize(rv["codes"], rv["cosets"], rv["scales"], cv)
-        oc.score(q, rk["codes"], rk["cosets"], rk["scales"], ck)
-        dt = time.perf_counter() - t0
-    cache_tokens = tokens * slabs / w.S  # slabs of S
+        oc.quantize(x, cdc, is_key=kind == "k")
+        return time.perf_counter() - t0
+
+
+def cpu_baseline(w, slabs, heads_per_job=1, max_procs=16):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    quantize + pack of K and V of `slabs` slabs (all heads, all tokens), in
+    single-threaded worker processes over the host's cores (at most
+    max_procs, the CPU share of one GPU)."""
+    import multiprocessing as mp
+
+    jobs = [(kind, w, s, h0, min(w.H, h0 + heads_per_job))
+            for kind in ("k", "v") for s in range(slabs) for h0 in range(0, w.H, heads_per_job)]
+    # no more processes than jobs: an idle process is not a core at work
+    nproc = max(1, min(max_procs, os.cpu_count() or 1, len(jobs)))
+    t0 = time.perf_counter()
+    with mp.get_context("spawn").Pool(nproc) as pool:
+        secs = pool.map(cpu_job, jobs, chunksize=1)
+    wall = time.perf_counter() - t0
+    busy = sum(secs)
+    cache_tokens = w.T * slabs / w.S          # the sample is slabs / S of the cache
     return {
-        "value": cache_tokens / dt,
+        "value": cache_tokens / (busy / nproc),
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": nproc,
         "kind": "oracle",
-        "sample": f"{slabs} of {w.S} slabs x {w.H} heads x {tokens} tokens, K+V quantize, "
-                  f"dequantize and 32-query scoring ({dt:.1f} s single-threaded numpy)",
+        "cpu_model": _cpu_model(),
+        "nproc": os.cpu_count(),
+        "sample": f"{slabs} of {w.S} slabs x {w.H} heads x {w.T} tokens, K and V quantize+pack "
+                  f"(fp64 oracle), {len(jobs)} jobs on {nproc} single-threaded processes: "
+                  f"{busy:.1f} s of oracle time ({wall:.1f} s wall incl. input generation); "
+                  f"tokens/s = sampled tokens / (oracle seconds / processes)",
     }
+
+
+def timed(fn, steps, warmup, stream):
+    """Median milliseconds of `fn` over `steps` calls (HIP events on the
+    stream the kernels run on), after `warmup` calls."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record(stream)
+        fn()
+        e[1].record(stream)
+    torch.cuda.synchronize()
+    return median([e[0].elapsed_time(e[1]) for e in ev])
+
+
+def other_workload(wname, steps, warmup, dev, stream, Hq):
+    """Quantize + pack, dequantize and (Hq > 0) packed-key scoring of one of
+    the other caches of the pages' models, each timed on its own."""
+    import torch
+
+    from e8_lattice_vector_amd import nq, synth, workloads
+
+    w = workloads.ALL[wname]
+    cfg = nq.Config(w.d, w.bits_k, w.bits_v, w.G,
+                    nq.PARITY_STRICT if w.strict else nq.PARITY_RELAXED, nq.DTYPE_F16, w.theta)
+    k, v = synth.workload_inputs(w, seed=0, device=dev)
+    pk = nq.alloc_packed(cfg, False, w.S, w.H, w.T, dev)
+    pv = nq.alloc_packed(cfg, True, w.S, w.H, w.T, dev)
+    ws = nq.alloc_workspace(cfg, w.S, w.H, w.T, dev)
+    kd, vd = torch.empty_like(k), torch.empty_like(v)
+    tq = timed(lambda: nq.quantize_kv(cfg, k, v, pk=pk, pv=pv, workspace=ws), steps, warmup,
+               stream)
+    tdq = timed(lambda: nq.dequantize_kv(cfg, pk, pv, w.S, w.H, w.T, k_out=kd, v_out=vd,
+                                         workspace=ws), steps, warmup, stream)
+    nv = w.S * w.H * w.T
+    fp16 = 2 * nv * w.d * 2
+    packed = pk.nbytes() + pv.nbytes()
+    table = w.T * (w.d // 2) * 8 if w.theta > 0 else 0
+    qb = fp16 + packed + table
+    out = {
+        "shape": f"{w.S} slabs x {w.H} KV heads x {w.T} tokens x d {w.d}",
+        "codec": f"k{w.bits_k}v{w.bits_v} {'strict' if w.strict else 'relaxed'}, scale per "
+                 f"{w.G or 'head vector'}, rope_theta {w.theta:g}",
+        "quantize": {"ms": tq, "tokens_per_s": w.T / (tq * 1e-3),
+                     "hbm_GBps": qb / (tq * 1e-3) / 1e9,
+                     "frac_hbm_peak": qb / (tq * 1e-3) / 1e9 / HBM_PEAK_GBPS, "bytes": qb},
+        "dequantize": {"ms": tdq, "tokens_per_s": w.T / (tdq * 1e-3),
+                       "hbm_GBps": qb / (tdq * 1e-3) / 1e9,
+                       "frac_hbm_peak": qb / (tdq * 1e-3) / 1e9 / HBM_PEAK_GBPS},
+    }
+    if Hq:
+        q = synth.queries(w.S, Hq, w.d, 0, dev)
+        sc = torch.empty((w.S, Hq, w.T), dtype=torch.float32, device=dev)
+        tsc = timed(lambda: nq.score_packed_keys(cfg, pk, q, w.S, w.H, w.T, scores=sc), steps,
+                    warmup, stream)
+        sb = pk.nbytes() + q.numel() * 2 + sc.numel() * 4
+        out["score"] = {"ms": tsc, "query_heads": Hq, "keys_per_s": nv / (tsc * 1e-3),
+                        "hbm_GBps": sb / (tsc * 1e-3) / 1e9,
+                        "frac_hbm_peak": sb / (tsc * 1e-3) / 1e9 / HBM_PEAK_GBPS}
+    del k, v, pk, pv, ws, kd, vd
+    torch.cuda.empty_cache()
+    return out
 
 
 def qwen_decode_scores(steps, warmup, dev, stream):
@@ -122,16 +241,8 @@ def qwen_decode_scores(steps, warmup, dev, stream):
         del k
     q = synth.queries(w.S, w.Hq, w.d, 0, dev)
     sc = torch.empty((w.S, w.Hq, w.T), dtype=torch.float32, device=dev)
-    for _ in range(warmup):
-        nq.score_packed_keys(cfg, pk, q, w.S, w.H, w.T, scores=sc)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    torch.cuda.synchronize()
-    ev[0].record(stream)
-    for _ in range(steps):
-        nq.score_packed_keys(cfg, pk, q, w.S, w.H, w.T, scores=sc)
-    ev[1].record(stream)
-    torch.cuda.synchronize()
-    ms = ev[0].elapsed_time(ev[1]) / steps
+    ms = timed(lambda: nq.score_packed_keys(cfg, pk, q, w.S, w.H, w.T, scores=sc), steps,
+               warmup, stream)
     keys = w.S * w.H * w.T
     nbytes = pk.nbytes() + q.numel() * 2 + sc.numel() * 4
     del pk, ws, q, sc
@@ -140,7 +251,7 @@ def qwen_decode_scores(steps, warmup, dev, stream):
         "ms": ms,
         "keys_per_s": keys / (ms * 1e-3),
         "GBps": nbytes / (ms * 1e-3) / 1e9,
-        "pct_hbm_peak": 100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "bytes": nbytes,
         "what": "scores of 40 fp16 decode queries per slab against 768 x 8 x 16384 packed keys "
                 "(36 B/key read, 20 B/key written)",
@@ -178,23 +289,20 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        nq.quantize_kv(cfg, k, None, pk=pk, workspace=ws)
+        nq.quantize_kv(cfg, k, v, pk=pk, pv=pv, workspace=ws)
         if ev is not None:
             ev[1].record(stream)
-        nq.quantize_kv(cfg, None, v, pv=pv, workspace=ws)
-        if ev is not None:
-            ev[2].record(stream)
         nq.dequantize_kv(cfg, pk, pv, w.S, w.H, w.T, k_out=kd, v_out=vd, workspace=ws)
         if ev is not None:
-            ev[3].record(stream)
+            ev[2].record(stream)
         nq.score_packed_keys(cfg, pk, q, w.S, w.H, w.T, scores=scores)
         if ev is not None:
-            ev[4].record(stream)
+            ev[3].record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -202,57 +310,48 @@ def main():
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    seg = [[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in events]
-    tk = sum(s[0] for s in seg) / args.steps
-    tv = sum(s[1] for s in seg) / args.steps
-    tdq = sum(s[2] for s in seg) / args.steps
-    tsc = sum(s[3] for s in seg) / args.steps
+    seg = [[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in events]
+    tq, tdq, tsc = (median([s_[j] for s_ in seg]) for j in range(3))
+    tstep = median([e[0].elapsed_time(e[3]) for e in events])
     ms_step = wall * 1e3 / args.steps
+    # the two tensors' launches, each in a call of its own
+    tk = timed(lambda: nq.quantize_kv(cfg, k, None, pk=pk, workspace=ws), args.steps,
+               args.warmup, stream)
+    tv = timed(lambda: nq.quantize_kv(cfg, None, v, pv=pv, workspace=ws), args.steps,
+               args.warmup, stream)
 
     nv = w.S * w.H * w.T
     fp16_bytes = nv * w.d * 2
     vec_bytes = pk.nbytes() // nv
     packed = nv * vec_bytes
     table = w.T * (w.d // 2) * 8
-    q_bytes = (fp16_bytes + packed) * 2 + table           # K and V, + RoPE table read
+    k_bytes = fp16_bytes + packed + table                 # K launch, + RoPE table read
+    v_bytes = fp16_bytes + packed
+    q_bytes = k_bytes + v_bytes
     dq_bytes = q_bytes
     sc_bytes = packed + w.S * Hq * w.d * 2 + w.S * Hq * w.T * 4
-    tq = tk + tv
     q_gbps = q_bytes / (tq * 1e-3) / 1e9
 
     # next row: value half of decode attention on the packed V, weights =
     # softmax of the step's scores (timed on its own, not part of the step)
     wts = torch.softmax(scores, dim=-1).contiguous()
     att = torch.empty((w.S, Hq, w.d), dtype=torch.float32, device=dev)
-    for _ in range(args.warmup):
-        nq.attend_packed_values(cfg, pv, wts, w.S, w.H, w.T, out=att)
-    ea = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    torch.cuda.synchronize()
-    ea[0].record(stream)
-    for _ in range(args.steps):
-        nq.attend_packed_values(cfg, pv, wts, w.S, w.H, w.T, out=att)
-    ea[1].record(stream)
-    torch.cuda.synchronize()
-    tat = ea[0].elapsed_time(ea[1]) / args.steps
+    tat = timed(lambda: nq.attend_packed_values(cfg, pv, wts, w.S, w.H, w.T, out=att),
+                args.steps, args.warmup, stream)
     at_bytes = packed + w.S * Hq * w.T * 4 + w.S * Hq * w.d * 4
     del wts, att
 
-    # plain device copy of 4 GiB for context
+    # plain device copy of 4 GiB (context only, not a ceiling)
     src = torch.empty(1 << 31, dtype=torch.float16, device=dev)
     dst = torch.empty_like(src)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    dst.copy_(src)
-    e0.record(stream)
-    for _ in range(5):
-        dst.copy_(src)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 2 * src.numel() * 2 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del src, dst
+    tcp = timed(lambda: dst.copy_(src), 5, 1, stream)
+    copy_gbps = 2 * src.numel() * 2 / (tcp * 1e-3) / 1e9
+    del src, dst, k, v, kd, vd, pk, pv, ws, q, scores
+    torch.cuda.empty_cache()
 
     out = {
         "metric": "KV quantize+pack tokens/s and HBM GB/s (% of peak), Llama-3.1-8B shape, 1 GPU",
-        "value": w.T / (ms_step * 1e-3),
+        "value": w.T / (tq * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -269,25 +368,42 @@ def main():
             "codec": f"k{w.bits_k}v{w.bits_v} {'strict' if w.strict else 'relaxed'} "
                      f"scale per {w.G or w.d} coords, rope_theta {w.theta:g}",
             "step": "quantize+pack K,V -> dequantize K,V -> score 32 decode queries",
+            "value": "tokens of the 32K cache / median time of one nq_quantize_kv call on K "
+                     "and V (RoPE table, fp32 kernels, fp64 near-tie passes)",
             "storage": "fp16 in/out, 36 B per packed vector",
+            "arithmetic": "fp32 (fp64 for near-tie vectors); scoring and attention multiply on "
+                          "bf16 matrix cores with exact code values and the fp32 query / "
+                          "weight split into two bf16 parts (hi + lo), fp32 accumulation",
         },
         "quantize": {
             "tokens_per_s": w.T / (tq * 1e-3),
             "ms": tq,
             "hbm_GBps": q_gbps,
             "fp16_kv_GBps": 2 * fp16_bytes / (tq * 1e-3) / 1e9,
-            "pct_hbm_peak": 100 * q_gbps / HBM_PEAK_GBPS,
-            "pct_copy_bw": 100 * q_gbps / copy_gbps,
+            "frac_hbm_peak": q_gbps / HBM_PEAK_GBPS,
+            "bytes": q_bytes,
         },
-        "kernels_ms": {"quantize_k(+rope table)": tk, "quantize_v": tv,
-                       "dequantize_kv(+rope table)": tdq, "score": tsc},
+        "step": {
+            "ms_median_events": tstep,
+            "ms_wall": ms_step,
+            "tokens_per_s": w.T / (tstep * 1e-3),
+        },
+        "kernels_ms_median": {"quantize_kv (K and V in one call)": tq,
+                              "quantize_k alone (rope table, fp32 kernel, fp64 pass)": tk,
+                              "quantize_v alone (counter clear, fp32 kernel, fp64 pass)": tv,
+                              "dequantize_kv (rope table, K, V)": tdq, "score": tsc},
+        "frac_hbm_peak": {"quantize_k": k_bytes / (tk * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                          "quantize_v": v_bytes / (tv * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                          "dequantize_kv": dq_bytes / (tdq * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                          "score": sc_bytes / (tsc * 1e-3) / 1e9 / HBM_PEAK_GBPS},
         "dequantize_GBps": dq_bytes / (tdq * 1e-3) / 1e9,
         "score_GBps": sc_bytes / (tsc * 1e-3) / 1e9,
-        "copy_GBps": copy_gbps,
+        "copy_GBps_context": copy_gbps,
         "next_rows": {
             "attend_packed_values": {
                 "ms": tat,
                 "GBps": at_bytes / (tat * 1e-3) / 1e9,
+                "frac_hbm_peak": at_bytes / (tat * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                 "what": "sum_t softmax(scores)_t * V_t over the packed V, 32 query heads",
             },
         },
@@ -300,15 +416,22 @@ def main():
             "traffic": profiled_traffic(["quantize_fast_kernel-llama-3.1-8b-32k.md",
                                          "quantize_mfma_kernel-llama-3.1-8b-32k.md"]),
             "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE/WRITE_SIZE, copy-calibrated)",
-            "kernel": "quantize: K launch quantize_fast_kernel (butterfly Hadamard, incl. "
-                      "RoPE-table build), V launch quantize_mfma_kernel (matrix-core Hadamard)",
+            "kernel": "quantize (one call on K and V): RoPE-table build, K launch "
+                      "quantize_fast_kernel (butterfly Hadamard), V launch quantize_mfma_kernel "
+                      "(matrix-core Hadamard), the fp64 near-tie pass after each",
+            "algorithmic_bytes_per_launch": {"K": k_bytes, "V": v_bytes},
             "avg_launch_ms": tq / 2,
         },
     }
+    if not args.no_other_shapes:
+        out["other_workloads"] = {
+            "mistral-7b": other_workload("mistral-7b", args.steps, args.warmup, dev, stream, 32),
+            "phi-3-mini": other_workload("phi-3-mini", args.steps, args.warmup, dev, stream, 0),
+        }
     if not args.no_decode_shape:
         out["score_decode_shape"] = qwen_decode_scores(args.steps, args.warmup, dev, stream)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_tokens, args.cpu_sample_slabs)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_slabs)
     print(json.dumps(out), flush=True)
 
 

@@ -67,6 +67,11 @@ __device__ __forceinline__ float median3(float b, float s, float x) {
 __device__ __forceinline__ double median3(double b, double s, double x) {
   return fmax(fmin(b, s), fmin(fmax(b, s), x));
 }
+__device__ __forceinline__ uint32_t median3u(uint32_t b, uint32_t s, uint32_t x) {
+  uint32_t r;
+  asm("v_med3_u32 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(s), "v"(x));
+  return r;
+}
 
 // Nearest codeword of the b-bit cube codebook for one 8-group, in fp32 or
 // fp64 (F).
@@ -181,32 +186,41 @@ __device__ __forceinline__ void e8_decode2(const float g[8], uint32_t& code,
   // 4 |e|.  |.| comes free as a source modifier.  Switching one coordinate
   // to its other neighbour costs 4 |t| on the integer coset and 4 |e| on the
   // half coset, so the second smallest of each bounds the margin.
-  uint32_t X = 0, Bn = 0, f0 = 1u << 14, f1 = 0;
-  float acc = 0.f, best0 = 0.f, sec0 = INFINITY, best1 = INFINITY, sec1 = INFINITY;
+  //
+  // The smallest |t| (|e|) and its coordinate come from one v_min_u32 on
+  // keys that hold the bits of |t| with the 3 low mantissa bits replaced by
+  // the coordinate index (non-negative floats order like their bits), so
+  // equal values pick the lowest index.  Values within 7 ulps may then pick
+  // either coordinate and carry up to 7 ulps (< 2e-6) of error into the
+  // costs, but the gap between them is then far below kNearTie, so those
+  // groups are re-decided in fp64 anyway.
+  uint32_t X = 0, Bn = 0;
+  float acc = 0.f, b1r = INFINITY;
+  uint32_t kb0 = ~0u, ks0 = ~0u, kb1 = ~0u, ks1 = ~0u;
 #pragma unroll
   for (int k = 7; k >= 0; --k) {
     const float t = fabsf(g[k]) - 1.0f;
-    const float at = fabsf(t);
-    const float ae = fabsf(at - 1.0f);
+    const float e = fabsf(t) - 1.0f;
     X = shift_in(X, g[k], 2);
     Bn = shift_in(Bn, t, 1);
-    acc = acc + ae;
-    if (k == 7) {
-      best0 = at;
-    } else {
-      sec0 = median3(best0, sec0, at);
-      if (at <= best0) {
-        best0 = at;
-        f0 = 1u << (2 * k);
-      }
-    }
+    acc = acc + fabsf(e);
+    const uint32_t k0 = (__float_as_uint(t) & 0x7ffffff8u) | (uint32_t)k;
+    ks0 = median3u(kb0, ks0, k0);
+    kb0 = min(kb0, k0);
     if (STRICT) {
-      sec1 = median3(best1, sec1, ae);
-      if (ae <= best1) { best1 = ae; f1 = 1u << (2 * k); }
+      const uint32_t k1 = (__float_as_uint(e) & 0x7ffffff8u) | (uint32_t)k;
+      ks1 = median3u(kb1, ks1, k1);
+      kb1 = min(kb1, k1);
     } else {
-      best1 = fminf(best1, ae);
+      b1r = fminf(b1r, fabsf(e));
     }
   }
+  const float best0 = __uint_as_float(kb0 & 0x7ffffff8u);
+  const float sec0 = __uint_as_float(ks0 & 0x7ffffff8u);
+  const float best1 = STRICT ? __uint_as_float(kb1 & 0x7ffffff8u) : b1r;
+  const float sec1 = __uint_as_float(ks1 & 0x7ffffff8u);
+  const uint32_t f0 = 1u << (2 * (kb0 & 7u));
+  const uint32_t f1 = STRICT ? 1u << (2 * (kb1 & 7u)) : 0u;
   const uint32_t odd0 = __builtin_popcount(Bn) & 1u;
   float lhs = __fmaf_rn(-2.f, acc, 8.f);
   uint32_t odd1 = 0;

@@ -234,12 +234,13 @@ __global__ __launch_bounds__(kExBlock) void exact_kernel(TensorArgs a, int all) 
 template <int N, int BITS, typename T>
 hipError_t exact_n(const TensorArgs& a, int all, hipStream_t s) {
   constexpr int VPB = kExBlock / (N / 8);
-  // the queue holds about 1/32 of the vectors; ~1e-3 are queued on random
-  // data, so a modest grid drains it (a full queue falls back to the
+  // the queue holds about 1/32 of the vectors and ~1.5e-3 of random vectors
+  // are queued: a grid of up to 2048 blocks takes them in one sweep, the
+  // blocks past the count exit at once (a full queue falls back to the
   // grid-stride loop over every vector)
   const int64_t vecs = all ? a.n_vec : (a.queue_cap < a.n_vec ? a.queue_cap : a.n_vec);
   int64_t blocks = (vecs + VPB - 1) / VPB;
-  const int64_t cap = all ? 65536 : 256;
+  const int64_t cap = all ? 65536 : 2048;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   if (a.strict)
@@ -282,9 +283,15 @@ __global__ __launch_bounds__(kExBlock) void rope_table_kernel(
   const int k = (int)(i % h);
   const double p = pos ? (double)pos[t] : (double)(pos0 + t);
   const double ang = p * f.omega[k];
-  double sn, cs;
-  sincos(ang, &sn, &cs);
-  table[i] = make_float2((float)cs, (float)sn);
+  // reduce the fp64 angle to [-pi, pi] in fp64 (2 pi as a two-term constant),
+  // then fp32 sincos: cos and sin to about one fp32 ulp, which is all the
+  // fp32 kernels need (their near-tie decisions are re-taken in fp64)
+  const double n = rint(ang * 0.15915494309189535);
+  double r = fma(-n, 6.283185307179586, ang);
+  r = fma(-n, 2.4492935982947064e-16, r);
+  float sn, cs;
+  sincosf((float)r, &sn, &cs);
+  table[i] = make_float2(cs, sn);
 }
 
 __global__ void clear_counters_kernel(unsigned long long* counters, int n) {

@@ -402,21 +402,40 @@ __device__ __forceinline__ int64_t xcd_wave_id() {
   return (int64_t)lb * (kBlock / 64) + w;
 }
 
-// Appends vector `vec` of every lane with `push` set to the call's queue of
-// vectors whose lattice decisions are re-taken in fp64 (one atomic add per
-// wave; entries past the queue's capacity are dropped, and the fp64 pass then
-// recomputes every vector).  All lanes of the wave must call this.
-__device__ __forceinline__ void queue_push(const TensorArgs& a, bool push, int64_t vec) {
+// What a wave needs to append to the queue of the fp64 pass, kept in LDS so
+// that the hot loop holds none of it in registers: the counter, the queue,
+// its capacity, and the index of the wave's first vector with the stride
+// between the (slab, head) planes it walks.
+struct QueueSlot {
+  unsigned long long* count;
+  int64_t* queue;
+  int64_t cap;
+  int64_t base;    // vector index of plane sh0, token t0 of the wave
+  int64_t stride;  // vectors per plane (T)
+};
+
+__device__ __forceinline__ void queue_slot_init(QueueSlot* slot, const TensorArgs& a,
+                                                int64_t base) {
+  if ((threadIdx.x & 63) == 0) *slot = QueueSlot{a.queue_count, a.queue, a.queue_cap, base, a.T};
+}
+
+// Appends vector slot.base + it * slot.stride + off of every lane with `push`
+// set to the call's queue of vectors whose lattice decisions are re-taken in
+// fp64 (one atomic add per wave; entries past the queue's capacity are
+// dropped, and the fp64 pass then recomputes every vector).  All lanes of
+// the wave must call this.
+__device__ __forceinline__ void queue_push(const QueueSlot* slot, bool push, int it, int off) {
   const uint64_t b = __ballot(push);
   if (b == 0) return;
+  const QueueSlot q = *slot;
   const int lane = threadIdx.x & 63;
   const int first = __builtin_ctzll(b);
   unsigned long long base = 0;
-  if (lane == first) base = atomicAdd(a.queue_count, (unsigned long long)__popcll(b));
+  if (lane == first) base = atomicAdd(q.count, (unsigned long long)__popcll(b));
   base = __shfl(base, first);
   if (push) {
     const unsigned long long r = base + (unsigned long long)__popcll(b & ((1ull << lane) - 1ull));
-    if (r < (unsigned long long)a.queue_cap) a.queue[r] = vec;
+    if (r < (unsigned long long)q.cap) q.queue[r] = q.base + (int64_t)it * q.stride + off;
   }
 }
 
@@ -441,6 +460,9 @@ __global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
   if (tt >= n_tt || sh0 >= SH) return;
   const int64_t sh1 = min64(SH, sh0 + sh_chunk);
   const int64_t t = tt * TPW + row;
+  __shared__ QueueSlot qslots[kBlock / 64];
+  QueueSlot* qslot = &qslots[threadIdx.x >> 6];
+  queue_slot_init(qslot, a, sh0 * a.T + tt * TPW);
   const bool tvalid = t < a.T;
   const int64_t tc = tvalid ? t : a.T - 1;
   const int j0 = 8 * m;
@@ -518,23 +540,21 @@ __global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
       constexpr int KR = N == 128 ? 3 : N == 64 ? 2 : N == 32 ? 1 : 0;
       partner_mul<KR>(pv, v, rs);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = __fadd_rn(__fmul_rn(v[k], rc[k]), pv[k]);
+      for (int k = 0; k < 8; ++k) v[k] = __fmaf_rn(v[k], rc[k], pv[k]);
     } else if (ROPE == 2) {
       float pv[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) pv[k] = __shfl(v[k], pl);
       if (data_lane) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-          v[k] = __fadd_rn(__fmul_rn(v[k], rc[k]), __fmul_rn(pv[k], rs[k]));
+        for (int k = 0; k < 8; ++k) v[k] = __fmaf_rn(v[k], rc[k], __fmul_rn(pv[k], rs[k]));
       }
     } else if (ROPE == 3) {
       float x[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) x[k] = v[k];
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        v[k] = __fadd_rn(__fmul_rn(x[k], rc[k]), __fmul_rn(x[k ^ 4], rs[k]));
+      for (int k = 0; k < 8; ++k) v[k] = __fmaf_rn(x[k], rc[k], __fmul_rn(x[k ^ 4], rs[k]));
     }
     if constexpr (kFuse) fwht_lane_24(v);
     else fwht_lane(v);
@@ -573,7 +593,7 @@ __global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
       const uint64_t nb = __ballot(near);
       if (nb != 0) {
         const bool lead = l == 0 && tvalid && ((nb >> row_shift) & kRowMask) != 0;
-        queue_push(a, lead, (sh0 + it) * a.T + t);
+        queue_push(qslot, lead, it, row);
       }
     }
     if (STRICT && a.compact) code = Compact<BITS>::fold(code, c);
@@ -648,6 +668,9 @@ __global__ __launch_bounds__(kBlock) void quantize_mfma_kernel(TensorArgs a, int
   if (sh0 >= SH) return;
   const int64_t sh1 = min64(SH, sh0 + sh_chunk);
   const int64_t t = tt * 16 + v;
+  __shared__ QueueSlot qslots[kBlock / 64];
+  QueueSlot* qslot = &qslots[threadIdx.x >> 6];
+  queue_slot_init(qslot, a, sh0 * a.T + tt * 16);
   const bool tvalid = t < a.T;
   const int64_t tc = tvalid ? t : a.T - 1;
 
@@ -748,7 +771,7 @@ __global__ __launch_bounds__(kBlock) void quantize_mfma_kernel(TensorArgs a, int
       if (nb != 0) {
         const uint64_t f = nb | (nb >> 16) | (nb >> 32) | (nb >> 48);
         const bool lead = p == 0 && tvalid && ((f >> v) & 1u) != 0;
-        queue_push(a, lead, (sh0 + it) * a.T + t);
+        queue_push(qslot, lead, it, v);
       }
     }
     if (tvalid) *reinterpret_cast<uint2*>(cb + oc) = make_uint2(words[0], words[1]);
@@ -812,11 +835,14 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(TensorArgs a) {
   {
     const uint64_t nb = __ballot(mgn < kNearTie);
     if (nb != 0) {
+      __shared__ QueueSlot qslots[kBlock / 64];
+      QueueSlot* qslot = &qslots[threadIdx.x >> 6];
+      queue_slot_init(qslot, a, vv - (threadIdx.x & 63) / VL);
       const int lane = threadIdx.x & 63;
       const uint64_t rows = nb >> (lane - m);
       const bool lead = m == 0 && live &&
                         (rows & (VL >= 64 ? ~0ull : ((1ull << VL) - 1ull))) != 0;
-      queue_push(a, lead, vv);
+      queue_push(qslot, lead, 0, lane / VL);
     }
   }
   if (!live) return;
