@@ -34,8 +34,10 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, vendor figure
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    # the GPU's clocks settle over the first ~25 ms of sustained work: the
+    # default warm-up (about 50 ms of steps) keeps the timed steps past that
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode-shape", action="store_true",
                     help="skip the scoring run at the Qwen2.5-14B decode shape")

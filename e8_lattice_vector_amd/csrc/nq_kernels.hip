@@ -627,6 +627,232 @@ __global__ __launch_bounds__(kBlock) void quantize_fast_kernel(TensorArgs a,
 }
 
 // ---------------------------------------------------------------------------
+// Keys with split-half RoPE at d = n = 128, fp16 input, one or two scales
+// per vector: the RoPE removal fused with the stride-64 butterfly.
+//
+// Lane l of an 8-lane row holds input coordinates 8m .. 8m+7 and their RoPE
+// partners 64 + 8m .. 64 + 8m+7 (m = lane_group(l), l < 8).  For a pair
+// (i, p = i + 64) whose angle has cosine c and sine s, the removal gives
+// x'_i = x_i c + x_p s and x'_p = x_p c - x_i s, and the stride-64 stage of
+// the transform then forms
+//     x'_i + x'_p = x_i (c - s) + x_p (c + s),
+//     x'_i - x'_p = x_i (c + s) - x_p (c - s),
+// each as one rounded product and one fused multiply-add straight from the
+// fp16 words (v_fma_mix), with the lane's (c - s, c + s) in registers: no
+// partner exchange and one cross-lane stage fewer than the fast path.
+// Stages 1, 2, 4 run inside the lane on both halves, stages 8, 16, 32
+// across the 8 lanes through DPP with the fast path's sign twist (the GF(2)
+// lane relabelling restricted to a = (1, 2, 7)).  The lane then holds output
+// groups m and m + 8 and decodes both.  The fp32 rounding order differs from
+// the textbook one; the decision margins and the fp64 pass make the codes
+// those of the fp64 definition all the same.
+// ---------------------------------------------------------------------------
+
+// x_i (c - s) + x_p (c + s) and x_i (c + s) - x_p (c - s) for the two pairs
+// of one 32-bit word of fp16 inputs (lo: word wi, partner word wp).
+#define NQ_PAIR_HALF(SEL, wi, wp, cm, cp, lo, hi)                                 \
+  do {                                                                            \
+    float t1_, t2_;                                                               \
+    asm("v_fma_mix_f32 %2, %5, %7, 0 op_sel:[" SEL ",0,0] op_sel_hi:[1,0,0]\n\t"    \
+        "v_fma_mix_f32 %3, %5, %6, 0 op_sel:[" SEL ",0,0] op_sel_hi:[1,0,0]\n\t"    \
+        "v_fma_mix_f32 %0, %4, %6, %2 op_sel:[" SEL ",0,0] op_sel_hi:[1,0,0]\n\t"   \
+        "v_fma_mix_f32 %1, %4, %7, -%3 op_sel:[" SEL ",0,0] op_sel_hi:[1,0,0]"      \
+        : "=&v"(lo), "=&v"(hi), "=&v"(t1_), "=&v"(t2_)                            \
+        : "v"(wi), "v"(wp), "v"(cm), "v"(cp));                                    \
+  } while (0)
+
+__device__ __forceinline__ void rope_stage64(const uint4& wl, const uint4& wh,
+                                             const float cm[8], const float cp[8],
+                                             float lo[8], float hi[8]) {
+  const uint32_t ui[4] = {wl.x, wl.y, wl.z, wl.w};
+  const uint32_t up[4] = {wh.x, wh.y, wh.z, wh.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    NQ_PAIR_HALF("0", ui[i], up[i], cm[2 * i], cp[2 * i], lo[2 * i], hi[2 * i]);
+    NQ_PAIR_HALF("1", ui[i], up[i], cm[2 * i + 1], cp[2 * i + 1], lo[2 * i + 1], hi[2 * i + 1]);
+  }
+}
+
+// max |v_k| over 16 values
+__device__ __forceinline__ float abs_max16(const float a[8], const float b[8]) {
+  float m;
+  asm("v_max3_f32 %0, |%1|, |%2|, |%3|\n\t"
+      "v_max3_f32 %0, %0, |%4|, |%5|\n\t"
+      "v_max3_f32 %0, %0, |%6|, |%7|\n\t"
+      "v_max3_f32 %0, %0, |%8|, |%9|\n\t"
+      "v_max3_f32 %0, %0, |%10|, |%11|\n\t"
+      "v_max3_f32 %0, %0, |%12|, |%13|\n\t"
+      "v_max3_f32 %0, %0, |%14|, |%15|\n\t"
+      "v_max_f32_e64 %0, %0, |%16|"
+      : "=&v"(m)
+      : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]),
+        "v"(a[7]), "v"(b[0]), "v"(b[1]), "v"(b[2]), "v"(b[3]), "v"(b[4]), "v"(b[5]),
+        "v"(b[6]), "v"(b[7]));
+  return m;
+}
+
+// One 8-group: scale, decode, margin.  `code` gets the packed indices (with
+// the coset bit folded in for compact packing), `c` the coset.
+template <int BITS, bool STRICT>
+__device__ __forceinline__ void pair_decode(const float v[8], float rs, int compact,
+                                            uint32_t& code, uint64_t& cball, bool& near) {
+  float y[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) y[k] = __fmul_rn(v[k], rs);
+  int c;
+  if (BITS == 2) {
+    e8_decode2<STRICT>(y, code, cball, c, near);
+  } else {
+    float mgn;
+    e8_decode<BITS, STRICT, float>(y, code, c, &mgn);
+    near = mgn < kNearTie;
+    cball = __ballot(c);
+  }
+  if (STRICT && compact) code = Compact<BITS>::fold(code, c);
+}
+
+template <int BITS>
+__device__ __forceinline__ void store_code(uint8_t* p, uint32_t code) {
+  if (BITS == 2) {
+    *reinterpret_cast<uint16_t*>(p) = (uint16_t)code;
+  } else {
+    p[0] = (uint8_t)(code & 0xffu);
+    p[1] = (uint8_t)((code >> 8) & 0xffu);
+    p[2] = (uint8_t)(code >> 16);
+  }
+}
+
+// NS scales per vector: 1 (G = 128) or 2 (G = 64, one per half).
+template <int BITS, bool STRICT, int NS>
+__global__ __launch_bounds__(kBlock) void quantize_pair_kernel(TensorArgs a, int sh_chunk) {
+  constexpr int TPW = 8;          // tokens per wave iteration
+  constexpr int BATCH = 8 / NS;   // iterations per batch of scale stores
+  const int lane = threadIdx.x & 63;
+  const int row = lane >> 3;
+  const int l = lane & 7;
+  const int m = lane_group(l);
+  const int64_t n_tt = (a.T + TPW - 1) / TPW;
+  const int64_t SH = a.n_vec / a.T;
+  const int64_t wave = xcd_wave_id();
+  const int64_t n_shc = (SH + sh_chunk - 1) / sh_chunk;
+  const int64_t tt = wave / n_shc;
+  const int64_t sh0 = (wave % n_shc) * sh_chunk;
+  if (tt >= n_tt) return;
+  const int64_t sh1 = min64(SH, sh0 + sh_chunk);
+  const int64_t t = tt * TPW + row;
+  __shared__ QueueSlot qslots[kBlock / 64];
+  QueueSlot* qslot = &qslots[threadIdx.x >> 6];
+  queue_slot_init(qslot, a, sh0 * a.T + tt * TPW);
+  const bool tvalid = t < a.T;
+  const int64_t tc = tvalid ? t : a.T - 1;
+  const int j0 = 8 * m;
+
+  // (c - s, c + s) of the lane's 8 pairs for its token
+  float cm[8], cp[8];
+  {
+    const float2* rp = a.rope + tc * 64 + j0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float2 cs = rp[k];
+      cm[k] = __fsub_rn(cs.x, cs.y);
+      cp[k] = __fadd_rn(cs.x, cs.y);
+    }
+  }
+  const float coef0 = (m & 1) ? -1.f : 1.f;
+  const float coef1 = (m & 2) ? -1.f : 1.f;
+  const float coef2 = (m & 4) ? -1.f : 1.f;
+  const bool neg_sigma = (__builtin_popcount(m) & 1) != 0;
+  const float kr = (neg_sigma ? -a.half_L : a.half_L) * (BITS == 2 ? 2.f : 1.f);
+  const int row_shift = row * 8;
+  // scale batching: lane m keeps scale (m % NS) of iteration m / NS of the batch
+  const int mi = m / NS;
+  const int which = m % NS;
+
+  // per-lane byte offsets inside one (slab, head) plane (below 2^31: the
+  // host checks); the plane bases advance uniformly
+  const uint32_t off_x = (uint32_t)(tc * 128 + j0) * 2u;
+  const uint32_t off_c = (uint32_t)(tc * a.code_bytes) + (uint32_t)(m * BITS);
+  const uint32_t off_s = (uint32_t)(tc * a.coset_bytes);
+  const int64_t plane_x = a.T * 128 * 2;
+  const int64_t plane_c = a.pT * a.code_bytes;
+  const int64_t plane_s = a.pT * a.coset_bytes;
+  const int64_t plane_g = a.pT * NS;
+  const uint32_t off_gb = ((uint32_t)(tc * NS + which) + (uint32_t)mi * (uint32_t)plane_g) * 2u;
+  float keep = 0.f;
+  const int n_it = (int)(sh1 - sh0);
+  const char* xb = static_cast<const char*>(a.x) + sh0 * plane_x;
+  uint8_t* cbp = a.codes + sh0 * plane_c;
+  uint8_t* qb = a.cosets + sh0 * plane_s;
+  char* gb = reinterpret_cast<char*>(a.scales) + sh0 * plane_g * 2;
+  uint32_t ox = off_x, oc = off_c, os = off_s;
+  for (int it = 0; it < n_it; ++it, xb += plane_x, cbp += plane_c, qb += plane_s) {
+    asm volatile("" : "+v"(ox), "+v"(oc), "+v"(os));
+    const uint4 wl = *reinterpret_cast<const uint4*>(xb + ox);
+    const uint4 wh = *reinterpret_cast<const uint4*>(xb + ox + 128);
+    float lo[8], hi[8];
+    rope_stage64(wl, wh, cm, cp, lo, hi);
+    fwht_lane(lo);
+    fwht_lane(hi);
+    stage_fmac<0>(lo, coef0);
+    stage_fmac<0>(hi, coef0);
+    stage_fmac<1>(lo, coef1);
+    stage_fmac<1>(hi, coef1);
+    stage_fmac<2>(lo, coef2);
+    stage_fmac<2>(hi, coef2);
+    float amax_lo, amax_hi, rs_lo, rs_hi;
+    if (NS == 1) {
+      float mx = abs_max16(lo, hi);
+      mx = group_max<8>(mx, 8);
+      asm("v_max_f32 %0, %1, %2" : "=v"(amax_lo) : "s"(a.eps), "v"(mx));
+      amax_hi = amax_lo;
+      // r = fl((L/2) / amax) = (L/2) fl(1/amax); fp16 inputs keep amax < 2^25
+      rs_lo = __fmul_rn(rcp_rn(amax_lo), kr);
+      rs_hi = rs_lo;
+    } else {
+      float ml = abs_max8(lo), mh = abs_max8(hi);
+      ml = group_max<8>(ml, 8);
+      mh = group_max<8>(mh, 8);
+      asm("v_max_f32 %0, %1, %2" : "=v"(amax_lo) : "s"(a.eps), "v"(ml));
+      asm("v_max_f32 %0, %1, %2" : "=v"(amax_hi) : "s"(a.eps), "v"(mh));
+      rs_lo = __fmul_rn(rcp_rn(amax_lo), kr);
+      rs_hi = __fmul_rn(rcp_rn(amax_hi), kr);
+    }
+    uint32_t code_lo, code_hi;
+    uint64_t cb_lo, cb_hi;
+    bool near_lo, near_hi;
+    pair_decode<BITS, STRICT>(lo, rs_lo, a.compact, code_lo, cb_lo, near_lo);
+    pair_decode<BITS, STRICT>(hi, rs_hi, a.compact, code_hi, cb_hi, near_hi);
+    {
+      // a vector with any near-tie group goes to the fp64 pass
+      const uint64_t nb = __ballot(near_lo || near_hi);
+      if (nb != 0) {
+        const bool lead = l == 0 && tvalid && ((nb >> row_shift) & 0xffull) != 0;
+        queue_push(qslot, lead, it, row);
+      }
+    }
+    const uint64_t cm_lo = coset_rows<8>(cb_lo);
+    const uint64_t cm_hi = coset_rows<8>(cb_hi);
+    const int slot = it & (BATCH - 1);
+    if (mi == slot) keep = (NS == 2 && which) ? amax_hi : amax_lo;
+    if (tvalid) {
+      store_code<BITS>(cbp + oc, code_lo);
+      store_code<BITS>(cbp + oc + 8 * BITS, code_hi);
+      if (l == 0 && !a.compact) {
+        const uint32_t cw = (uint32_t)((cm_lo >> row_shift) & 0xffull) |
+                            ((uint32_t)((cm_hi >> row_shift) & 0xffull) << 8);
+        *reinterpret_cast<uint16_t*>(qb + os) = (uint16_t)cw;
+      }
+    }
+    if (slot == BATCH - 1 || it == n_it - 1) {
+      if (tvalid && mi <= slot) {
+        char* sb = gb + (int64_t)(it - slot) * plane_g * 2;
+        *reinterpret_cast<uint16_t*>(sb + off_gb) = f64_to_f16_rn((double)keep * a.sigma_k);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Quantize with the rotation on the matrix cores: vectors without RoPE
 // (values, or keys when no RoPE is removed), d = n = 128, 2-bit codes, one
 // scale per vector, fp16 input.
@@ -2447,12 +2673,23 @@ inline int sh_chunk_for(int64_t SH, int64_t n_tt) {
   return (int)((SH + n_shc - 1) / n_shc);
 }
 
+// (slab, head) planes per quantize wave: up to 64, so that a wave reads its
+// token tile's RoPE rows once for many planes, but no fewer than about 8192
+// waves in all (short caches would otherwise leave most SIMDs idle).
+inline int quantize_chunk(int64_t SH, int64_t n_tt) {
+  int64_t c = SH * n_tt / 8192;
+  if (c > 64) c = 64;
+  if (c > SH) c = SH;
+  if (c < 1) c = 1;
+  return (int)c;
+}
+
 template <int N, int BITS, bool STRICT, typename T, int ROPE, bool PAD>
 hipError_t quantize_fast_launch(const TensorArgs& a, hipStream_t s) {
   constexpr int TPW = 64 / (N / 8);
   const int64_t SH = a.n_vec / a.T;
   const int64_t n_tt = (a.T + TPW - 1) / TPW;
-  const int chunk = (int)(SH < 64 ? SH : 64);
+  const int chunk = quantize_chunk(SH, n_tt);
   const int64_t waves = n_tt * ((SH + chunk - 1) / chunk);
   const int64_t blocks = ((waves + kBlock / 64 - 1) / (kBlock / 64) + 7) / 8 * 8;
   hipLaunchKernelGGL((quantize_fast_kernel<N, BITS, STRICT, T, ROPE, PAD>),
@@ -2469,6 +2706,29 @@ hipError_t quantize_fast_rope(const TensorArgs& a, hipStream_t s) {
   if (a.d == 8) return quantize_fast_launch<N, BITS, STRICT, T, 3, false>(a, s);
   if (N >= 16 && a.d == N) return quantize_fast_launch<N, BITS, STRICT, T, 1, false>(a, s);
   return quantize_fast_launch<N, BITS, STRICT, T, 2, true>(a, s);
+}
+
+// 8 tokens per wave, up to 64 (slab, head) planes per wave, tile-major (the waves
+// sharing a token tile are neighbours and share its RoPE rows in L2).
+template <int BITS, bool STRICT, int NS>
+hipError_t quantize_pair_launch(const TensorArgs& a, hipStream_t s) {
+  const int64_t SH = a.n_vec / a.T;
+  const int64_t n_tt = (a.T + 7) / 8;
+  const int chunk = quantize_chunk(SH, n_tt);
+  const int64_t waves = n_tt * ((SH + chunk - 1) / chunk);
+  const int64_t blocks = ((waves + kBlock / 64 - 1) / (kBlock / 64) + 7) / 8 * 8;
+  hipLaunchKernelGGL((quantize_pair_kernel<BITS, STRICT, NS>), dim3((unsigned)blocks),
+                     dim3(kBlock), 0, s, a, chunk);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t quantize_pair(const TensorArgs& a, hipStream_t s) {
+  if (a.n_scales == 1)
+    return a.strict ? quantize_pair_launch<BITS, true, 1>(a, s)
+                    : quantize_pair_launch<BITS, false, 1>(a, s);
+  return a.strict ? quantize_pair_launch<BITS, true, 2>(a, s)
+                  : quantize_pair_launch<BITS, false, 2>(a, s);
 }
 
 // 16 tokens per wave, kQmChunk (slab, head) planes per wave, tile-fastest.
@@ -2492,6 +2752,10 @@ hipError_t quantize_n(const TensorArgs& a, hipStream_t s) {
       if constexpr (N == 128 && BITS == 2 && std::is_same<T, __half>::value) {
         if (a.d == 128 && a.n_scales == 1 && a.rope == nullptr)
           return a.strict ? quantize_mfma_launch<true>(a, s) : quantize_mfma_launch<false>(a, s);
+      }
+      if constexpr (N == 128 && std::is_same<T, __half>::value) {
+        if (a.d == 128 && a.rope != nullptr && (a.n_scales == 1 || a.n_scales == 2))
+          return quantize_pair<BITS>(a, s);
       }
       return a.strict ? quantize_fast_rope<N, BITS, true, T>(a, s)
                       : quantize_fast_rope<N, BITS, false, T>(a, s);
