@@ -204,13 +204,17 @@ double rope_freq(const nq_config* c, int i) {
 // Builds the fp32 cos/sin table at the start of the workspace when keys need
 // RoPE; in the same launch copies the fp64 frequencies to `omega` and clears
 // the n_counters queue counters at `counters` (each when not null).
+void rope_freqs(const nq_config* c, nq::RopeFreqs* f) {
+  for (int i = 0; i < c->head_dim / 2; ++i) f->omega[i] = rope_freq(c, i);
+}
+
 int prepare_rope(const nq_config* c, int64_t T, const int32_t* positions, int64_t pos0,
                  void* ws, double* omega, unsigned long long* counters, int n_counters,
                  hipStream_t s, const float2** out) {
   *out = nullptr;
   nq::RopeFreqs f;
   const int d = c->head_dim;
-  for (int i = 0; i < d / 2; ++i) f.omega[i] = rope_freq(c, i);
+  rope_freqs(c, &f);
   float2* table = static_cast<float2*>(ws);
   if (nq::launch_rope_table(positions, pos0, T, d, f, table, omega, counters, n_counters, s) !=
       hipSuccess)
@@ -327,23 +331,33 @@ int nq_dequantize_kv(const nq_config* cfg, const nq_packed* pk,
   if (positions != nullptr && !aligned16(positions)) return NQ_ERR_INVALID_ARG;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (k_out != nullptr) {
-    const float2* rope = nullptr;
-    if (rope_bytes(cfg, T) != 0) {
-      if (ws == nullptr || ws_bytes < rope_bytes(cfg, T)) return NQ_ERR_WORKSPACE;
-      if (!aligned16(ws)) return NQ_ERR_INVALID_ARG;
-      if ((st = prepare_rope(cfg, T, positions, pk->token_offset, ws, nullptr, nullptr, 0, s,
-                             &rope)) != NQ_OK)
-        return st;
-    }
     nq::TensorArgs a = tensor_args(cfg, layout(cfg, 0), S, H, T, pk);
     a.y = k_out;
-    a.rope = rope;
-    if (nq::launch_dequantize(a, cfg->in_dtype, s) != hipSuccess) return NQ_ERR_HIP;
+    nq::RopeFreqs f;
+    const bool rope = rope_bytes(cfg, T) != 0;
+    if (rope) {
+      if (ws == nullptr || ws_bytes < rope_bytes(cfg, T)) return NQ_ERR_WORKSPACE;
+      if (!aligned16(ws)) return NQ_ERR_INVALID_ARG;
+      rope_freqs(cfg, &f);
+      a.positions = positions;
+      a.pos0 = pk->token_offset;
+      // the matrix-core kernel forms its own cos / sin rows; the others
+      // read the table
+      if (!nq::dequantize_forms_rope_rows(a, cfg->in_dtype)) {
+        const float2* table = nullptr;
+        if ((st = prepare_rope(cfg, T, positions, pk->token_offset, ws, nullptr, nullptr, 0, s,
+                               &table)) != NQ_OK)
+          return st;
+        a.rope = table;
+      }
+    }
+    if (nq::launch_dequantize(a, cfg->in_dtype, rope ? &f : nullptr, s) != hipSuccess)
+      return NQ_ERR_HIP;
   }
   if (v_out != nullptr) {
     nq::TensorArgs a = tensor_args(cfg, layout(cfg, 1), S, H, T, pv);
     a.y = v_out;
-    if (nq::launch_dequantize(a, cfg->in_dtype, s) != hipSuccess) return NQ_ERR_HIP;
+    if (nq::launch_dequantize(a, cfg->in_dtype, nullptr, s) != hipSuccess) return NQ_ERR_HIP;
   }
   return NQ_OK;
 }

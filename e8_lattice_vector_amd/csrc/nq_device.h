@@ -58,6 +58,19 @@ __device__ __forceinline__ uint32_t shift_in(uint32_t x, float w, int n) {
   return __builtin_amdgcn_alignbit(x, __float_as_uint(w), (uint32_t)(32 - n));
 }
 
+// cos and sin of the angle p * omega (position times RoPE frequency): the
+// angle is formed and reduced to [-pi, pi] in fp64 (2 pi as a two-term
+// constant), then the reduced angle is rounded once to fp32 for an fp32
+// sincos: both to about one fp32 ulp.  The RoPE table and the kernels that
+// form their own rows use this one routine, so their values are identical.
+__device__ __forceinline__ void rope_cos_sin(double p, double omega, float& c, float& s) {
+  const double ang = p * omega;
+  const double n = rint(ang * 0.15915494309189535);
+  double r = fma(-n, 6.283185307179586, ang);
+  r = fma(-n, 2.4492935982947064e-16, r);
+  sincosf((float)r, &s, &c);
+}
+
 // The median of three: with b the largest (smallest) and s the second
 // largest (smallest) of the values seen so far, median3(b, s, x) is the
 // second largest (smallest) once x joins them.  One v_med3_f32 in fp32.

@@ -282,15 +282,10 @@ __global__ __launch_bounds__(kExBlock) void rope_table_kernel(
   const int64_t t = i / h;
   const int k = (int)(i % h);
   const double p = pos ? (double)pos[t] : (double)(pos0 + t);
-  const double ang = p * f.omega[k];
-  // reduce the fp64 angle to [-pi, pi] in fp64 (2 pi as a two-term constant),
-  // then fp32 sincos: cos and sin to about one fp32 ulp, which is all the
-  // fp32 kernels need (their near-tie decisions are re-taken in fp64)
-  const double n = rint(ang * 0.15915494309189535);
-  double r = fma(-n, 6.283185307179586, ang);
-  r = fma(-n, 2.4492935982947064e-16, r);
+  // cos and sin to about one fp32 ulp, which is all the fp32 kernels need
+  // (their near-tie decisions are re-taken in fp64)
   float sn, cs;
-  sincosf((float)r, &sn, &cs);
+  rope_cos_sin(p, f.omega[k], cs, sn);
   table[i] = make_float2(cs, sn);
 }
 

@@ -86,7 +86,13 @@ hipError_t launch_quantize(const TensorArgs& a, int in_dtype, hipStream_t s);
 int quantize_impl(const nq_config* cfg, const void* k, const void* v, int64_t S, int32_t H,
                   int64_t T, const int32_t* positions, const nq_packed* pk, const nq_packed* pv,
                   void* ws, size_t ws_bytes, void* stream);
-hipError_t launch_dequantize(const TensorArgs& a, int out_dtype, hipStream_t s);
+// Dequantize; for keys with RoPE, f holds the frequencies (a kernel that
+// forms its own cos / sin rows uses f, the others the table at a.rope).
+hipError_t launch_dequantize(const TensorArgs& a, int out_dtype, const RopeFreqs* f,
+                             hipStream_t s);
+// Whether dequantize forms the cos / sin rows itself for these keys (then
+// no table is built).
+bool dequantize_forms_rope_rows(const TensorArgs& a, int out_dtype);
 hipError_t launch_score(const ScoreArgs& a, int in_dtype, hipStream_t s);
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 hipError_t launch_decode_debug(const float* y, int64_t n_groups, int bits,

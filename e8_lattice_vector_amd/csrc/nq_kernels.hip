@@ -1266,7 +1266,8 @@ __global__ __launch_bounds__(kBlock) void dequantize_fast_kernel(TensorArgs a,
 constexpr int kDmChunk = 32;
 
 template <bool CMP>
-__global__ __launch_bounds__(kBlock) void dequantize_mfma_kernel(TensorArgs a, int sh_chunk) {
+__global__ __launch_bounds__(kBlock) void dequantize_mfma_kernel(TensorArgs a, int sh_chunk,
+                                                                 RopeFreqs f) {
   const int lane = threadIdx.x & 63;
   const int v = lane & 15;
   const int p = lane >> 4;
@@ -1293,17 +1294,17 @@ __global__ __launch_bounds__(kBlock) void dequantize_mfma_kernel(TensorArgs a, i
     }
   }
   // cos / sin of angle (coordinate mod 64) r + 4 p0 + 32 p1 + 8 tau0 + 16 tau1
+  // for this lane's token, formed here once for all the wave's planes (the
+  // same values as the RoPE table's)
   float rc[4][4], rn[4][4];
   {
-    const float2* rp = a.rope + tc * 64 + 4 * (p & 1) + 32 * (p >> 1);
+    const double pos = a.positions != nullptr ? (double)a.positions[tc] : (double)(a.pos0 + tc);
+    const int k0 = 4 * (p & 1) + 32 * (p >> 1);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float2 cs = rp[8 * (q & 1) + 16 * (q >> 1) + r];
-        rc[q][r] = cs.x;
-        rn[q][r] = cs.y;
-      }
+      for (int r = 0; r < 4; ++r)
+        rope_cos_sin(pos, f.omega[k0 + 8 * (q & 1) + 16 * (q >> 1) + r], rc[q][r], rn[q][r]);
     }
   }
   const float half_rs = 0.5f * a.inv_sqrt_n;
@@ -2181,6 +2182,37 @@ __device__ __forceinline__ void value_table(uint2* tbl) {
   }
 }
 
+// The same table in kTblCopies copies, entry e of copy r at uint2 index
+// e * kTblCopies + r: lane l reads copy l % kTblCopies.  On gfx950's 64
+// four-byte LDS banks an 8-byte entry of copy r then sits in bank pair r or
+// r + 16 only, so of the 32 lanes one ds_read_b64 pass serves, at most two
+// can contend for a bank pair (about 2.3x fewer conflict stalls than random
+// lookups in one copy, measured).
+constexpr int kTblCopies = 16;
+// Entry e of the value table: the bf16 of idx - 2 + c/2 for the 4
+// coordinates of code byte e & 255 with coset bit e >> 8.
+__device__ __forceinline__ uint2 value_entry(int e) {
+  const int c = e >> 8, byte = e & 255;
+  uint32_t w[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float lo = (float)((byte >> (4 * h)) & 3) - 2.f + 0.5f * (float)c;
+    const float hi = (float)((byte >> (4 * h + 2)) & 3) - 2.f + 0.5f * (float)c;
+    w[h] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+  }
+  return make_uint2(w[0], w[1]);
+}
+// Copy 0 is computed (one entry per thread), then replicated by every thread
+// (neighbouring lanes write neighbouring copies of one entry).  Ends with a
+// barrier.
+__device__ __forceinline__ void value_table_copies(uint2* tbl) {
+  for (int e = threadIdx.x; e < 512; e += blockDim.x) tbl[e * kTblCopies] = value_entry(e);
+  __syncthreads();
+  for (int i = threadIdx.x; i < 512 * kTblCopies; i += blockDim.x)
+    if (i % kTblCopies != 0) tbl[i] = tbl[i - i % kTblCopies];
+  __syncthreads();
+}
+
 // Variant for up to 4 query heads a pass: the 16 A rows are (head, hi / lo
 // part, sub) and the two bf16 of a K-slot pair are two coordinates of one
 // token (sub 0 and 1), so a lookup in a 4 KB LDS table -- entry (c, code byte)
@@ -2332,11 +2364,10 @@ __global__ __launch_bounds__(1024) void attend_mfma4_kernel(AttendArgs a, int n_
 // cover the 128 coordinates.  Lane (key l % 16, group block g = l / 16)
 // takes the 8-groups 4 g .. 4 g + 3 of its key (8 contiguous code bytes);
 // product b uses 8-group 4 g + b, whose two table entries are that lane's B
-// operand as they come.  Up to 4 query heads a pass the rows are (head 0..3,
-// part) and rows 0..3 + 4..7 are summed across lane rows (v_permlane16_swap);
-// 5..8 heads use all 16 rows (head 0..7, part), summed across the wave's
-// halves (v_permlane32_swap).  Each wave scores 32 consecutive keys per
-// step, and two workgroups share a CU.
+// operand as they come.  Row 2h + part holds the hi or lo part of head h,
+// so the lane of group block g receives both parts of heads 2g and 2g + 1 and
+// adds them itself.  Each wave scores 32 consecutive keys per step with the
+// next step's loads in flight, and two workgroups share a CU.
 // ---------------------------------------------------------------------------
 constexpr int kScoreMfmaBlock = 1024;
 
@@ -2344,24 +2375,25 @@ template <int HPP, typename QT, bool CMP>
 __global__ __launch_bounds__(kScoreMfmaBlock, 8) void score_mfma_kernel(ScoreArgs a, int n_pass,
                                                                      int64_t chunk) {
   static_assert(HPP <= 8, "rows are (head, part)");
-  constexpr bool W8 = HPP > 4;             // rows (head 0..7, part) instead of (head 0..3, part)
   constexpr int N = 128;
   constexpr int U = 2;                     // 16-key blocks per wave per step
   extern __shared__ float qt[];            // [HPP][N] rotated queries
-  __shared__ uint2 tbl[512];
-  value_table(tbl);
+  __shared__ uint2 tbl[512 * kTblCopies];  // the value table, kTblCopies copies
   const int64_t s = blockIdx.z;
   const int h = blockIdx.y / n_pass;
   const int pass = blockIdx.y % n_pass;
   const int grp = a.Hq / a.H;
   const int hq0 = h * grp + pass * HPP;
   const int nh = min(HPP, h * grp + grp - hq0);
-  for (int i = threadIdx.x; i < HPP * N; i += blockDim.x) {
-    const int hh = i / N, j = i % N;
-    qt[i] = (hh < nh && j < a.d)
-                ? Io<QT>::load1(a.q, (s * a.Hq + hq0 + hh) * (int64_t)a.d + j)
-                : 0.f;
-  }
+  // one query coordinate per thread (HPP * N <= 1024 threads), loaded
+  // while the table is built
+  static_assert(HPP * N <= kScoreMfmaBlock, "one query coordinate per thread");
+  const int qi = threadIdx.x;
+  float qv = 0.f;
+  if (qi < HPP * N && qi / N < nh && qi % N < a.d)
+    qv = Io<QT>::load1(a.q, (s * a.Hq + hq0 + qi / N) * (int64_t)a.d + qi % N);
+  value_table_copies(tbl);
+  if (qi < HPP * N) qt[qi] = qv;
   __syncthreads();
   for (int hs = 1; hs < N; hs <<= 1) {
     for (int i = threadIdx.x; i < HPP * (N / 2); i += blockDim.x) {
@@ -2374,13 +2406,14 @@ __global__ __launch_bounds__(kScoreMfmaBlock, 8) void score_mfma_kernel(ScoreArg
     __syncthreads();
   }
   const int lane = threadIdx.x & 63;
-  const int wv = threadIdx.x >> 6;
+  // wave index in a scalar register: the key loop's control stays uniform
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int nw = blockDim.x >> 6;
   const int col = lane & 15;               // key of the block; A row
-  const int kg = lane >> 4;                // 8-groups 4 kg .. 4 kg + 3
-  const int hh = W8 ? (col & 7) : (col & 3);
-  const bool part = W8 ? (col >= 8) : ((col & 4) != 0);   // the lo-part row
-  const bool arow = (W8 || col < 8) && hh < nh;
+  const int kg = lane >> 4;                // 8-groups 4 kg .. 4 kg + 3; heads 2 kg, 2 kg + 1
+  const int hh = col >> 1;                 // A row col: head col / 2,
+  const bool part = (col & 1) != 0;        // its lo part on odd rows
+  const bool arow = hh < nh;
   nq_bf16x8 A[4];
 #pragma unroll
   for (int b = 0; b < 4; ++b) {
@@ -2409,18 +2442,34 @@ __global__ __launch_bounds__(kScoreMfmaBlock, 8) void score_mfma_kernel(ScoreArg
   const uint16_t* csp = reinterpret_cast<const uint16_t*>(a.cosets) + base;
   const uint16_t* scp = a.scales + base;
   float* op = a.out + (s * a.Hq + hq0) * a.T + t0;
+  // rows 0 .. nh-1 of the pass, keys t0 .. t0 + nk - 1 (below 2^31 bytes:
+  // T < 2^26 and nh <= 8); dword 3 is the gfx9-family raw buffer format
+  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+      op, 0, (int)(((uint32_t)(nh - 1) * (uint32_t)a.T + (uint32_t)nk) * 4u), 0x00020000);
   const uint32_t cofs = 8u * (uint32_t)kg;
-  for (int kb = 16 * U * wv; kb < nk; kb += 16 * U * nw) {
+  // this lane's table copy, as a byte offset in both 16-bit halves
+  const uint32_t lane_copy = (uint32_t)(lane % kTblCopies) * 8u * 0x00010001u;
+  // codes, coset words and scales of a step's U blocks, in two register
+  // sets used in turn: the next step's loads are in flight while a step
+  // computes, and no register holding a load in flight is copied
+  struct StepData {
     uint2 cw[U];
     uint32_t cs[U], sc[U];
+  };
+  auto load_step = [&](int kb_, StepData& d) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint32_t t = (uint32_t)min(kb + 16 * u + col, nk - 1);
-      cw[u] = *reinterpret_cast<const uint2*>(cp + (t * (uint32_t)(N / 4) + cofs));
-      cs[u] = CMP ? 0u : (uint32_t)csp[t];
-      sc[u] = scp[t];
+      const uint32_t t = (uint32_t)min(kb_ + 16 * u + col, nk - 1);
+      d.cw[u] = *reinterpret_cast<const uint2*>(cp + (t * (uint32_t)(N / 4) + cofs));
+      d.cs[u] = CMP ? 0u : (uint32_t)csp[t];
+      d.sc[u] = scp[t];
     }
-    float v[U][4];
+  };
+  auto compute_step = [&](int kb, const StepData& sd) {
+    const uint2* cw = sd.cw;
+    const uint32_t* cs = sd.cs;
+    const uint32_t* sc = sd.sc;
+    float v[U][2];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       uint32_t w[2] = {cw[u].x, cw[u].y};
@@ -2446,51 +2495,50 @@ __global__ __launch_bounds__(kScoreMfmaBlock, 8) void score_mfma_kernel(ScoreArg
                                  : (0x04010400u + 0x01000100u * (uint32_t)b +
                                     ((b & 1) ? 0x00020002u : 0u));
         const uint32_t ix = __builtin_amdgcn_perm(cc[b >> 1], w[b >> 1], sel);
-        const uint32_t ad = (ix << 3) & 0xfff8fff8u;
+        // entries ix.lo and ix.hi (< 512 each) of this lane's copy: byte
+        // offsets (ix * kTblCopies + copy) * 8 in the two 16-bit halves
+        const uint32_t ad = (ix << 7) | lane_copy;
         const uint2 e0 = *reinterpret_cast<const uint2*>(tb + (ad & 0xffffu));
         const uint2 e1 = *reinterpret_cast<const uint2*>(tb + (ad >> 16));
         const nq_u4 bv = {e0.x, e0.y, e1.x, e1.y};
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[b], __builtin_bit_cast(nq_bf16x8, bv),
                                                       acc, 0, 0, 0);
       }
+      // rows 4 kg .. 4 kg + 3: (head 2 kg hi, lo, head 2 kg + 1 hi, lo)
       const float f = h2f((uint16_t)sc[u]) * a.inv_sqrt_n;
+      v[u][0] = (acc[0] + acc[1]) * f;
+      v[u][1] = (acc[2] + acc[3]) * f;
+    }
+    // Stores through a buffer resource: every lane issues them, and a lane
+    // with nothing to store (tail key, or head beyond nh) gets an offset past
+    // the resource's range, which the hardware drops.  No store sits behind
+    // a branch, so the waits for the next step's loads need not wait for
+    // these stores.
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        // hi + lo parts: rows 0..3 + 4..7 sit 16 lanes apart (lane rows
-        // swapped pairwise), rows 0..7 + 8..15 32 lanes apart (halves swapped)
-        uint32_t s0, s1;
-        if (W8) {
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[r]),
-                                                           __float_as_uint(acc[r]), false, false);
-          s0 = sw[0];
-          s1 = sw[1];
-        } else {
-          const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[r]),
-                                                           __float_as_uint(acc[r]), false, false);
-          s0 = sw[0];
-          s1 = sw[1];
-        }
-        v[u][r] = (__uint_as_float(s0) + __uint_as_float(s1)) * f;
+    for (int u = 0; u < U; ++u) {
+      const int t = kb + 16 * u + col;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int head = 2 * kg + j;
+        const bool ok = t < nk && head < nh;
+        const uint32_t off = ok ? ((uint32_t)head * (uint32_t)a.T + (uint32_t)t) * 4u : 0xFFFFFFFCu;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[u][j]), orsrc, (int)off, 0, 0);
       }
     }
-    // Up to 4 heads: lane rows 0 and 1 hold the same sums, and each stores
-    // one of two adjacent 16-key blocks (a store covers 32 consecutive keys).
-    // 5..8 heads: lane rows 0 and 2 hold heads 0..3, rows 1 and 3 heads 4..7;
-    // rows 0, 1 store the first block, rows 2, 3 the second.
-#pragma unroll
-    for (int u = 0; u < U; u += 2) {
-      const int blk = W8 ? (kg >> 1) : kg;
-      const int h0 = W8 ? 4 * (kg & 1) : 0;
-      const int t = kb + 16 * (u + blk) + col;
-      const uint32_t m1 = 0u - (uint32_t)(blk & 1);      // bit select, no indexing
-      if ((W8 || kg < 2) && t < nk) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t x = (__float_as_uint(v[u + 1][r]) & m1) | (__float_as_uint(v[u][r]) & ~m1);
-          if (h0 + r < nh) (op + (h0 + r) * a.T)[(uint32_t)t] = __uint_as_float(x);
-        }
-      }
-    }
+  };
+  const int kstep = 16 * U * nw;
+  StepData d0, d1;
+  int kb = 16 * U * wv;
+  if (kb < nk) load_step(kb, d0);
+  // the scheduling barriers keep the prefetch loads ahead of the step's work
+  for (; kb < nk; kb += 2 * kstep) {
+    load_step(min(kb + kstep, nk - 1), d1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_step(kb, d0);
+    if (kb + kstep >= nk) break;
+    load_step(min(kb + 2 * kstep, nk - 1), d0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_step(kb + kstep, d1);
   }
 }
 
@@ -2810,7 +2858,7 @@ hipError_t dequantize_tw_launch(const TensorArgs& a, hipStream_t s) {
 }
 
 // 16 tokens per wave, kDmChunk (slab, head) planes per wave, tile-fastest.
-inline hipError_t dequantize_mfma_launch(const TensorArgs& a, hipStream_t s) {
+inline hipError_t dequantize_mfma_launch(const TensorArgs& a, const RopeFreqs& f, hipStream_t s) {
   const int64_t SH = a.n_vec / a.T;
   const int64_t n_tt = (a.T + 15) / 16;
   const int chunk = (int)(SH < kDmChunk ? SH : kDmChunk);
@@ -2818,21 +2866,25 @@ inline hipError_t dequantize_mfma_launch(const TensorArgs& a, hipStream_t s) {
   const int64_t blocks = ((waves + kBlock / 64 - 1) / (kBlock / 64) + 7) / 8 * 8;
   if (a.compact)
     hipLaunchKernelGGL((dequantize_mfma_kernel<true>), dim3((unsigned)blocks), dim3(kBlock), 0, s,
-                       a, chunk);
+                       a, chunk, f);
   else
     hipLaunchKernelGGL((dequantize_mfma_kernel<false>), dim3((unsigned)blocks), dim3(kBlock), 0, s,
-                       a, chunk);
+                       a, chunk, f);
   return hipGetLastError();
 }
 
+// Keys with RoPE that the matrix-core kernel dequantizes, forming its own
+// cos / sin rows: d = n = 128, 2 bits, one scale per vector, fp16 output, and
+// per-lane byte offsets that fit 32 bits in the dense and packed planes.
+bool forms_rope_rows(const TensorArgs& a, int out_dtype) {
+  return out_dtype == 0 && a.n == 128 && a.bits == 2 && a.d == 128 && a.n_scales == 1 &&
+         max64(a.T, a.pT) * 256 < ((int64_t)1 << 31);
+}
+
 template <int N, int BITS, typename T>
-hipError_t dequantize_n(const TensorArgs& a, hipStream_t s) {
+hipError_t dequantize_n(const TensorArgs& a, const RopeFreqs* f, hipStream_t s) {
   if constexpr (N == 128 && BITS == 2 && std::is_same<T, __half>::value) {
-    // keys with RoPE; per-lane byte offsets are 32-bit, in the dense planes
-    // and the packed ones
-    if (a.rope != nullptr && a.d == 128 && a.n_scales == 1 &&
-        max64(a.T, a.pT) * 256 < ((int64_t)1 << 31))
-      return dequantize_mfma_launch(a, s);
+    if (f != nullptr && forms_rope_rows(a, 0)) return dequantize_mfma_launch(a, *f, s);
   }
   if constexpr ((N == 64 || N == 128) && (N * BITS / 8) % 16 == 0) {
     if (a.rope == nullptr) return dequantize_tw_launch<N, BITS, T>(a, s);
@@ -2991,9 +3043,9 @@ hipError_t quantize_t(const TensorArgs& a, hipStream_t s) {
 }
 
 template <typename T>
-hipError_t dequantize_t(const TensorArgs& a, hipStream_t s) {
-  if (a.bits == 2) { NQ_DISPATCH_N(a.n, dequantize_n, 2, T, a, s) }
-  if (a.bits == 3) { NQ_DISPATCH_N(a.n, dequantize_n, 3, T, a, s) }
+hipError_t dequantize_t(const TensorArgs& a, const RopeFreqs* f, hipStream_t s) {
+  if (a.bits == 2) { NQ_DISPATCH_N(a.n, dequantize_n, 2, T, a, f, s) }
+  if (a.bits == 3) { NQ_DISPATCH_N(a.n, dequantize_n, 3, T, a, f, s) }
   return hipErrorInvalidValue;
 }
 
@@ -3123,8 +3175,13 @@ hipError_t launch_quantize(const TensorArgs& a, int in_dtype, hipStream_t s) {
   return in_dtype == 0 ? quantize_t<__half>(a, s) : quantize_t<float>(a, s);
 }
 
-hipError_t launch_dequantize(const TensorArgs& a, int out_dtype, hipStream_t s) {
-  return out_dtype == 0 ? dequantize_t<__half>(a, s) : dequantize_t<float>(a, s);
+bool dequantize_forms_rope_rows(const TensorArgs& a, int out_dtype) {
+  return forms_rope_rows(a, out_dtype);
+}
+
+hipError_t launch_dequantize(const TensorArgs& a, int out_dtype, const RopeFreqs* f,
+                             hipStream_t s) {
+  return out_dtype == 0 ? dequantize_t<__half>(a, f, s) : dequantize_t<float>(a, f, s);
 }
 
 hipError_t launch_score(const ScoreArgs& a, int in_dtype, hipStream_t s) {
