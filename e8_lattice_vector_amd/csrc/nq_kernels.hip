@@ -2188,7 +2188,7 @@ __device__ __forceinline__ void value_table(uint2* tbl) {
 // r + 16 only, so of the 32 lanes one ds_read_b64 pass serves, at most two
 // can contend for a bank pair (about 2.3x fewer conflict stalls than random
 // lookups in one copy, measured).
-constexpr int kTblCopies = 16;
+constexpr int kTblCopies = 16;    // copies for the register-streamed scorer
 // Entry e of the value table: the bf16 of idx - 2 + c/2 for the 4
 // coordinates of code byte e & 255 with coset bit e >> 8.
 __device__ __forceinline__ uint2 value_entry(int e) {
@@ -2202,14 +2202,16 @@ __device__ __forceinline__ uint2 value_entry(int e) {
   }
   return make_uint2(w[0], w[1]);
 }
-// Copy 0 is computed (one entry per thread), then replicated by every thread
+// The table in TC copies, entry e of copy r at index e * TC + r.  Copy 0 is
+// computed (one entry per thread), then replicated by every thread
 // (neighbouring lanes write neighbouring copies of one entry).  Ends with a
 // barrier.
+template <int TC>
 __device__ __forceinline__ void value_table_copies(uint2* tbl) {
-  for (int e = threadIdx.x; e < 512; e += blockDim.x) tbl[e * kTblCopies] = value_entry(e);
+  for (int e = threadIdx.x; e < 512; e += blockDim.x) tbl[e * TC] = value_entry(e);
   __syncthreads();
-  for (int i = threadIdx.x; i < 512 * kTblCopies; i += blockDim.x)
-    if (i % kTblCopies != 0) tbl[i] = tbl[i - i % kTblCopies];
+  for (int i = threadIdx.x; i < 512 * TC; i += blockDim.x)
+    if (i % TC != 0) tbl[i] = tbl[i - i % TC];
   __syncthreads();
 }
 
@@ -2353,6 +2355,101 @@ __global__ __launch_bounds__(1024) void attend_mfma4_kernel(AttendArgs a, int n_
   }
 }
 
+// q~ = H pad(q) of the pass's query heads, in place in LDS (qt: HPP rows of
+// 128 floats, filled and followed by a barrier).
+template <int HPP>
+__device__ __forceinline__ void rotate_queries(float* qt) {
+  constexpr int N = 128;
+  for (int hs = 1; hs < N; hs <<= 1) {
+    for (int i = threadIdx.x; i < HPP * (N / 2); i += blockDim.x) {
+      const int hh = i / (N / 2), r = i % (N / 2);
+      const int j = (r / hs) * 2 * hs + (r % hs);
+      const float x0 = qt[hh * N + j], x1 = qt[hh * N + j + hs];
+      qt[hh * N + j] = x0 + x1;
+      qt[hh * N + j + hs] = x0 - x1;
+    }
+    __syncthreads();
+  }
+}
+
+// The A operands of the four 16x16x32 products: lane (row col = lane & 15,
+// k-group kg = lane >> 4) holds coordinates 8 (4 kg + b) .. + 7 of row col,
+// which is head col / 2's hi part (even rows) or lo part (odd rows).
+template <int HPP>
+__device__ __forceinline__ void score_a_operands(const float* qt, int nh, int lane,
+                                                 nq_bf16x8 (&A)[4]) {
+  constexpr int N = 128;
+  const int col = lane & 15, kg = lane >> 4;
+  const int hh = col >> 1;
+  const bool part = (col & 1) != 0;
+  const bool arow = hh < nh;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    nq_u4 av;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      uint32_t pr = 0;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const float v = arow ? qt[hh * N + 8 * (4 * kg + b) + 2 * e + k] : 0.f;
+        const float hi = (float)(__bf16)v;
+        const float x = part ? v - hi : v;
+        const uint32_t bits = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
+        pr |= bits << (16 * k);
+      }
+      av[e] = pr;
+    }
+    A[b] = __builtin_bit_cast(nq_bf16x8, av);
+  }
+}
+
+// One 16-key block: the four products over the key's code words w (8-groups
+// 4 kg .. 4 kg + 3 of key col), cosets cs (the key's coset word), and the
+// scores of heads 2 kg and 2 kg + 1 scaled by f.  TC table copies; lane_copy
+// is the lane's copy as a byte offset in both 16-bit halves.
+template <bool CMP, int TC>
+__device__ __forceinline__ void score_block(const nq_bf16x8 (&A)[4], uint2 cw, uint32_t cs,
+                                            int kg, const char* tb, uint32_t lane_copy, float f,
+                                            float& v0, float& v1) {
+  constexpr int kShift = TC == 16 ? 7 : TC == 8 ? 6 : TC == 4 ? 5 : TC == 2 ? 4 : 3;
+  static_assert((1 << (kShift - 3)) == TC, "TC a power of two up to 16");
+  uint32_t w[2] = {cw.x, cw.y};
+  uint32_t cc[2];
+  if (CMP) {
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+      cc[d] = (w[d] >> 14) & 0x00010001u;
+      const uint32_t p0 = (uint32_t)__builtin_popcount(w[d] & 0x00001555u) & 1u;
+      const uint32_t p1 = (uint32_t)__builtin_popcount(w[d] & 0x15550000u) & 1u;
+      w[d] = (w[d] & ~0x40004000u) | (p0 << 14) | (p1 << 30);
+    }
+  } else {
+    // coset bits of groups 4 kg .. 4 kg + 3 spread to bytes 0..3
+    const uint32_t sp = __umul24((cs >> (4 * kg)) & 15u, 0x00204081u) & 0x01010101u;
+    cc[0] = cc[1] = sp;
+  }
+  nq_f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    // 16-bit halves: table entries (code byte 0 | c << 8), (code byte 1 | c << 8)
+    const uint32_t sel = CMP ? ((b & 1) ? 0x06030602u : 0x04010400u)
+                             : (0x04010400u + 0x01000100u * (uint32_t)b +
+                                ((b & 1) ? 0x00020002u : 0u));
+    const uint32_t ix = __builtin_amdgcn_perm(cc[b >> 1], w[b >> 1], sel);
+    // entries ix.lo and ix.hi (< 512 each) of this lane's copy: byte offsets
+    // (ix * TC + copy) * 8 in the two 16-bit halves
+    const uint32_t ad = (ix << kShift) | lane_copy;
+    const uint2 e0 = *reinterpret_cast<const uint2*>(tb + (ad & 0xffffu));
+    const uint2 e1 = *reinterpret_cast<const uint2*>(tb + (ad >> 16));
+    const nq_u4 bv = {e0.x, e0.y, e1.x, e1.y};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[b], __builtin_bit_cast(nq_bf16x8, bv), acc,
+                                                  0, 0, 0);
+  }
+  // rows 4 kg .. 4 kg + 3: (head 2 kg hi, lo, head 2 kg + 1 hi, lo)
+  v0 = (acc[0] + acc[1]) * f;
+  v1 = (acc[2] + acc[3]) * f;
+}
+
 // ---------------------------------------------------------------------------
 // Packed-key scores on the matrix cores, for 2-bit keys with one scale per
 // vector at n = 128.  With q~ = H pad(q) and p = idx - 2 + c/2,
@@ -2392,47 +2489,18 @@ __global__ __launch_bounds__(kScoreMfmaBlock, 8) void score_mfma_kernel(ScoreArg
   float qv = 0.f;
   if (qi < HPP * N && qi / N < nh && qi % N < a.d)
     qv = Io<QT>::load1(a.q, (s * a.Hq + hq0 + qi / N) * (int64_t)a.d + qi % N);
-  value_table_copies(tbl);
+  value_table_copies<kTblCopies>(tbl);
   if (qi < HPP * N) qt[qi] = qv;
   __syncthreads();
-  for (int hs = 1; hs < N; hs <<= 1) {
-    for (int i = threadIdx.x; i < HPP * (N / 2); i += blockDim.x) {
-      const int hh = i / (N / 2), r = i % (N / 2);
-      const int j = (r / hs) * 2 * hs + (r % hs);
-      const float x0 = qt[hh * N + j], x1 = qt[hh * N + j + hs];
-      qt[hh * N + j] = x0 + x1;
-      qt[hh * N + j + hs] = x0 - x1;
-    }
-    __syncthreads();
-  }
+  rotate_queries<HPP>(qt);
   const int lane = threadIdx.x & 63;
   // wave index in a scalar register: the key loop's control stays uniform
   const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int nw = blockDim.x >> 6;
   const int col = lane & 15;               // key of the block; A row
   const int kg = lane >> 4;                // 8-groups 4 kg .. 4 kg + 3; heads 2 kg, 2 kg + 1
-  const int hh = col >> 1;                 // A row col: head col / 2,
-  const bool part = (col & 1) != 0;        // its lo part on odd rows
-  const bool arow = hh < nh;
   nq_bf16x8 A[4];
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    nq_u4 av;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      uint32_t pr = 0;
-#pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const float v = arow ? qt[hh * N + 8 * (4 * kg + b) + 2 * e + k] : 0.f;
-        const float hi = (float)(__bf16)v;
-        const float x = part ? v - hi : v;
-        const uint32_t bits = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
-        pr |= bits << (16 * k);
-      }
-      av[e] = pr;
-    }
-    A[b] = __builtin_bit_cast(nq_bf16x8, av);
-  }
+  score_a_operands<HPP>(qt, nh, lane, A);
   const char* tb = reinterpret_cast<const char*>(tbl);
   // this workgroup's keys t0 .. t0 + nk - 1 (nk < 2^26: 32-bit offsets)
   const int64_t t0 = (int64_t)blockIdx.x * chunk;
@@ -2471,44 +2539,9 @@ __global__ __launch_bounds__(kScoreMfmaBlock, 8) void score_mfma_kernel(ScoreArg
     const uint32_t* sc = sd.sc;
     float v[U][2];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      uint32_t w[2] = {cw[u].x, cw[u].y};
-      uint32_t cc[2];
-      if (CMP) {
-#pragma unroll
-        for (int d = 0; d < 2; ++d) {
-          cc[d] = (w[d] >> 14) & 0x00010001u;
-          const uint32_t p0 = (uint32_t)__builtin_popcount(w[d] & 0x00001555u) & 1u;
-          const uint32_t p1 = (uint32_t)__builtin_popcount(w[d] & 0x15550000u) & 1u;
-          w[d] = (w[d] & ~0x40004000u) | (p0 << 14) | (p1 << 30);
-        }
-      } else {
-        // coset bits of groups 4 kg .. 4 kg + 3 spread to bytes 0..3
-        const uint32_t sp = __umul24((cs[u] >> (4 * kg)) & 15u, 0x00204081u) & 0x01010101u;
-        cc[0] = cc[1] = sp;
-      }
-      nq_f4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        // 16-bit halves: table entries (code byte 0 | c << 8), (code byte 1 | c << 8)
-        const uint32_t sel = CMP ? ((b & 1) ? 0x06030602u : 0x04010400u)
-                                 : (0x04010400u + 0x01000100u * (uint32_t)b +
-                                    ((b & 1) ? 0x00020002u : 0u));
-        const uint32_t ix = __builtin_amdgcn_perm(cc[b >> 1], w[b >> 1], sel);
-        // entries ix.lo and ix.hi (< 512 each) of this lane's copy: byte
-        // offsets (ix * kTblCopies + copy) * 8 in the two 16-bit halves
-        const uint32_t ad = (ix << 7) | lane_copy;
-        const uint2 e0 = *reinterpret_cast<const uint2*>(tb + (ad & 0xffffu));
-        const uint2 e1 = *reinterpret_cast<const uint2*>(tb + (ad >> 16));
-        const nq_u4 bv = {e0.x, e0.y, e1.x, e1.y};
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[b], __builtin_bit_cast(nq_bf16x8, bv),
-                                                      acc, 0, 0, 0);
-      }
-      // rows 4 kg .. 4 kg + 3: (head 2 kg hi, lo, head 2 kg + 1 hi, lo)
-      const float f = h2f((uint16_t)sc[u]) * a.inv_sqrt_n;
-      v[u][0] = (acc[0] + acc[1]) * f;
-      v[u][1] = (acc[2] + acc[3]) * f;
-    }
+    for (int u = 0; u < U; ++u)
+      score_block<CMP, kTblCopies>(A, cw[u], cs[u], kg, tb, lane_copy,
+                                   h2f((uint16_t)sc[u]) * a.inv_sqrt_n, v[u][0], v[u][1]);
     // Stores through a buffer resource: every lane issues them, and a lane
     // with nothing to store (tail key, or head beyond nh) gets an offset past
     // the resource's range, which the hardware drops.  No store sits behind
