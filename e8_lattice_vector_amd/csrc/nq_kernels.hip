@@ -854,7 +854,8 @@ __global__ __launch_bounds__(kBlock) void quantize_pair_kernel(TensorArgs a, int
 
 // ---------------------------------------------------------------------------
 // Quantize with the rotation on the matrix cores: vectors without RoPE
-// (values, or keys when no RoPE is removed), d = n = 128, 2-bit codes, one
+// (values, or keys when no RoPE is removed), n = 128 with d = 128 or 96 (the
+// lanes of the padding coordinates feed zeros), 2-bit codes, one
 // scale per vector, fp16 input.
 //
 // The Walsh-Hadamard product u = H x of 16 vectors is a 128 x 128 by
@@ -914,10 +915,14 @@ __global__ __launch_bounds__(kBlock) void quantize_mfma_kernel(TensorArgs a, int
   }
   const float kr = a.half_L * 2.f;  // the 2-bit decoder works on g = 2y
 
-  const uint32_t off_x = (uint32_t)(tc * 256) + 64u * (uint32_t)p;
+  // input rows of d fp16 (d = 96 or 128): lane p feeds coordinates
+  // 32p .. 32p+31, zeros (no load) where they are padding
+  const int row_x = 2 * a.d;
+  const bool data_lane = 32 * p < a.d;
+  const uint32_t off_x = (uint32_t)(tc * row_x) + 64u * (uint32_t)p;
   const uint32_t off_c = (uint32_t)(tc * a.code_bytes) + 8u * (uint32_t)p;
   const uint32_t off_s = (uint32_t)(tc * a.coset_bytes);
-  const int64_t plane_x = a.T * 256;
+  const int64_t plane_x = a.T * row_x;
   const int64_t plane_c = a.pT * a.code_bytes;
   const int64_t plane_s = a.pT * a.coset_bytes;
   const int64_t plane_g = a.pT;  // one fp16 scale per vector
@@ -929,16 +934,18 @@ __global__ __launch_bounds__(kBlock) void quantize_mfma_kernel(TensorArgs a, int
   char* gb = reinterpret_cast<char*>(a.scales) + sh0 * plane_g * 2;
   uint32_t ox = off_x, oc = off_c, os = off_s;
   float keep = 0.f;
-  // the next plane's input is in flight while one is decoded
+  // the next plane's input is in flight while one is decoded (zeros on
+  // padding lanes)
   uint4 nxt[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) nxt[k] = *reinterpret_cast<const uint4*>(xb + ox + 16 * k);
+  for (int k = 0; k < 4; ++k)
+    nxt[k] = data_lane ? *reinterpret_cast<const uint4*>(xb + ox + 16 * k) : make_uint4(0, 0, 0, 0);
   for (int it = 0; it < n_it; ++it, xb += plane_x, cb += plane_c, qb += plane_s) {
     asm volatile("" : "+v"(ox), "+v"(oc), "+v"(os));
     uint4 raw[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) raw[k] = nxt[k];
-    if (it + 1 < n_it) {
+    if (it + 1 < n_it && data_lane) {
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         nxt[k] = *reinterpret_cast<const uint4*>(xb + plane_x + ox + 16 * k);
@@ -2831,7 +2838,8 @@ hipError_t quantize_n(const TensorArgs& a, hipStream_t s) {
     // per-lane byte offsets are 32-bit, in the dense planes and the packed ones
     if (max64(a.T, a.pT) * a.d * (int64_t)sizeof(T) < ((int64_t)1 << 31)) {
       if constexpr (N == 128 && BITS == 2 && std::is_same<T, __half>::value) {
-        if (a.d == 128 && a.n_scales == 1 && a.rope == nullptr)
+        // d = 128, or 96 (padded to 128: the last lane quarter feeds zeros)
+        if ((a.d == 128 || a.d == 96) && a.n_scales == 1 && a.rope == nullptr)
           return a.strict ? quantize_mfma_launch<true>(a, s) : quantize_mfma_launch<false>(a, s);
       }
       if constexpr (N == 128 && std::is_same<T, __half>::value) {
