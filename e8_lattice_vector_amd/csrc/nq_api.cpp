@@ -256,12 +256,15 @@ int quantize_impl(const nq_config* cfg, const void* k, const void* v, int64_t S,
   } else if (nq::launch_clear_counters(counters, 2, s) != hipSuccess) {
     return NQ_ERR_HIP;
   }
-  // each tensor: the fp32 kernel (which queues near-tie vectors), then the
-  // fp64 pass over the queue; with cfg->exact every vector takes the fp64 pass
+  // each tensor's fp32 kernel (which queues near-tie vectors), then the fp64
+  // pass over the queues, one launch for both tensors when they share bits;
+  // with cfg->exact every vector takes the fp64 pass
+  nq::TensorArgs args[2];
   for (int is_v = 0; is_v < 2; ++is_v) {
     const void* x = is_v ? v : k;
     if (x == nullptr) continue;
-    nq::TensorArgs a = tensor_args(cfg, layout(cfg, is_v), S, H, T, is_v ? pv : pk);
+    nq::TensorArgs& a = args[is_v];
+    a = tensor_args(cfg, layout(cfg, is_v), S, H, T, is_v ? pv : pk);
     a.x = x;
     a.rope = is_v ? nullptr : rope;
     a.omega = is_v ? nullptr : omega;
@@ -271,7 +274,16 @@ int quantize_impl(const nq_config* cfg, const void* k, const void* v, int64_t S,
     a.queue = reinterpret_cast<int64_t*>(wb + (is_v ? w.queue_v : w.queue_k));
     a.queue_cap = w.queue_cap;
     if (!cfg->exact && nq::launch_quantize(a, cfg->in_dtype, s) != hipSuccess) return NQ_ERR_HIP;
-    if (nq::launch_exact(a, cfg->in_dtype, cfg->exact, s) != hipSuccess) return NQ_ERR_HIP;
+  }
+  if (k != nullptr && v != nullptr && args[0].bits == args[1].bits) {
+    if (nq::launch_exact2(args[0], args[1], cfg->in_dtype, cfg->exact, s) != hipSuccess)
+      return NQ_ERR_HIP;
+  } else {
+    for (int is_v = 0; is_v < 2; ++is_v) {
+      if ((is_v ? v : k) == nullptr) continue;
+      if (nq::launch_exact(args[is_v], cfg->in_dtype, cfg->exact, s) != hipSuccess)
+        return NQ_ERR_HIP;
+    }
   }
   return NQ_OK;
 }

@@ -109,15 +109,16 @@ __device__ void e8_decode_int(const int64_t N[8], const int neg[8], int64_t A, u
 
 // One vector per VL = n/8 lanes (lane m holds coordinates 8m .. 8m+7 of the
 // padded vector), 64/VL vectors per wave, a grid-stride loop over the items.
+// The pass over one tensor by `nblocks` blocks, this being block `block`.
 template <int N, int BITS, bool STRICT, typename InT>
-__global__ __launch_bounds__(kExBlock) void exact_kernel(TensorArgs a, int all) {
+__device__ __forceinline__ void exact_body(TensorArgs a, int all, int block, int nblocks) {
   constexpr int VL = N / 8;
   constexpr int VPW = 64 / VL;
   const int lane = threadIdx.x & 63;
   const int m = lane % VL;
   const int row = lane / VL;
-  const int64_t n_waves = (int64_t)gridDim.x * (kExBlock / 64);
-  const int64_t wave = (int64_t)blockIdx.x * (kExBlock / 64) + (threadIdx.x >> 6);
+  const int64_t n_waves = (int64_t)nblocks * (kExBlock / 64);
+  const int64_t wave = (int64_t)block * (kExBlock / 64) + (threadIdx.x >> 6);
   const unsigned long long cnt = all ? 0ull : *a.queue_count;
   const bool every = all || cnt > (unsigned long long)a.queue_cap;
   const int64_t items = every ? a.n_vec : (int64_t)cnt;
@@ -231,8 +232,23 @@ __global__ __launch_bounds__(kExBlock) void exact_kernel(TensorArgs a, int all) 
   }
 }
 
-template <int N, int BITS, typename T>
-hipError_t exact_n(const TensorArgs& a, int all, hipStream_t s) {
+template <int N, int BITS, bool STRICT, typename InT>
+__global__ __launch_bounds__(kExBlock) void exact_kernel(TensorArgs a, int all) {
+  exact_body<N, BITS, STRICT, InT>(a, all, blockIdx.x, gridDim.x);
+}
+
+// Both tensors of a call in one launch (the same n, bits and parity): blocks
+// 0 .. nk - 1 take the keys, the rest the values.
+template <int N, int BITS, bool STRICT, typename InT>
+__global__ __launch_bounds__(kExBlock) void exact_kernel2(TensorArgs ak, TensorArgs av, int all,
+                                                          int nk) {
+  const bool keys = (int)blockIdx.x < nk;
+  exact_body<N, BITS, STRICT, InT>(keys ? ak : av, all, keys ? (int)blockIdx.x : (int)blockIdx.x - nk,
+                                   keys ? nk : (int)gridDim.x - nk);
+}
+
+template <int N>
+int64_t exact_blocks(const TensorArgs& a, int all) {
   constexpr int VPB = kExBlock / (N / 8);
   // the queue holds about 1/32 of the vectors and ~1.5e-3 of random vectors
   // are queued: a grid of up to 2048 blocks takes them in one sweep, the
@@ -243,6 +259,23 @@ hipError_t exact_n(const TensorArgs& a, int all, hipStream_t s) {
   const int64_t cap = all ? 65536 : 2048;
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
+  return blocks;
+}
+
+template <int N, int BITS, typename T>
+hipError_t exact_n2(const TensorArgs& ak, const TensorArgs& av, int all, hipStream_t s) {
+  const int64_t bk = exact_blocks<N>(ak, all), bv = exact_blocks<N>(av, all);
+  const dim3 g((unsigned)(bk + bv)), b(kExBlock);
+  if (ak.strict)
+    hipLaunchKernelGGL((exact_kernel2<N, BITS, true, T>), g, b, 0, s, ak, av, all, (int)bk);
+  else
+    hipLaunchKernelGGL((exact_kernel2<N, BITS, false, T>), g, b, 0, s, ak, av, all, (int)bk);
+  return hipGetLastError();
+}
+
+template <int N, int BITS, typename T>
+hipError_t exact_n(const TensorArgs& a, int all, hipStream_t s) {
+  const int64_t blocks = exact_blocks<N>(a, all);
   if (a.strict)
     hipLaunchKernelGGL((exact_kernel<N, BITS, true, T>), dim3((unsigned)blocks), dim3(kExBlock),
                        0, s, a, all);
@@ -270,6 +303,19 @@ hipError_t exact_t(const TensorArgs& a, int all, hipStream_t s) {
   if (a.bits == 2) return exact_b<2, T>(a, all, s);
   if (a.bits == 3) return exact_b<3, T>(a, all, s);
   return hipErrorInvalidValue;
+}
+
+template <int BITS, typename T>
+hipError_t exact_b2(const TensorArgs& ak, const TensorArgs& av, int all, hipStream_t s) {
+  switch (ak.n) {
+    case 8: return exact_n2<8, BITS, T>(ak, av, all, s);
+    case 16: return exact_n2<16, BITS, T>(ak, av, all, s);
+    case 32: return exact_n2<32, BITS, T>(ak, av, all, s);
+    case 64: return exact_n2<64, BITS, T>(ak, av, all, s);
+    case 128: return exact_n2<128, BITS, T>(ak, av, all, s);
+    case 256: return exact_n2<256, BITS, T>(ak, av, all, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 __global__ __launch_bounds__(kExBlock) void rope_table_kernel(
@@ -396,6 +442,16 @@ __global__ __launch_bounds__(kExBlock) void decode_debug_kernel(
 
 hipError_t launch_exact(const TensorArgs& a, int in_dtype, int all, hipStream_t s) {
   return in_dtype == 0 ? exact_t<__half>(a, all, s) : exact_t<float>(a, all, s);
+}
+
+hipError_t launch_exact2(const TensorArgs& ak, const TensorArgs& av, int in_dtype, int all,
+                         hipStream_t s) {
+  if (ak.n != av.n || ak.bits != av.bits || ak.strict != av.strict) return hipErrorInvalidValue;
+  if (ak.bits == 2)
+    return in_dtype == 0 ? exact_b2<2, __half>(ak, av, all, s) : exact_b2<2, float>(ak, av, all, s);
+  if (ak.bits == 3)
+    return in_dtype == 0 ? exact_b2<3, __half>(ak, av, all, s) : exact_b2<3, float>(ak, av, all, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_rope_table(const int32_t* positions, int64_t pos0, int64_t T, int d,

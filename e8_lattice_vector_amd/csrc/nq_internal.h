@@ -81,6 +81,10 @@ hipError_t launch_rope_table(const int32_t* positions, int64_t pos0, int64_t T,
 hipError_t launch_clear_counters(unsigned long long* counters, int n, hipStream_t s);
 // The fp64 pass: the queued vectors (all = 0) or every vector (all = 1).
 hipError_t launch_exact(const TensorArgs& a, int in_dtype, int all, hipStream_t s);
+// The fp64 pass over both tensors of a call in one launch (same n, bits and
+// parity).
+hipError_t launch_exact2(const TensorArgs& ak, const TensorArgs& av, int in_dtype, int all,
+                         hipStream_t s);
 hipError_t launch_quantize(const TensorArgs& a, int in_dtype, hipStream_t s);
 // The body of nq_quantize_kv (argument checks, launches) on a given workspace.
 int quantize_impl(const nq_config* cfg, const void* k, const void* v, int64_t S, int32_t H,
