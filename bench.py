@@ -397,7 +397,7 @@ def main():
         "kernels_ms_median": {"quantize_kv (K and V in one call)": tq,
                               "quantize_k alone (rope table, fp32 kernel, fp64 pass)": tk,
                               "quantize_v alone (counter clear, fp32 kernel, fp64 pass)": tv,
-                              "dequantize_kv (rope table, K, V)": tdq,
+                              "dequantize_kv (K, V)": tdq,
                               "score (in the step, after dequantize)": tsc,
                               "score alone (back to back)": tsa},
         "frac_hbm_peak": {"quantize_k": k_bytes / (tk * 1e-3) / 1e9 / HBM_PEAK_GBPS,

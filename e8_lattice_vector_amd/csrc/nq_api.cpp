@@ -205,7 +205,11 @@ double rope_freq(const nq_config* c, int i) {
 // RoPE; in the same launch copies the fp64 frequencies to `omega` and clears
 // the n_counters queue counters at `counters` (each when not null).
 void rope_freqs(const nq_config* c, nq::RopeFreqs* f) {
-  for (int i = 0; i < c->head_dim / 2; ++i) f->omega[i] = rope_freq(c, i);
+  for (int i = 0; i < c->head_dim / 2; ++i) {
+    f->omega[i] = rope_freq(c, i);
+    f->step_c[i] = (float)cos(16.0 * f->omega[i]);
+    f->step_s[i] = (float)sin(16.0 * f->omega[i]);
+  }
 }
 
 int prepare_rope(const nq_config* c, int64_t T, const int32_t* positions, int64_t pos0,

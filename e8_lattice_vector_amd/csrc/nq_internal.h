@@ -69,6 +69,9 @@ struct AttendArgs {
 constexpr int kMaxHalfDim = 128;
 struct RopeFreqs {
   double omega[kMaxHalfDim];  // theta^(-2i/d), computed on the host
+  // cos and sin of 16 omega_i (the angle step of a 16-token tile), rounded
+  // once to fp32 on the host
+  float step_c[kMaxHalfDim], step_s[kMaxHalfDim];
 };
 
 // cos / sin of positions[t] (or pos0 + t when positions is null) times

@@ -40,6 +40,7 @@ __host__ __device__ constexpr int64_t max64(int64_t a, int64_t b) { return a > b
 
 typedef float nq_f2 __attribute__((ext_vector_type(2)));
 typedef float nq_f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t nq_u4 __attribute__((ext_vector_type(4)));
 
 template <typename T>
 struct Io;
@@ -1250,6 +1251,22 @@ __global__ __launch_bounds__(kBlock) void dequantize_fast_kernel(TensorArgs a,
   }
 }
 
+// Copies n >= 1 elements from global memory to a wave-private LDS slice: U
+// loads per lane are issued before any of them is written, so that they
+// are in flight together (a load-then-write loop waits out each one).
+// Lanes past the end copy element n - 1 again, onto itself: no write is
+// conditional, so the compiler cannot sink a load into a branch.
+template <int U, typename E>
+__device__ __forceinline__ void wave_copy(E* l, const E* g, int n, int lane) {
+  for (int b = 0; b < n; b += 64 * U) {
+    E t[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) t[u] = g[min(b + lane + 64 * u, n - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) l[min(b + lane + 64 * u, n - 1)] = t[u];
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Dequantize keys with the rotation on the matrix cores (RoPE, d = n = 128,
 // 2-bit codes, one scale per vector, fp16 output).
@@ -1266,10 +1283,141 @@ __global__ __launch_bounds__(kBlock) void dequantize_fast_kernel(TensorArgs a,
 // per-lane pattern chosen by tau >> 2 times the tile-uniform sign
 // (-1)^((tau & 1)(k & 1) + (tau >> 1 & 1)(k >> 1)).  The fp16 results pass
 // through the wave's LDS tile so that every global store writes 1 KiB of
-// contiguous output.  A wave keeps its 16-token tile (and the tile's cos /
-// sin in registers) while it walks kDmChunk (slab, head) planes; neighbouring
-// waves take neighbouring tiles.
+// contiguous output.  Lane l needs cos / sin of its token at the 16 angles
+// (coordinate mod 64) 4 p0 + 32 p1 + 8 q0 + 16 q1 + r (q, r < 4).
 // ---------------------------------------------------------------------------
+struct DmFrags {
+  nq_f16x8 Ap[2], An[2];   // H's fragments: two per-lane sign patterns, negated
+};
+
+__device__ __forceinline__ DmFrags dm_frags(int v, int p) {
+  DmFrags h;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int par = __builtin_popcount(v & j & 7) + ((v >> 3) & 1) * (p & 1) + q * (p >> 1);
+      h.Ap[q][j] = (par & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
+      h.An[q][j] = (par & 1) ? (_Float16)1.0f : (_Float16)-1.0f;
+    }
+  }
+  return h;
+}
+
+__device__ __forceinline__ int dm_freq(int p, int q, int r) {
+  return 4 * (p & 1) + 32 * (p >> 1) + 8 * (q & 1) + 16 * (q >> 1) + r;
+}
+
+// cos / sin of the lane's 16 angles at position pos (the same values as the
+// RoPE table's).  The frequencies are read 8 at a time before any of them
+// is used, so their loads are in flight together.
+__device__ __forceinline__ void dm_cos_sin(double pos, const RopeFreqs& f, int p,
+                                           float (&rc)[4][4], float (&rn)[4][4]) {
+#pragma unroll
+  for (int q0 = 0; q0 < 4; q0 += 2) {
+    double om[2][4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) om[q][r] = f.omega[dm_freq(p, q0 + q, r)];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) rope_cos_sin(pos, om[q][r], rc[q0 + q][r], rn[q0 + q][r]);
+  }
+}
+
+// A lane's packed words of one token: code word pair (8-groups 4p .. 4p + 3),
+// coset bits, scale bits.
+struct DmMeta {
+  uint2 cw;
+  uint32_t cs, sb;
+};
+
+// Raw buffer (gfx9-family format word) over `bytes` bytes (< 2^31) at p.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t dm_rsrc(char* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, (int)bytes, 0x00020000);
+}
+
+// One 16-token tile of one plane -> 16 rows of 256 B at byte yoff of the
+// buffer yr.  Rows from `rows` on are not stored: their stores take an
+// offset past the buffer's end, which the hardware drops, so no store is
+// conditional and the compiler's wait counts stay exact.
+template <bool CMP>
+__device__ __forceinline__ void dm_tile(const DmFrags& h, const DmMeta& m, float half_rs,
+                                        const float (&rc)[4][4], const float (&rn)[4][4],
+                                        char* tile, int v, int p, __amdgpu_buffer_rsrc_t yr,
+                                        uint32_t yoff, int rows) {
+  nq_f4 acc[8];
+#pragma unroll
+  for (int tau = 0; tau < 8; ++tau) acc[tau] = nq_f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t w = ((k < 2 ? m.cw.x : m.cw.y) >> (16 * (k & 1))) & 0xffffu;
+    int c = (int)((m.cs >> (4 * p + k)) & 1u);
+    if (CMP) w = Compact<2>::unfold(w, c);
+    // fp16 1024 + 2 idx + c for the group's 8 coordinates, two per word
+    const uint32_t base = 0x64006400u | (c ? 0x00010001u : 0u);
+    uint32_t bw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t nib = (w >> (4 * q)) & 0xfu;
+      bw[q] = (((nib | (nib << 14)) & 0x00030003u) << 1) | base;
+    }
+    const nq_f16x8 B = __builtin_bit_cast(nq_f16x8, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+#pragma unroll
+    for (int tau = 0; tau < 8; ++tau) {
+      const bool neg = (((tau & 1) * (k & 1) + ((tau >> 1) & 1) * (k >> 1)) & 1) != 0;
+      acc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(neg ? h.An[tau >> 2] : h.Ap[tau >> 2], B,
+                                                        acc[tau], 0, 0, 0);
+    }
+  }
+  // coordinate 0 (lane p = 0, tile 0, row 0) carries the 1028 * 128 offset
+  if (p == 0) acc[0][0] -= 131584.f;
+  const float f = h2f((uint16_t)m.sb) * half_rs;
+  // per pair of tiles (q, q + 4): scale, RoPE forward (x_i c - x_{i+64} s
+  // in the lower half, x_{i+64} c + x_i s in the upper), fp16 results into
+  // the wave's LDS tile (16 tokens x 256 B; the 16-byte chunks of token row
+  // v rotated by v against bank conflicts)
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    float xl[4], xu[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float lo = acc[q][r] * f, up = acc[q + 4][r] * f;
+      xl[r] = __fmaf_rn(lo, rc[q][r], -(up * rn[q][r]));
+      xu[r] = __fmaf_rn(up, rc[q][r], lo * rn[q][r]);
+    }
+#pragma unroll
+    for (int hi = 0; hi < 2; ++hi) {
+      const float* x = hi ? xu : xl;
+      const int tau = q + 4 * hi;
+      const uint32_t u0 = __builtin_bit_cast(uint32_t, __floats2half2_rn(x[0], x[1]));
+      const uint32_t u1 = __builtin_bit_cast(uint32_t, __floats2half2_rn(x[2], x[3]));
+      // byte 8 p0 + 64 p1 + 16 tau0 + 32 tau1 + 128 tau2 of row v
+      const int ch = 4 * (p >> 1) + (tau & 1) + 2 * ((tau >> 1) & 1) + 8 * (tau >> 2);
+      *reinterpret_cast<uint2*>(tile + v * 256 + ((ch ^ v) << 4) + 8 * (p & 1)) =
+          make_uint2(u0, u1);
+    }
+    // one pair at a time: the scheduler would otherwise form every pair's
+    // products first and hold them all in registers
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    // store i, lane l: token row 4i + p of the tile, 16-byte chunk v
+    const int row = 4 * i + p;
+    const uint4 val = *reinterpret_cast<const uint4*>(tile + row * 256 + ((v ^ row) << 4));
+    const uint32_t off = row < rows ? yoff + 1024u * i + 16u * (16u * p + v) : 0x80000000u;
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(nq_u4, val), yr, (int)off, 0, 0);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Plane-walking form (explicit positions): a wave keeps its 16-token tile
+// (and the tile's cos / sin in registers) while it walks kDmChunk (slab,
+// head) planes; neighbouring waves take neighbouring tiles.
 constexpr int kDmChunk = 32;
 
 template <bool CMP>
@@ -1286,40 +1434,19 @@ __global__ __launch_bounds__(kBlock) void dequantize_mfma_kernel(TensorArgs a, i
   if (sh0 >= SH) return;
   const int64_t sh1 = min64(SH, sh0 + sh_chunk);
   const int64_t t = tt * 16 + v;
-  const bool tvalid = t < a.T;
-  const int64_t tc = tvalid ? t : a.T - 1;
-
-  // H's fragments: the two per-lane sign patterns and their negatives
-  nq_f16x8 Ap[2], An[2];
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int par = __builtin_popcount(v & j & 7) + ((v >> 3) & 1) * (p & 1) + q * (p >> 1);
-      Ap[q][j] = (par & 1) ? (_Float16)-1.0f : (_Float16)1.0f;
-      An[q][j] = (par & 1) ? (_Float16)1.0f : (_Float16)-1.0f;
-    }
-  }
-  // cos / sin of angle (coordinate mod 64) r + 4 p0 + 32 p1 + 8 tau0 + 16 tau1
-  // for this lane's token, formed here once for all the wave's planes (the
-  // same values as the RoPE table's)
+  const int64_t tc = t < a.T ? t : a.T - 1;
+  const DmFrags h = dm_frags(v, p);
+  // this lane's cos / sin, formed once for all the wave's planes (the same
+  // values as the RoPE table's)
   float rc[4][4], rn[4][4];
-  {
-    const double pos = a.positions != nullptr ? (double)a.positions[tc] : (double)(a.pos0 + tc);
-    const int k0 = 4 * (p & 1) + 32 * (p >> 1);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        rope_cos_sin(pos, f.omega[k0 + 8 * (q & 1) + 16 * (q >> 1) + r], rc[q][r], rn[q][r]);
-    }
-  }
+  dm_cos_sin(a.positions != nullptr ? (double)a.positions[tc] : (double)(a.pos0 + tc), f, p, rc,
+             rn);
   const float half_rs = 0.5f * a.inv_sqrt_n;
   const uint32_t off_c = (uint32_t)(tc * a.code_bytes) + 8u * (uint32_t)p;
   const uint32_t off_s = (uint32_t)(tc * a.coset_bytes);
   const uint32_t off_g = (uint32_t)tc * 2u;
-  // output: the tile's 4 KiB stretch, 16 bytes per lane per store
-  const uint32_t off_y = (uint32_t)(tt * 16 * 256) + 16u * (uint32_t)lane;
+  const uint32_t off_y = (uint32_t)(tt * 16 * 256);   // the tile's 4 KiB stretch
+  const int rows = (int)min64(16, a.T - tt * 16);
   __shared__ __align__(16) char lds_tiles[kBlock / 64][16 * 256];
   char* tile = lds_tiles[threadIdx.x >> 6];
   const int64_t plane_y = a.T * 256;
@@ -1331,84 +1458,123 @@ __global__ __launch_bounds__(kBlock) void dequantize_mfma_kernel(TensorArgs a, i
   const uint8_t* cb = a.codes + sh0 * plane_c;
   const uint8_t* qb = a.cosets + sh0 * plane_s;
   const char* gb = reinterpret_cast<const char*>(a.scales) + sh0 * plane_g;
-  uint32_t oc = off_c, os = off_s, og = off_g, oy = off_y;
-  // the next plane's code words, coset word and scale are loaded one ahead
-  auto load_meta = [&](int q, uint2& cw, uint32_t& cs, uint32_t& sb) {
-    cw = *reinterpret_cast<const uint2*>(cb + q * plane_c + oc);
-    cs = CMP ? 0u : (uint32_t)*reinterpret_cast<const uint16_t*>(qb + q * plane_s + os);
-    sb = (uint32_t)*reinterpret_cast<const uint16_t*>(gb + q * plane_g + og);
+  // plane min(it, n_it - 1): the one-ahead load past the last plane reloads it
+  auto load_meta = [&](int it, DmMeta& m) {
+    const int q = min(it, n_it - 1);
+    m.cw = *reinterpret_cast<const uint2*>(cb + q * plane_c + off_c);
+    m.cs = CMP ? 0u : (uint32_t)*reinterpret_cast<const uint16_t*>(qb + q * plane_s + off_s);
+    m.sb = (uint32_t)*reinterpret_cast<const uint16_t*>(gb + q * plane_g + off_g);
   };
-  uint2 cw_n;
-  uint32_t cs_n, sb_n;
-  load_meta(0, cw_n, cs_n, sb_n);
-  for (int it = 0; it < n_it;
-       ++it, yb += plane_y, cb += plane_c, qb += plane_s, gb += plane_g) {
-    asm volatile("" : "+v"(oc), "+v"(os), "+v"(og), "+v"(oy));
-    const uint2 cw = cw_n;
-    const uint32_t cs = cs_n, sbits = sb_n;
-    if (it + 1 < n_it) load_meta(1, cw_n, cs_n, sb_n);
-    nq_f4 acc[8];
-#pragma unroll
-    for (int tau = 0; tau < 8; ++tau) acc[tau] = nq_f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t w = ((k < 2 ? cw.x : cw.y) >> (16 * (k & 1))) & 0xffffu;
-      int c = (int)((cs >> (4 * p + k)) & 1u);
-      if (CMP) w = Compact<2>::unfold(w, c);
-      // fp16 1024 + 2 idx + c for the group's 8 coordinates, two per word
-      const uint32_t base = 0x64006400u | (c ? 0x00010001u : 0u);
-      uint32_t bw[4];
+  auto step = [&](int it, const DmMeta& m) {
+    dm_tile<CMP>(h, m, half_rs, rc, rn, tile, v, p, dm_rsrc(yb + it * plane_y, plane_y), off_y,
+                 rows);
+  };
+  // the next plane's words are loaded one ahead, into two register sets used
+  // in turn, so that no copy of a word still in flight makes the wave wait
+  DmMeta m0, m1;
+  load_meta(0, m0);
+#pragma unroll 1
+  for (int it = 0; it < n_it; it += 2) {
+    load_meta(it + 1, m1);
+    step(it, m0);
+    if (it + 1 >= n_it) break;
+    load_meta(it + 2, m0);
+    step(it + 1, m1);
+  }
+}
+
+// Token-walking form (positions pos0 + t): a wave walks a run of kDtRun
+// tiles of one (slab, head) plane, so each wave writes one contiguous
+// stretch of output (128 KiB).  It copies the packed words of kDtChunk tiles
+// at a time into its LDS slice; the tiles of a chunk then issue no global
+// load, only stores, which therefore never wait for one another (loads and
+// stores in flight together share one wait counter that cannot be waited on
+// in part).  The lane's cos / sin are formed at the run's first tile and
+// rotated by the angle of 16 tokens (host-computed cos / sin of 16 omega)
+// from tile to tile: after at most kDtRun - 1 rotations they are within a
+// few 1e-6 of the directly formed values.
+constexpr int kDtRun = 32;
+constexpr int kDtChunk = 8;
+constexpr int kDtTok = 16 * kDtChunk;   // tokens per chunk
+
+template <bool CMP>
+__global__ __launch_bounds__(kBlock) void dequantize_mfma_tw_kernel(TensorArgs a, RopeFreqs f) {
+  const int lane = threadIdx.x & 63;
+  const int v = lane & 15;
+  const int p = lane >> 4;
+  const int64_t n_tt = (a.T + 15) / 16;
+  const int64_t n_run = (n_tt + kDtRun - 1) / kDtRun;
+  const int64_t SH = a.n_vec / a.T;
+  const int64_t wave = xcd_wave_id();
+  const int64_t sh = wave / n_run;
+  if (sh >= SH) return;                     // whole wave; no block barrier below
+  const int64_t tt0 = (wave % n_run) * kDtRun;
+  const int nt = (int)min64((int64_t)16 * kDtRun, a.T - tt0 * 16);   // tokens of the run
+  const int n_it = (nt + 15) / 16;
+  // the wave's LDS slice: a chunk's code rows (32 B a token), coset words
+  // and scales, then the step's cos / sin for lane group p ([p][0 .. 15]
+  // cos, [p][16 .. 31] sin, in (q, r) order)
+  __shared__ __align__(16) char lds_meta[kBlock / 64][kDtTok * 36 + 512];
+  __shared__ __align__(16) char lds_tiles[kBlock / 64][16 * 256];
+  char* mc = lds_meta[threadIdx.x >> 6];
+  uint16_t* mq = reinterpret_cast<uint16_t*>(mc + kDtTok * 32);
+  uint16_t* mg = mq + kDtTok;
+  float* mst = reinterpret_cast<float*>(mc + kDtTok * 36);
+  char* tile = lds_tiles[threadIdx.x >> 6];
+  {
+    const int k = dm_freq(p, (lane >> 2) & 3, lane & 3);
+    mst[32 * p + (lane & 15)] = f.step_c[k];
+    mst[32 * p + 16 + (lane & 15)] = f.step_s[k];
+  }
+  const DmFrags h = dm_frags(v, p);
+  float rc[4][4], rn[4][4];
+  dm_cos_sin((double)(a.pos0 + tt0 * 16 + v), f, p, rc, rn);
+  const float4* stp = reinterpret_cast<const float4*>(mst + 32 * p);
+  const float half_rs = 0.5f * a.inv_sqrt_n;
+  const __amdgpu_buffer_rsrc_t yr =
+      dm_rsrc(static_cast<char*>(a.y) + (sh * a.T + tt0 * 16) * 256, (int64_t)nt * 256);
+  const int64_t v0 = sh * a.pT + tt0 * 16;
+#pragma unroll 1
+  for (int c0 = 0; c0 < n_it; c0 += kDtChunk) {
+    // the chunk's tokens ct0 .. ct0 + cnt - 1 of the run into the slice (the
+    // previous chunk's reads of it have all returned: their values are used)
+    const int ct0 = 16 * c0;
+    const int cnt = min(kDtTok, nt - ct0);
+    wave_copy<2 * kDtTok / 64>(reinterpret_cast<uint4*>(mc),
+                               reinterpret_cast<const uint4*>(a.codes + (v0 + ct0) * 32),
+                               2 * cnt, lane);
+    if (!CMP)
+      wave_copy<kDtTok / 64>(mq, reinterpret_cast<const uint16_t*>(a.cosets) + v0 + ct0, cnt,
+                             lane);
+    wave_copy<kDtTok / 64>(mg, a.scales + v0 + ct0, cnt, lane);
+    // the slice is written and read by this wave only; the wait makes the
+    // copies visible
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    const int c1 = min(n_it, c0 + kDtChunk);
+#pragma unroll 1
+    for (int it = c0; it < c1; ++it) {
+      const int t = min(16 * it + v, nt - 1) - ct0;   // token within the chunk
+      DmMeta m;
+      m.cw = *reinterpret_cast<const uint2*>(mc + 32 * t + 8 * p);
+      m.cs = CMP ? 0u : (uint32_t)mq[t];
+      m.sb = (uint32_t)mg[t];
+      dm_tile<CMP>(h, m, half_rs, rc, rn, tile, v, p, yr, 4096u * (uint32_t)it,
+                   min(16, nt - 16 * it));
+      // the step's cos / sin are read after the tile, not held through it
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t nib = (w >> (4 * q)) & 0xfu;
-        bw[q] = (((nib | (nib << 14)) & 0x00030003u) << 1) | base;
-      }
-      const nq_f16x8 B = __builtin_bit_cast(nq_f16x8, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+        const float4 dc4 = stp[q], dn4 = stp[4 + q];
+        const float dc[4] = {dc4.x, dc4.y, dc4.z, dc4.w}, dn[4] = {dn4.x, dn4.y, dn4.z, dn4.w};
 #pragma unroll
-      for (int tau = 0; tau < 8; ++tau) {
-        const bool neg = (((tau & 1) * (k & 1) + ((tau >> 1) & 1) * (k >> 1)) & 1) != 0;
-        acc[tau] = __builtin_amdgcn_mfma_f32_16x16x32_f16(neg ? An[tau >> 2] : Ap[tau >> 2], B,
-                                                          acc[tau], 0, 0, 0);
-      }
-    }
-    // coordinate 0 (lane p = 0, tile 0, row 0) carries the 1028 * 128 offset
-    if (p == 0) acc[0][0] -= 131584.f;
-    const float f = h2f((uint16_t)sbits) * half_rs;
-    float x[8][4];
-#pragma unroll
-    for (int tau = 0; tau < 8; ++tau)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x[tau][r] = acc[tau][r] * f;
-    // RoPE forward: x_i c - x_{i+64} s (lower half), x_{i+64} c + x_i s
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float lo = x[q][r], up = x[q + 4][r];
-        x[q][r] = __fmaf_rn(lo, rc[q][r], -(up * rn[q][r]));
-        x[q + 4][r] = __fmaf_rn(up, rc[q][r], lo * rn[q][r]);
+        for (int r = 0; r < 4; ++r) {
+          const float c = rc[q][r], sn = rn[q][r];
+          rc[q][r] = __fmaf_rn(c, dc[r], -(sn * dn[r]));
+          rn[q][r] = __fmaf_rn(sn, dc[r], c * dn[r]);
+        }
       }
     }
-    // fp16 results into the wave's LDS tile (16 tokens x 256 B; the 16-byte
-    // chunks of token row v rotated by v against bank conflicts)
-#pragma unroll
-    for (int tau = 0; tau < 8; ++tau) {
-      const uint32_t u0 = __builtin_bit_cast(uint32_t, __floats2half2_rn(x[tau][0], x[tau][1]));
-      const uint32_t u1 = __builtin_bit_cast(uint32_t, __floats2half2_rn(x[tau][2], x[tau][3]));
-      // byte 8 p0 + 64 p1 + 16 tau0 + 32 tau1 + 128 tau2 of row v
-      const int ch = 4 * (p >> 1) + (tau & 1) + 2 * ((tau >> 1) & 1) + 8 * (tau >> 2);
-      *reinterpret_cast<uint2*>(tile + v * 256 + ((ch ^ v) << 4) + 8 * (p & 1)) =
-          make_uint2(u0, u1);
-    }
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // store i, lane l: token row 4i + p of the tile, 16-byte chunk v
-      const int row = 4 * i + p;
-      const uint4 val = *reinterpret_cast<const uint4*>(tile + row * 256 + ((v ^ row) << 4));
-      if (tt * 16 + row < a.T) *reinterpret_cast<uint4*>(yb + oy + 1024 * i) = val;
-    }
-    __builtin_amdgcn_wave_barrier();
   }
 }
 
@@ -1989,7 +2155,6 @@ __global__ __launch_bounds__((att_block<BITS, HPP>())) void attend_kernel(Attend
 // form further down, which needs fewer instructions per token.
 // ---------------------------------------------------------------------------
 typedef __bf16 nq_bf16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t nq_u4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float i8_to_f(uint32_t x, int byte) {
   return (float)(int)(int8_t)(x >> (8 * byte));
@@ -2902,6 +3067,17 @@ hipError_t dequantize_tw_launch(const TensorArgs& a, hipStream_t s) {
 inline hipError_t dequantize_mfma_launch(const TensorArgs& a, const RopeFreqs& f, hipStream_t s) {
   const int64_t SH = a.n_vec / a.T;
   const int64_t n_tt = (a.T + 15) / 16;
+  if (a.positions == nullptr) {
+    const int64_t waves = SH * ((n_tt + kDtRun - 1) / kDtRun);
+    const int64_t blocks = ((waves + kBlock / 64 - 1) / (kBlock / 64) + 7) / 8 * 8;
+    if (a.compact)
+      hipLaunchKernelGGL((dequantize_mfma_tw_kernel<true>), dim3((unsigned)blocks), dim3(kBlock),
+                         0, s, a, f);
+    else
+      hipLaunchKernelGGL((dequantize_mfma_tw_kernel<false>), dim3((unsigned)blocks), dim3(kBlock),
+                         0, s, a, f);
+    return hipGetLastError();
+  }
   const int chunk = (int)(SH < kDmChunk ? SH : kDmChunk);
   const int64_t waves = n_tt * ((SH + chunk - 1) / chunk);
   const int64_t blocks = ((waves + kBlock / 64 - 1) / (kBlock / 64) + 7) / 8 * 8;

@@ -3,7 +3,8 @@
 A cache filled by a prefill chunk, single-token appends and a multi-token
 chunk, quantized block by block at the cache's end, must hold the same bytes
 as one quantization of the whole prefix, and those bytes match the oracle.
-Reads of a window (score, attend, dequantize) equal reads of a dense copy.
+Reads of a window (score, attend, dequantize) equal reads of a dense copy
+(dequantized keys within one fp16 step).
 """
 
 import numpy as np
@@ -76,7 +77,12 @@ def test_append_matches_one_shot(cfg, block):
     torch.cuda.synchronize()
     assert torch.equal(s_win, s_ref)
     assert torch.equal(o_win, o_ref)
-    assert torch.equal(kd_win, kd_ref) and torch.equal(vd_win, vd_ref)
+    assert torch.equal(vd_win, vd_ref)
+    # keys: the window (positions 100 + t) takes the token-walking kernel,
+    # whose cos / sin are rotated from tile to tile; the dense copy with
+    # explicit positions forms them directly: within one fp16 step
+    kw, kr = kd_win.float(), kd_ref.float()
+    assert ((kw - kr).abs() <= kr.abs() * 2.0 ** -10 + 2.0 ** -24).all()
     # the dequantized window against the oracle (RoPE at positions 100..249)
     codec = oracle_codec(cfg, False)
     codes, cosets, scales = to_np(sub)
