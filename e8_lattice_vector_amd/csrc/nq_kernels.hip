@@ -1103,6 +1103,11 @@ __global__ __launch_bounds__(kBlock) void quantize_kernel(TensorArgs a) {
 
 template <typename T>
 struct OutIo;
+// Dequantized output: written once, read by a later consumer, and far
+// larger than the caches, so the stores are non-temporal (they do not fill
+// the L2 with dirty lines that a following kernel then has to wait behind).
+constexpr int kStoreNT = 2;   // cache-policy bits of a raw buffer store: nt
+
 template <>
 struct OutIo<__half> {
   // fp16 RNE, two values per v_cvt_pk_f16_f32; `flip` xors the sign bits
@@ -1112,8 +1117,8 @@ struct OutIo<__half> {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       u[i] = __builtin_bit_cast(uint32_t, __floats2half2_rn(v[2 * i], v[2 * i + 1])) ^ flip;
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(base) + off) =
-        make_uint4(u[0], u[1], u[2], u[3]);
+    const nq_u4 w = {u[0], u[1], u[2], u[3]};
+    __builtin_nontemporal_store(w, reinterpret_cast<nq_u4*>(static_cast<uint16_t*>(base) + off));
   }
   static constexpr uint32_t kFlip = 0x80008000u;
 };
@@ -1125,7 +1130,9 @@ struct OutIo<float> {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       w[i] = __uint_as_float(__float_as_uint(v[i]) ^ flip);
-    Io<float>::store8(base, off, w);
+    nq_f4* p = reinterpret_cast<nq_f4*>(static_cast<float*>(base) + off);
+    __builtin_nontemporal_store(nq_f4{w[0], w[1], w[2], w[3]}, p);
+    __builtin_nontemporal_store(nq_f4{w[4], w[5], w[6], w[7]}, p + 1);
   }
   static constexpr uint32_t kFlip = 0x80000000u;
 };
@@ -1342,7 +1349,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dm_rsrc(char* p, int64_t bytes
 // One 16-token tile of one plane -> 16 rows of 256 B at byte yoff of the
 // buffer yr.  Rows from `rows` on are not stored: their stores take an
 // offset past the buffer's end, which the hardware drops, so no store is
-// conditional and the compiler's wait counts stay exact.
+// conditional and the compiler's wait counts stay exact.  The stores are
+// non-temporal, as every dequantized output is.
 template <bool CMP>
 __device__ __forceinline__ void dm_tile(const DmFrags& h, const DmMeta& m, float half_rs,
                                         const float (&rc)[4][4], const float (&rn)[4][4],
@@ -1410,7 +1418,8 @@ __device__ __forceinline__ void dm_tile(const DmFrags& h, const DmMeta& m, float
     const int row = 4 * i + p;
     const uint4 val = *reinterpret_cast<const uint4*>(tile + row * 256 + ((v ^ row) << 4));
     const uint32_t off = row < rows ? yoff + 1024u * i + 16u * (16u * p + v) : 0x80000000u;
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(nq_u4, val), yr, (int)off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(nq_u4, val), yr, (int)off, 0,
+                                           kStoreNT);
   }
   __builtin_amdgcn_wave_barrier();
 }
@@ -1711,7 +1720,7 @@ __global__ __launch_bounds__(kBlock) void dequantize_kernel(TensorArgs a) {
   fwht_cross<VL>(v, m);
   if (a.rope != nullptr) rope_lane<false>(v, m, a.d, a.rope + t * (a.d >> 1));
   const int j0 = 8 * m;
-  if (live && j0 < a.d) Io<OutT>::store8(a.y, vec * a.d + j0, v);
+  if (live && j0 < a.d) OutIo<OutT>::store8(a.y, vec * a.d + j0, v, 0u);
 }
 
 // One key per thread; the rotated queries of the GQA group (q~ = H pad(q))
