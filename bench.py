@@ -154,13 +154,22 @@ def cpu_baseline(w, slabs, heads_per_job=1, max_procs=16):
     }
 
 
-def timed(fn, steps, warmup, stream):
+def timed(fn, steps, warmup, stream, min_warm_s=0.05):
     """Median milliseconds of `fn` over `steps` calls (HIP events on the
-    stream the kernels run on), after `warmup` calls."""
+    stream the kernels run on), after `warmup` calls and at least
+    `min_warm_s` seconds of untimed calls: after a change of workload the
+    GPU's clocks settle over tens of milliseconds (a memory-bound kernel
+    timed after 20 short calls ran up to 40 % slower than after 50 ms)."""
     import torch
 
     for _ in range(warmup):
         fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < min_warm_s:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     torch.cuda.synchronize()
     for e in ev:

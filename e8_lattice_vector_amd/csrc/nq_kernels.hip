@@ -2351,26 +2351,16 @@ __global__ __launch_bounds__(1024) void attend_mfma_kernel(AttendArgs a, int n_p
   }
 }
 
-// The 2-bit code values of one byte as bf16: entry c * 256 + byte holds
-// idx - 2 + c/2 for the byte's 4 coordinates (exact in bf16), low
-// coordinate first.  Written by the whole workgroup; a barrier must follow.
-__device__ __forceinline__ void value_table(uint2* tbl) {
-  uint32_t* tw = reinterpret_cast<uint32_t*>(tbl);
-  for (int i = threadIdx.x; i < 1024; i += blockDim.x) {
-    const int c = i >> 9, byte = (i >> 1) & 255, f = 4 * (i & 1);
-    const float lo = (float)((byte >> f) & 3) - 2.f + 0.5f * (float)c;
-    const float hi = (float)((byte >> (f + 2)) & 3) - 2.f + 0.5f * (float)c;
-    tw[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
-  }
-}
 
-// The same table in kTblCopies copies, entry e of copy r at uint2 index
-// e * kTblCopies + r: lane l reads copy l % kTblCopies.  On gfx950's 64
+// The 2-bit code values of one byte as bf16 (entry c * 256 + byte holds
+// idx - 2 + c/2 for the byte's 4 coordinates, exact in bf16, low coordinate
+// first), in kTblCopies copies: entry e of copy r at uint2 index
+// e * kTblCopies + r, and lane l reads copy l % kTblCopies.  On gfx950's 64
 // four-byte LDS banks an 8-byte entry of copy r then sits in bank pair r or
 // r + 16 only, so of the 32 lanes one ds_read_b64 pass serves, at most two
 // can contend for a bank pair (about 2.3x fewer conflict stalls than random
 // lookups in one copy, measured).
-constexpr int kTblCopies = 16;    // copies for the register-streamed scorer
+constexpr int kTblCopies = 16;    // copies for the scorer and the attention kernels
 // Entry e of the value table: the bf16 of idx - 2 + c/2 for the 4
 // coordinates of code byte e & 255 with coset bit e >> 8.
 __device__ __forceinline__ uint2 value_entry(int e) {
@@ -2404,11 +2394,15 @@ __device__ __forceinline__ void value_table_copies(uint2* tbl) {
 // operand words directly.  Column g of block b holds coordinates 8 g + 2 b
 // (sub 0) and 8 g + 2 b + 1 (sub 1); the A row of sub 0 carries the weight in
 // the low bf16 of each pair and 0 in the high one, sub 1 the reverse.
-template <bool CMP>
+template <bool CMP, int TC>
 __device__ __forceinline__ void att_mma4(nq_f4 (&acc)[4], const AttChunk& k,
                                          const uint2* __restrict__ tbl, int col,
                                          uint32_t pmask, uint32_t asel) {
+  static_assert(TC == 1 || TC == 16, "table copies");
   const char* tb = reinterpret_cast<const char*>(tbl);
+  // this lane's table copy (entry e of copy r at byte 8 (TC e + r)), as a
+  // byte offset in both 16-bit halves
+  const uint32_t lane_copy = (uint32_t)((threadIdx.x & 63) % TC) * 8u * 0x00010001u;
 #pragma unroll
   for (int hc = 0; hc < 2; ++hc) {
     nq_u4 av;
@@ -2434,7 +2428,8 @@ __device__ __forceinline__ void att_mma4(nq_f4 (&acc)[4], const AttChunk& k,
         av[j] = __builtin_amdgcn_perm(__float_as_uint(x), __float_as_uint(x), asel);
         // 16-bit halves: table indices (code byte 0 | c << 8), (code byte 1 | c << 8)
         const uint32_t ix = __builtin_amdgcn_perm(cc, cw, e ? 0x06030602u : 0x04010400u);
-        const uint32_t ad = ((ix << 3) & 0xfff8fff8u);
+        const uint32_t ad = TC == 1 ? ((ix << 3) & 0xfff8fff8u)
+                                    : (((ix << 7) & 0xff80ff80u) | lane_copy);
         const uint2 e0 = *reinterpret_cast<const uint2*>(tb + (ad & 0xffffu));
         const uint2 e1 = *reinterpret_cast<const uint2*>(tb + (ad >> 16));
         bw[0][j] = e0.x;
@@ -2459,8 +2454,8 @@ __global__ __launch_bounds__(1024) void attend_mfma4_kernel(AttendArgs a, int n_
   constexpr int N = 128;
   constexpr int U = 2;                     // chunks of 32 tokens per wave per step
   extern __shared__ float red[];           // [n_waves][HPP][N]
-  __shared__ uint2 tbl[512];               // entry c * 256 + code byte
-  value_table(tbl);
+  __shared__ uint2 tbl[512 * kTblCopies];  // entry c * 256 + code byte, kTblCopies copies
+  value_table_copies<kTblCopies>(tbl);
   const int64_t s = blockIdx.z;
   const int h = blockIdx.y / n_pass;
   const int pass = blockIdx.y % n_pass;
@@ -2501,7 +2496,7 @@ __global__ __launch_bounds__(1024) void attend_mfma4_kernel(AttendArgs a, int n_
         att_load<false, CMP>(k[u], cp, csp, scp, wr, c0 + u * step + 8 * kg, T, arow);
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) att_mma4<CMP>(acc, k[u], tbl, col, pmask, asel);
+    for (int u = 0; u < U; ++u) att_mma4<CMP, kTblCopies>(acc, k[u], tbl, col, pmask, asel);
   }
   // rows 4..7 / 12..15 (lanes 16..31 / 48..63) hold the low parts of rows
   // 0..3 / 8..11 (lanes 0..15 / 32..47); lanes 0..15 have sub 0, 32..47 sub 1
@@ -2767,7 +2762,7 @@ __global__ __launch_bounds__(kScoreMfmaBlock, 8) void score_mfma_kernel(ScoreArg
 // before a chunk's use counts the loads issued after it; no other vector
 // memory operation is issued inside the loop.
 // ---------------------------------------------------------------------------
-constexpr int kAttStages = 4;
+constexpr int kAttStages = 3;
 constexpr int kAttStage = 1664;           // bytes per stage
 
 // token -> 32-byte slot of the stage's code area
@@ -2790,8 +2785,8 @@ __global__ __launch_bounds__(1024) void attend_dma_kernel(AttendArgs a, int n_pa
   constexpr int N = 128;
   constexpr int R = kAttStages;
   extern __shared__ __align__(16) char dyn[];   // stages; reduction buffer afterwards
-  __shared__ uint2 tbl[512];
-  value_table(tbl);
+  __shared__ uint2 tbl[512 * kTblCopies];   // kTblCopies copies of the value table
+  value_table_copies<kTblCopies>(tbl);
   const int64_t s = blockIdx.z;
   const int h = blockIdx.y / n_pass;
   const int pass = blockIdx.y % n_pass;
@@ -2882,14 +2877,14 @@ __global__ __launch_bounds__(1024) void attend_dma_kernel(AttendArgs a, int n_pa
 #pragma unroll
       for (int i = 0; i < 8; ++i) ch.wt[i] = 0.f;
     }
-    att_mma4<CMP>(acc, ch, tbl, col, pmask, asel);
+    att_mma4<CMP, kTblCopies>(acc, ch, tbl, col, pmask, asel);
   }
   // the partial chunk (T not a multiple of 32), through registers
   if ((T & 31) != 0 && wv == nfull % nw) {
     AttChunk ch;
     const float* wr = wrow + (int64_t)(arow ? hh : 0) * a.T;
     att_load<false, CMP>(ch, cp + 2 * col, csp, scp, wr, nfull * 32 + 8 * kg, T, arow);
-    att_mma4<CMP>(acc, ch, tbl, col, pmask, asel);
+    att_mma4<CMP, kTblCopies>(acc, ch, tbl, col, pmask, asel);
   }
   att_wait_vm<0>();
   __syncthreads();                              // stages become the reduction buffer
