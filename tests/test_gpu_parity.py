@@ -60,6 +60,9 @@ CASES = [
                                      0, 4.0), 1, 3, 211, True),
     # compact strict packing (coset bit folded into idx_7's low bit)
     ("llama-compact", nq.Config(128, 2, 2, 0, S_, F16, 5e5, packing=CP), 2, 3, 517, False),
+    # the same with explicit positions: the plane-walking matrix-core key
+    # dequantize on compact planes
+    ("llama-compact-positions", nq.Config(128, 2, 2, 0, S_, F16, 5e5, packing=CP), 2, 3, 300, True),
     ("mistral-k3-compact", nq.Config(128, 3, 2, 64, S_, F16, 1e6, packing=CP), 2, 2, 300, True),
     ("phi3-pad-compact", nq.Config(96, 2, 3, 32, S_, F16, 1e4, packing=CP), 1, 3, 211, False),
     ("d8-compact-f32", nq.Config(8, 2, 3, 8, S_, F32, 0.0, packing=CP), 1, 2, 99, False),
