@@ -43,7 +43,7 @@ def parse():
                     help="skip the scoring run at the Qwen2.5-14B decode shape")
     ap.add_argument("--no-other-shapes", action="store_true",
                     help="skip the Mistral-7B and Phi-3-mini caches")
-    ap.add_argument("--cpu-sample-slabs", type=int, default=1,
+    ap.add_argument("--cpu-sample-slabs", type=int, default=2,
                     help="slabs of the cache (all heads and tokens, K and V) the oracle runs on")
     return ap.parse_args()
 
