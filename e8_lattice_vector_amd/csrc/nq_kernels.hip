@@ -2752,6 +2752,160 @@ __global__ __launch_bounds__(kScoreMfmaBlock, 8) void score_mfma_kernel(ScoreArg
   }
 }
 
+// ---------------------------------------------------------------------------
+// Packed-key scores on the matrix cores for 3-bit keys at n = 128 with one
+// scale per vector or one per 64 coordinates (no compact packing): the same
+// contraction as score_mfma_kernel, with the B operand formed arithmetically
+// instead of from a table.  Lane (key col, k-group kg) loads the 12 code
+// bytes of 8-groups 4 kg .. 4 kg + 3 of its key (group 4 kg + b at bits
+// 24 b .. 24 b + 23 of the three words); for product b its 8 coordinates
+// enter as bf16 of 2 p = 2 idx - 8 + c (exact small integers), and the
+// factor 1/2 joins the scale.  With two scales the halves (coordinates 0..63
+// in k-groups 0, 1; 64..127 in k-groups 2, 3) accumulate separately: each
+// product runs twice, with the B operand of the other half's lanes zeroed.
+// ---------------------------------------------------------------------------
+template <int NS>
+__device__ __forceinline__ void score_block3(const nq_bf16x8 (&A)[4], uint3 cw, uint32_t cs,
+                                             int kg, float f0, float f1, float& v0, float& v1) {
+  // coset bits of groups 4 kg .. 4 kg + 3
+  const uint32_t cb = (cs >> (4 * kg)) & 15u;
+  nq_f4 acc[NS];
+#pragma unroll
+  for (int hh = 0; hh < NS; ++hh) acc[hh] = nq_f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    // the group's 24-bit code word: 8 fields idx_j at bits 3 j
+    uint32_t g;
+    if (b == 0) g = cw.x;
+    else if (b == 1) g = __builtin_amdgcn_alignbit(cw.y, cw.x, 24);
+    else if (b == 2) g = __builtin_amdgcn_alignbit(cw.z, cw.y, 16);
+    else g = cw.z >> 8;
+    // 2 p - c + 8 = 2 idx; 2 p = 2 idx + c - 8
+    const int off = (int)((cb >> b) & 1u) - 8;
+    uint32_t bw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float lo = (float)((int)((g >> (6 * e)) & 7u) * 2 + off);
+      const float hi = (float)((int)((g >> (6 * e + 3)) & 7u) * 2 + off);
+      // bf16 of both (exact: integers below 16 in magnitude), low first
+      bw[e] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+    }
+    if (NS == 1) {
+      const nq_bf16x8 B = __builtin_bit_cast(nq_bf16x8, make_uint4(bw[0], bw[1], bw[2], bw[3]));
+      acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[b], B, acc[0], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int hh = 0; hh < NS; ++hh) {
+        const bool mine = (kg >> 1) == hh;   // this lane's coordinates are in half hh
+        const nq_bf16x8 B = __builtin_bit_cast(
+            nq_bf16x8, make_uint4(mine ? bw[0] : 0u, mine ? bw[1] : 0u, mine ? bw[2] : 0u,
+                                  mine ? bw[3] : 0u));
+        acc[hh] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[b], B, acc[hh], 0, 0, 0);
+      }
+    }
+  }
+  // rows 4 kg .. 4 kg + 3: (head 2 kg hi, lo, head 2 kg + 1 hi, lo)
+  if (NS == 1) {
+    v0 = (acc[0][0] + acc[0][1]) * f0;
+    v1 = (acc[0][2] + acc[0][3]) * f0;
+  } else {
+    v0 = (acc[0][0] + acc[0][1]) * f0 + (acc[NS - 1][0] + acc[NS - 1][1]) * f1;
+    v1 = (acc[0][2] + acc[0][3]) * f0 + (acc[NS - 1][2] + acc[NS - 1][3]) * f1;
+  }
+}
+
+// Two workgroups per CU with one scale per vector (64 VGPRs); with two, the
+// second accumulator and the masked operands need one workgroup's registers.
+template <int HPP, typename QT, int NS>
+__global__ __launch_bounds__(kScoreMfmaBlock, NS == 1 ? 8 : 4) void score_mfma3_kernel(
+    ScoreArgs a, int n_pass, int64_t chunk) {
+  static_assert(HPP <= 8, "rows are (head, part)");
+  static_assert(NS == 1 || NS == 2, "one scale per vector or per 64 coordinates");
+  constexpr int N = 128;
+  constexpr int CB = 48;                   // code bytes per key
+  constexpr int U = 2;                     // 16-key blocks per wave per step
+  extern __shared__ float qt[];            // [HPP][N] rotated queries
+  const int64_t s = blockIdx.z;
+  const int h = blockIdx.y / n_pass;
+  const int pass = blockIdx.y % n_pass;
+  const int grp = a.Hq / a.H;
+  const int hq0 = h * grp + pass * HPP;
+  const int nh = min(HPP, h * grp + grp - hq0);
+  static_assert(HPP * N <= kScoreMfmaBlock, "one query coordinate per thread");
+  const int qi = threadIdx.x;
+  float qv = 0.f;
+  if (qi < HPP * N && qi / N < nh && qi % N < a.d)
+    qv = Io<QT>::load1(a.q, (s * a.Hq + hq0 + qi / N) * (int64_t)a.d + qi % N);
+  if (qi < HPP * N) qt[qi] = qv;
+  __syncthreads();
+  rotate_queries<HPP>(qt);
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int nw = blockDim.x >> 6;
+  const int col = lane & 15;               // key of the block; A row
+  const int kg = lane >> 4;                // 8-groups 4 kg .. 4 kg + 3; heads 2 kg, 2 kg + 1
+  nq_bf16x8 A[4];
+  score_a_operands<HPP>(qt, nh, lane, A);
+  const int64_t t0 = (int64_t)blockIdx.x * chunk;
+  const int nk = (int)(min64(a.T, t0 + chunk) - t0);
+  const int64_t base = (s * a.H + h) * a.pT + t0;
+  const uint8_t* cp = a.codes + base * CB;
+  const uint16_t* csp = reinterpret_cast<const uint16_t*>(a.cosets) + base;
+  const uint16_t* scp = a.scales + base * NS;
+  float* op = a.out + (s * a.Hq + hq0) * a.T + t0;
+  const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+      op, 0, (int)(((uint32_t)(nh - 1) * (uint32_t)a.T + (uint32_t)nk) * 4u), 0x00020000);
+  const uint32_t cofs = 12u * (uint32_t)kg;
+  // the scale factor carries the 1/2 of the doubled code values
+  const float fs = 0.5f * a.inv_sqrt_n;
+  struct StepData {
+    uint3 cw[U];
+    uint32_t cs[U], sc[U];
+  };
+  auto load_step = [&](int kb_, StepData& d) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t t = (uint32_t)min(kb_ + 16 * u + col, nk - 1);
+      d.cw[u] = *reinterpret_cast<const uint3*>(cp + (t * (uint32_t)CB + cofs));
+      d.cs[u] = (uint32_t)csp[t];
+      d.sc[u] = NS == 2 ? *reinterpret_cast<const uint32_t*>(scp + 2 * t) : (uint32_t)scp[t];
+    }
+  };
+  auto compute_step = [&](int kb, const StepData& sd) {
+    float v[U][2];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      score_block3<NS>(A, sd.cw[u], sd.cs[u], kg, h2f((uint16_t)(sd.sc[u] & 0xffffu)) * fs,
+                       h2f((uint16_t)(sd.sc[u] >> 16)) * fs, v[u][0], v[u][1]);
+    // buffer stores: lanes with nothing to store take an offset past the
+    // resource's range, which the hardware drops
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = kb + 16 * u + col;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int head = 2 * kg + j;
+        const bool ok = t < nk && head < nh;
+        const uint32_t off = ok ? ((uint32_t)head * (uint32_t)a.T + (uint32_t)t) * 4u : 0xFFFFFFFCu;
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v[u][j]), orsrc, (int)off, 0, 0);
+      }
+    }
+  };
+  const int kstep = 16 * U * nw;
+  StepData d0, d1;
+  int kb = 16 * U * wv;
+  if (kb < nk) load_step(kb, d0);
+  for (; kb < nk; kb += 2 * kstep) {
+    load_step(min(kb + kstep, nk - 1), d1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_step(kb, d0);
+    if (kb + kstep >= nk) break;
+    load_step(min(kb + 2 * kstep, nk - 1), d0);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_step(kb + kstep, d1);
+  }
+}
+
 // Pipelined form of the table variant: each wave keeps kAttStages 32-token
 // chunks in flight in LDS stages, filled by direct global -> LDS loads (no
 // registers held for data in flight).  A stage holds the chunk's codes
@@ -3170,6 +3324,37 @@ hipError_t score_mfma_launch(const ScoreArgs& a, int n_pass, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int HPP, typename T, int NS>
+hipError_t score_mfma3_launch(const ScoreArgs& a, int n_pass, hipStream_t s) {
+  const size_t lds = sizeof(float) * HPP * 128;
+  const int64_t pairs = a.S * a.H * n_pass;
+  int64_t n_chunks = (512 + pairs - 1) / pairs;
+  const int64_t min_chunk = 4096;
+  n_chunks = max64(1, min64(n_chunks, (a.T + min_chunk - 1) / min_chunk));
+  const int64_t chunk = (a.T + n_chunks - 1) / n_chunks;
+  const dim3 grid((unsigned)n_chunks, (unsigned)(a.H * n_pass), (unsigned)a.S);
+  hipLaunchKernelGGL((score_mfma3_kernel<HPP, T, NS>), grid, dim3(kScoreMfmaBlock), lds, s, a,
+                     n_pass, chunk);
+  return hipGetLastError();
+}
+
+template <typename T, int NS>
+hipError_t score_mfma3(const ScoreArgs& a, hipStream_t s) {
+  const int grp = a.Hq / a.H;
+  const int n_pass = (grp + 7) / 8;
+  const int hpp = (grp + n_pass - 1) / n_pass;
+  switch (hpp) {
+    case 1: return score_mfma3_launch<1, T, NS>(a, n_pass, s);
+    case 2: return score_mfma3_launch<2, T, NS>(a, n_pass, s);
+    case 3: return score_mfma3_launch<3, T, NS>(a, n_pass, s);
+    case 4: return score_mfma3_launch<4, T, NS>(a, n_pass, s);
+    case 5: return score_mfma3_launch<5, T, NS>(a, n_pass, s);
+    case 6: return score_mfma3_launch<6, T, NS>(a, n_pass, s);
+    case 7: return score_mfma3_launch<7, T, NS>(a, n_pass, s);
+    default: return score_mfma3_launch<8, T, NS>(a, n_pass, s);
+  }
+}
+
 template <typename T>
 hipError_t score_mfma(const ScoreArgs& a, hipStream_t s) {
   const int grp = a.Hq / a.H;
@@ -3228,6 +3413,14 @@ template <int N, int BITS, typename T>
 hipError_t score_n(const ScoreArgs& a, hipStream_t s) {
   if constexpr (N == 128 && BITS == 2) {
     if (a.n_scales == 1 && a.T < ((int64_t)1 << 26)) return score_mfma<T>(a, s);
+  }
+  if constexpr (N == 128 && BITS == 3) {
+    // 4-byte code loads need the token stride to keep them aligned (48 B a
+    // key: always), the 2-scale words need 4-byte aligned scale rows
+    if (!a.compact && a.T < ((int64_t)1 << 26)) {
+      if (a.n_scales == 1) return score_mfma3<T, 1>(a, s);
+      if (a.n_scales == 2 && ((uintptr_t)a.scales & 3) == 0) return score_mfma3<T, 2>(a, s);
+    }
   }
   if constexpr (N >= 64) {
     const bool coset_bytes_align = (a.G == N) || (a.G % 64 == 0);

@@ -133,6 +133,10 @@ def test_magnitude_edges_matrix_core(scale, parity):
     (nq.Config(128, 2, 2, 0, R_, F16, 5e5), 5),
     (nq.Config(96, 2, 2, 32, S_, F16, 1e4), 3),
     (nq.Config(128, 3, 2, 64, R_, F16, 1e6), 4),
+    # 3-bit keys on the matrix cores: one scale per vector (5 heads a pass),
+    # two passes of fp32 queries with a scale per 64 coordinates
+    (nq.Config(128, 3, 2, 0, S_, F16, 1e4), 5),
+    (nq.Config(128, 3, 3, 64, R_, F32, 5e5), 12),
     (nq.Config(64, 2, 2, 0, R_, F32, 0.0), 12),
     (nq.Config(256, 3, 2, 0, S_, F16, 1e4), 2),
     (nq.Config(128, 2, 2, 64, R_, F16, 5e5), 8),
@@ -437,6 +441,29 @@ def test_matrix_core_split_precision(parity):
     log(f"[split] score {e_score:.2e}, attend {e_att:.2e}")
     assert e_score <= 1e-5, e_score
     assert e_att <= 2e-5, e_att
+
+
+@pytest.mark.parametrize("G", [0, 64])
+def test_matrix_core_split_precision_3bit(G):
+    """The 3-bit matrix-core scorer (code values formed arithmetically, the
+    same two-part query operand): within 1e-5 |q||D0 k| per score."""
+    cfg = nq.Config(128, 3, 2, G, R_, F16, 1e6)
+    S, H, T, grp = 2, 2, 4096, 4
+    log(f"[split3] G={G}")
+    k, _ = _inputs(cfg, S, H, T, 37)
+    pk, _ = nq.quantize_kv(cfg, k, None)
+    q = synth.queries(S, H * grp, 128, 37, DEV, cfg.torch_dtype)
+    sc = nq.score_packed_keys(cfg, pk, q, S, H, T)
+    torch.cuda.synchronize()
+    ck = oracle_codec(cfg, False)
+    codes, cosets, scales = to_np(pk)
+    ref = oc.score(q.cpu().numpy(), codes, cosets, scales, ck)
+    kd = oc.dequantize(codes, cosets, scales, ck, apply_rope=False)
+    kn = np.repeat(np.linalg.norm(kd, axis=-1), grp, axis=1)
+    qn = np.linalg.norm(q.cpu().numpy().astype(np.float64), axis=-1)[:, :, None]
+    e_score = np.max(np.abs(sc.cpu().numpy() - ref) / (qn * kn))
+    log(f"[split3] score {e_score:.2e}")
+    assert e_score <= 1e-5, e_score
 
 
 def test_attend_llama_full_sampled():
