@@ -856,8 +856,8 @@ __global__ __launch_bounds__(kBlock) void quantize_pair_kernel(TensorArgs a, int
 // ---------------------------------------------------------------------------
 // Quantize with the rotation on the matrix cores: vectors without RoPE
 // (values, or keys when no RoPE is removed), n = 128 with d = 128 or 96 (the
-// lanes of the padding coordinates feed zeros), 2-bit codes, one
-// scale per vector, fp16 input.
+// lanes of the padding coordinates feed zeros), 2-bit codes, one scale per
+// vector (NS = 1) or per 64 coordinates (NS = 2), fp16 input.
 //
 // The Walsh-Hadamard product u = H x of 16 vectors is a 128 x 128 by
 // 128 x 16 matrix product: 8 output tiles x 4 K chunks of
@@ -883,8 +883,9 @@ typedef _Float16 nq_f16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kQmChunk = 8;  // (slab, head) planes per wave
 
-template <bool STRICT>
+template <bool STRICT, int NS>
 __global__ __launch_bounds__(kBlock) void quantize_mfma_kernel(TensorArgs a, int sh_chunk) {
+  static_assert(NS == 1 || NS == 2, "one scale per vector or per 64 coordinates");
   const int lane = threadIdx.x & 63;
   const int v = lane & 15;
   const int p = lane >> 4;
@@ -926,8 +927,12 @@ __global__ __launch_bounds__(kBlock) void quantize_mfma_kernel(TensorArgs a, int
   const int64_t plane_x = a.T * row_x;
   const int64_t plane_c = a.pT * a.code_bytes;
   const int64_t plane_s = a.pT * a.coset_bytes;
-  const int64_t plane_g = a.pT;  // one fp16 scale per vector
-  const uint32_t off_gb = (uint32_t)(tc + (int64_t)p * plane_g) * 2u;
+  const int64_t plane_g = a.pT * NS;  // NS fp16 scales per vector
+  // scale batching: lane p stores scale (p >> 1 for NS = 2) of iteration
+  // it0 + p (NS = 1) or it0 + (p & 1) (NS = 2) of a batch starting at it0
+  const int which = NS == 2 ? (p >> 1) : 0;
+  const int mi = NS == 2 ? (p & 1) : p;
+  const uint32_t off_gb = (uint32_t)(tc * NS + which + (int64_t)mi * plane_g) * 2u;
   const int n_it = (int)(sh1 - sh0);
   const char* xb = static_cast<const char*>(a.x) + sh0 * plane_x;
   uint8_t* cb = a.codes + sh0 * plane_c;
@@ -964,8 +969,9 @@ __global__ __launch_bounds__(kBlock) void quantize_mfma_kernel(TensorArgs a, int
                                                           acc[tau], 0, 0, 0);
       }
     }
-    // vector maximum of |u|: the lane's 32 values, then the 4 lanes of the
-    // vector (16 and 32 lanes apart)
+    // maximum of |u| over the scale group: the lane's 32 values, then the
+    // lanes of the vector 16 apart (lanes p, p ^ 1 hold coordinates 0..63 or
+    // 64..127) and, with one scale per vector, 32 apart
     float mx = 0.f;
 #pragma unroll
     for (int tau = 0; tau < 8; ++tau)
@@ -975,9 +981,11 @@ __global__ __launch_bounds__(kBlock) void quantize_mfma_kernel(TensorArgs a, int
       const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(mx), __float_as_uint(mx),
                                                         false, false);
       mx = fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
-      const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx),
-                                                        false, false);
-      mx = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+      if (NS == 1) {
+        const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx),
+                                                          __float_as_uint(mx), false, false);
+        mx = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+      }
     }
     float amax;
     asm("v_max_f32 %0, %1, %2" : "=v"(amax) : "s"(a.eps), "v"(mx));
@@ -1018,11 +1026,13 @@ __global__ __launch_bounds__(kBlock) void quantize_mfma_kernel(TensorArgs a, int
       x = s32[0] | s32[1];
       if (tvalid && p == 0 && !a.compact) *reinterpret_cast<uint16_t*>(qb + os) = (uint16_t)x;
     }
-    // scales: lane p converts and stores the scale of iteration 4q + p
-    const int slot = it & 3;
-    if (p == slot) keep = amax;
-    if (slot == 3 || it == n_it - 1) {
-      if (tvalid && p <= slot) {
+    // scales: in batches of 4 / NS iterations, lane p keeps and stores the
+    // scale `which` of the batch's iteration mi
+    constexpr int BATCH = 4 / NS;
+    const int slot = it & (BATCH - 1);
+    if (mi == slot) keep = amax;
+    if (slot == BATCH - 1 || it == n_it - 1) {
+      if (tvalid && mi <= slot) {
         char* sb = gb + (int64_t)(it - slot) * plane_g * 2;
         *reinterpret_cast<uint16_t*>(sb + off_gb) = f64_to_f16_rn((double)keep * a.sigma_k);
       }
@@ -3144,15 +3154,15 @@ hipError_t quantize_pair(const TensorArgs& a, hipStream_t s) {
 }
 
 // 16 tokens per wave, kQmChunk (slab, head) planes per wave, tile-fastest.
-template <bool STRICT>
+template <bool STRICT, int NS>
 hipError_t quantize_mfma_launch(const TensorArgs& a, hipStream_t s) {
   const int64_t SH = a.n_vec / a.T;
   const int64_t n_tt = (a.T + 15) / 16;
   const int chunk = (int)(SH < kQmChunk ? SH : kQmChunk);
   const int64_t waves = n_tt * ((SH + chunk - 1) / chunk);
   const int64_t blocks = ((waves + kBlock / 64 - 1) / (kBlock / 64) + 7) / 8 * 8;
-  hipLaunchKernelGGL((quantize_mfma_kernel<STRICT>), dim3((unsigned)blocks), dim3(kBlock), 0, s,
-                     a, chunk);
+  hipLaunchKernelGGL((quantize_mfma_kernel<STRICT, NS>), dim3((unsigned)blocks), dim3(kBlock), 0,
+                     s, a, chunk);
   return hipGetLastError();
 }
 
@@ -3163,8 +3173,12 @@ hipError_t quantize_n(const TensorArgs& a, hipStream_t s) {
     if (max64(a.T, a.pT) * a.d * (int64_t)sizeof(T) < ((int64_t)1 << 31)) {
       if constexpr (N == 128 && BITS == 2 && std::is_same<T, __half>::value) {
         // d = 128, or 96 (padded to 128: the last lane quarter feeds zeros)
-        if ((a.d == 128 || a.d == 96) && a.n_scales == 1 && a.rope == nullptr)
-          return a.strict ? quantize_mfma_launch<true>(a, s) : quantize_mfma_launch<false>(a, s);
+        if ((a.d == 128 || a.d == 96) && a.rope == nullptr) {
+          if (a.n_scales == 1)
+            return a.strict ? quantize_mfma_launch<true, 1>(a, s) : quantize_mfma_launch<false, 1>(a, s);
+          if (a.n_scales == 2)
+            return a.strict ? quantize_mfma_launch<true, 2>(a, s) : quantize_mfma_launch<false, 2>(a, s);
+        }
       }
       if constexpr (N == 128 && std::is_same<T, __half>::value) {
         if (a.d == 128 && a.rope != nullptr && (a.n_scales == 1 || a.n_scales == 2))

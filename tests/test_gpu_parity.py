@@ -49,6 +49,11 @@ CASES = [
     # (16-token tiles, 8 planes per wave: ragged tiles and plane chunks)
     ("norope-relaxed", nq.Config(128, 2, 2, 0, R_, F16, 0.0), 1, 11, 45, False),
     ("norope-strict", nq.Config(128, 2, 2, 0, S_, F16, 0.0), 2, 5, 77, False),
+    # the same kernel with a scale per 64 coordinates (two scales a vector),
+    # at d = 128 and at d = 96 (padding lanes), odd plane counts for the
+    # batched scale stores
+    ("norope-g64-strict", nq.Config(128, 2, 2, 64, S_, F16, 0.0), 1, 3, 333, False),
+    ("norope-g64-d96", nq.Config(96, 2, 2, 64, R_, F16, 0.0), 1, 5, 77, False),
     # RoPE keys on the matrix-core dequantize (32 planes per wave: 35 planes
     # leave a chunk of 3; 37 tokens leave a tile of 5), explicit positions
     ("llama-plane-chunks", nq.Config(128, 2, 2, 0, R_, F16, 5e5), 5, 7, 37, True),
