@@ -45,6 +45,10 @@ CASES = [
     ("d80-g16-strict", nq.Config(80, 2, 2, 16, S_, F16, 1e4), 1, 2, 95, False),
     ("d16-g8", nq.Config(16, 2, 3, 8, S_, F16, 0.0), 3, 1, 50, False),
     ("single-token", nq.Config(128, 2, 2, 0, S_, F16, 5e5), 1, 1, 1, True),
+    # the token-walking key dequantize: one token, and one token past a
+    # whole 512-token run
+    ("single-token-pos0", nq.Config(128, 2, 2, 0, R_, F16, 5e5), 2, 3, 1, False),
+    ("run-edge", nq.Config(128, 2, 2, 0, R_, F16, 5e5), 1, 2, 513, False),
     # no RoPE removal: keys and values both take the matrix-core rotation
     # (16-token tiles, 8 planes per wave: ragged tiles and plane chunks)
     ("norope-relaxed", nq.Config(128, 2, 2, 0, R_, F16, 0.0), 1, 11, 45, False),
@@ -202,6 +206,37 @@ def test_score_one_scale_shapes(d, parity, packing, dt, grp, T, t0):
     kn = np.repeat(np.linalg.norm(kd, axis=-1), grp, axis=1)
     qnorm = np.linalg.norm(q.cpu().numpy().astype(np.float64), axis=-1)
     check_scores(s.cpu().numpy(), ref, qnorm[:, :, None], kn, "score1")
+
+
+@pytest.mark.parametrize("G,parity,dt,grp,T,t0", [
+    (0, R_, F16, 4, 4111, 0),       # ragged last block
+    (64, S_, F32, 1, 17, 0),
+    (64, R_, F16, 2, 15, 0),        # fewer keys than one 16-key block
+    (0, S_, F16, 7, 333, 3),        # 7 heads, window
+    (64, R_, F16, 8, 600, 13),      # all 16 rows, window at an odd offset
+    (0, R_, F16, 12, 1, 0),         # two passes of 6 heads, one key
+])
+def test_score_3bit_shapes(G, parity, dt, grp, T, t0):
+    """3-bit keys at n = 128 (the matrix-core scorer, one or two scales per
+    vector): head counts, query dtypes, ragged and tiny key counts, token
+    windows."""
+    cfg = nq.Config(128, 3, 2, G, parity, dt, 1e4)
+    S, H = 2, 2
+    log(f"[score3] G={G} parity={parity} dt={dt} grp={grp} T={T} t0={t0}")
+    k, _ = _inputs(cfg, S, H, T, 29, pos=np.arange(t0, t0 + T))
+    pk = nq.alloc_packed(cfg, False, S, H, t0 + T + 5, DEV)
+    nq.quantize_kv(cfg, k, None, pk=pk, token_offset=t0)
+    q = synth.queries(S, H * grp, cfg.head_dim, 29, DEV, cfg.torch_dtype)
+    s = nq.score_packed_keys(cfg, pk, q, S, H, T, token_offset=t0)
+    torch.cuda.synchronize()
+    codec = oracle_codec(cfg, False)
+    codes, cosets, scales = (pl[:, :, t0:t0 + T].cpu().numpy()
+                             for pl in (pk.codes, pk.cosets, pk.scales))
+    ref = oc.score(q.cpu().numpy(), codes, cosets, scales, codec)
+    kd = oc.dequantize(codes, cosets, scales, codec, apply_rope=False)
+    kn = np.repeat(np.linalg.norm(kd, axis=-1), grp, axis=1)
+    qnorm = np.linalg.norm(q.cpu().numpy().astype(np.float64), axis=-1)
+    check_scores(s.cpu().numpy(), ref, qnorm[:, :, None], kn, "score3")
 
 
 @pytest.mark.parametrize("bits", [2, 3])
