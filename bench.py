@@ -3,7 +3,7 @@
 Headline (the metric): quantize + pack of the Llama-3.1-8B 32K-token cache
 (32 layers x 8 KV heads x 32768 tokens x head_dim 128, fp16 K and V, k2v2
 relaxed, one scale per head vector); `value` = tokens of the cache / median
-time of the K and V quantize calls (HIP events on the kernels' stream).
+time of one quantize call on K and V (HIP events on the kernels' stream).
 
 One step = the whole path over that cache:
   1. quantize + pack K (RoPE removed, theta 5e5) and V      nq_quantize_kv
