@@ -12,6 +12,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace nq {
 
 // Decisions of the fp32 decoders whose margin -- the squared-distance gap
@@ -132,17 +134,54 @@ __device__ __forceinline__ void e8_decode(const F y[8], uint32_t& code, int& cos
   const int odd1 = STRICT ? (((S1 + 2 * NS) >> 1) & 1) : 0;
   F b0 = -INFINITY, b1 = -INFINITY, s0 = -INFINITY, s1 = -INFINITY;
   int i0 = 0, i1 = 0;
+  if (std::is_same<F, float>::value && margin) {
+    // fp32 with a margin (the hot paths): the largest and second largest
+    // kappa as unsigned keys, no compare masks.  kappa >= 0 (ok) maps to
+    // 0x80000000 | bits(|d|), kappa < 0 to 0x7fffffff ^ bits(|d|), so the
+    // keys order like kappa; the low 3 bits are replaced by 7 - k, so the
+    // lowest index wins exact ties.  Kappas within 8 ulps may pick either
+    // coordinate and carry up to 8 ulps (< 2e-6) into the costs, but the
+    // gap between them is then far below kNearTie, so those groups are
+    // re-decided in fp64 anyway.  ok is the sign bit of d or of P - (L - 3)
+    // (resp. L - 2).
+    uint32_t kb0 = 0u, ks0 = 0u, kb1 = 0u, ks1 = 0u;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const bool ok0 = (d0[k] < 0) || (P0[k] <= L - 4);
-    const F k0 = ok0 ? fabs(d0[k]) : -fabs(d0[k]);
-    if (margin) s0 = median3(b0, s0, k0);
-    if (k0 > b0) { b0 = k0; i0 = k; }
-    if (STRICT || margin) {
-      const bool ok1 = (d1[k] < 0) || (P1[k] <= L - 3);
-      const F k1 = ok1 ? fabs(d1[k]) : -fabs(d1[k]);
-      if (STRICT && margin) s1 = median3(b1, s1, k1);
-      if (k1 > b1) { b1 = k1; i1 = k; }
+    for (int k = 0; k < 8; ++k) {
+      const uint32_t u0 = __float_as_uint((float)d0[k]);
+      const uint32_t m0 = (uint32_t)((int32_t)(u0 | (uint32_t)(P0[k] - (L - 3))) >> 31);
+      const uint32_t key0 = (((~u0 & 0x7fffffffu) ^ m0) & ~7u) | (uint32_t)(7 - k);
+      ks0 = median3u(kb0, ks0, key0);
+      kb0 = max(kb0, key0);
+      const uint32_t u1 = __float_as_uint((float)d1[k]);
+      const uint32_t m1 = (uint32_t)((int32_t)(u1 | (uint32_t)(P1[k] - (L - 2))) >> 31);
+      const uint32_t key1 = (((~u1 & 0x7fffffffu) ^ m1) & ~7u) | (uint32_t)(7 - k);
+      if (STRICT) ks1 = median3u(kb1, ks1, key1);
+      kb1 = max(kb1, key1);
+    }
+    const auto unkey = [](uint32_t key) -> float {
+      const uint32_t kk = key & ~7u;
+      return (kk & 0x80000000u) ? __uint_as_float(kk & 0x7fffffffu)
+                                : -__uint_as_float(kk ^ 0x7ffffff8u);
+    };
+    b0 = unkey(kb0);
+    s0 = unkey(ks0);
+    i0 = 7 - (int)(kb0 & 7u);
+    b1 = unkey(kb1);
+    s1 = STRICT ? unkey(ks1) : (F)-INFINITY;
+    i1 = 7 - (int)(kb1 & 7u);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const bool ok0 = (d0[k] < 0) || (P0[k] <= L - 4);
+      const F k0 = ok0 ? fabs(d0[k]) : -fabs(d0[k]);
+      if (margin) s0 = median3(b0, s0, k0);
+      if (k0 > b0) { b0 = k0; i0 = k; }
+      if (STRICT || margin) {
+        const bool ok1 = (d1[k] < 0) || (P1[k] <= L - 3);
+        const F k1 = ok1 ? fabs(d1[k]) : -fabs(d1[k]);
+        if (STRICT && margin) s1 = median3(b1, s1, k1);
+        if (k1 > b1) { b1 = k1; i1 = k; }
+      }
     }
   }
   if (odd0) D0 = D0 + fma((F)-4, b0, (F)4);
