@@ -1504,16 +1504,17 @@ __global__ __launch_bounds__(kBlock) void dequantize_mfma_kernel(TensorArgs a, i
 
 // Token-walking form (positions pos0 + t): a wave walks a run of kDtRun
 // tiles of one (slab, head) plane, so each wave writes one contiguous
-// stretch of output (128 KiB).  It copies the packed words of kDtChunk tiles
+// stretch of output (32 KiB).  It copies the packed words of kDtChunk tiles
 // at a time into its LDS slice; the tiles of a chunk then issue no global
 // load, only stores, which therefore never wait for one another (with a
 // tile's words loaded from global memory in the loop, the wait for them also
 // waited out the previous tile's stores).  The lane's cos / sin are formed
 // at the run's first tile and rotated by the angle of 16 tokens
 // (host-computed cos / sin of 16 omega) from tile to tile: after at most
-// kDtRun - 1 rotations they are within a few 1e-6 of the directly formed
-// values.
-constexpr int kDtRun = 32;
+// kDtRun - 1 rotations they are within 4e-7 of the directly formed
+// values.  Runs of one chunk measured faster than runs of 16 or 32 tiles,
+// although each run forms its 16 cos / sin pairs afresh.
+constexpr int kDtRun = 8;
 constexpr int kDtChunk = 8;
 constexpr int kDtTok = 16 * kDtChunk;   // tokens per chunk
 
