@@ -45,10 +45,11 @@ CASES = [
     ("d80-g16-strict", nq.Config(80, 2, 2, 16, S_, F16, 1e4), 1, 2, 95, False),
     ("d16-g8", nq.Config(16, 2, 3, 8, S_, F16, 0.0), 3, 1, 50, False),
     ("single-token", nq.Config(128, 2, 2, 0, S_, F16, 5e5), 1, 1, 1, True),
-    # the token-walking key dequantize: one token, and one token past a
-    # whole 512-token run
+    # the token-walking key dequantize (runs of 128 tokens): one token, one
+    # token past whole runs, one token short of two runs
     ("single-token-pos0", nq.Config(128, 2, 2, 0, R_, F16, 5e5), 2, 3, 1, False),
     ("run-edge", nq.Config(128, 2, 2, 0, R_, F16, 5e5), 1, 2, 513, False),
+    ("run-short", nq.Config(128, 2, 2, 0, R_, F16, 5e5), 1, 3, 255, False),
     # no RoPE removal: keys and values both take the matrix-core rotation
     # (16-token tiles, 8 planes per wave: ragged tiles and plane chunks)
     ("norope-relaxed", nq.Config(128, 2, 2, 0, R_, F16, 0.0), 1, 11, 45, False),
