@@ -1361,7 +1361,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dm_rsrc(char* p, int64_t bytes
 // offset past the buffer's end, which the hardware drops, so no store is
 // conditional and the compiler's wait counts stay exact.  The stores are
 // non-temporal, as every dequantized output is.
-template <bool CMP>
+template <bool CMP, bool ROPE = true>
 __device__ __forceinline__ void dm_tile(const DmFrags& h, const DmMeta& m, float half_rs,
                                         const float (&rc)[4][4], const float (&rn)[4][4],
                                         char* tile, int v, int p, __amdgpu_buffer_rsrc_t yr,
@@ -1403,8 +1403,13 @@ __device__ __forceinline__ void dm_tile(const DmFrags& h, const DmMeta& m, float
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float lo = acc[q][r] * f, up = acc[q + 4][r] * f;
-      xl[r] = __fmaf_rn(lo, rc[q][r], -(up * rn[q][r]));
-      xu[r] = __fmaf_rn(up, rc[q][r], lo * rn[q][r]);
+      if (ROPE) {
+        xl[r] = __fmaf_rn(lo, rc[q][r], -(up * rn[q][r]));
+        xu[r] = __fmaf_rn(up, rc[q][r], lo * rn[q][r]);
+      } else {
+        xl[r] = lo;
+        xu[r] = up;
+      }
     }
 #pragma unroll
     for (int hi = 0; hi < 2; ++hi) {
@@ -1518,7 +1523,7 @@ constexpr int kDtRun = 8;
 constexpr int kDtChunk = 8;
 constexpr int kDtTok = 16 * kDtChunk;   // tokens per chunk
 
-template <bool CMP>
+template <bool CMP, bool ROPE>
 __global__ __launch_bounds__(kBlock) void dequantize_mfma_tw_kernel(TensorArgs a, RopeFreqs f) {
   const int lane = threadIdx.x & 63;
   const int v = lane & 15;
@@ -1542,14 +1547,14 @@ __global__ __launch_bounds__(kBlock) void dequantize_mfma_tw_kernel(TensorArgs a
   uint16_t* mg = mq + kDtTok;
   float* mst = reinterpret_cast<float*>(mc + kDtTok * 36);
   char* tile = lds_tiles[threadIdx.x >> 6];
-  {
+  if (ROPE) {
     const int k = dm_freq(p, (lane >> 2) & 3, lane & 3);
     mst[32 * p + (lane & 15)] = f.step_c[k];
     mst[32 * p + 16 + (lane & 15)] = f.step_s[k];
   }
   const DmFrags h = dm_frags(v, p);
-  float rc[4][4], rn[4][4];
-  dm_cos_sin((double)(a.pos0 + tt0 * 16 + v), f, p, rc, rn);
+  float rc[4][4] = {}, rn[4][4] = {};
+  if (ROPE) dm_cos_sin((double)(a.pos0 + tt0 * 16 + v), f, p, rc, rn);
   const float4* stp = reinterpret_cast<const float4*>(mst + 32 * p);
   const float half_rs = 0.5f * a.inv_sqrt_n;
   const __amdgpu_buffer_rsrc_t yr =
@@ -1580,10 +1585,11 @@ __global__ __launch_bounds__(kBlock) void dequantize_mfma_tw_kernel(TensorArgs a
       m.cw = *reinterpret_cast<const uint2*>(mc + 32 * t + 8 * p);
       m.cs = CMP ? 0u : (uint32_t)mq[t];
       m.sb = (uint32_t)mg[t];
-      dm_tile<CMP>(h, m, half_rs, rc, rn, tile, v, p, yr, 4096u * (uint32_t)it,
+      dm_tile<CMP, ROPE>(h, m, half_rs, rc, rn, tile, v, p, yr, 4096u * (uint32_t)it,
                    min(16, nt - 16 * it));
       // the step's cos / sin are read after the tile, not held through it
       __builtin_amdgcn_sched_barrier(0);
+      if (!ROPE) continue;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const float4 dc4 = stp[q], dn4 = stp[4 + q];
@@ -3245,11 +3251,11 @@ inline hipError_t dequantize_mfma_launch(const TensorArgs& a, const RopeFreqs& f
     const int64_t waves = SH * ((n_tt + kDtRun - 1) / kDtRun);
     const int64_t blocks = ((waves + kBlock / 64 - 1) / (kBlock / 64) + 7) / 8 * 8;
     if (a.compact)
-      hipLaunchKernelGGL((dequantize_mfma_tw_kernel<true>), dim3((unsigned)blocks), dim3(kBlock),
-                         0, s, a, f);
+      hipLaunchKernelGGL((dequantize_mfma_tw_kernel<true, true>), dim3((unsigned)blocks),
+                         dim3(kBlock), 0, s, a, f);
     else
-      hipLaunchKernelGGL((dequantize_mfma_tw_kernel<false>), dim3((unsigned)blocks), dim3(kBlock),
-                         0, s, a, f);
+      hipLaunchKernelGGL((dequantize_mfma_tw_kernel<false, true>), dim3((unsigned)blocks),
+                         dim3(kBlock), 0, s, a, f);
     return hipGetLastError();
   }
   const int chunk = (int)(SH < kDmChunk ? SH : kDmChunk);
@@ -3261,6 +3267,23 @@ inline hipError_t dequantize_mfma_launch(const TensorArgs& a, const RopeFreqs& f
   else
     hipLaunchKernelGGL((dequantize_mfma_kernel<false>), dim3((unsigned)blocks), dim3(kBlock), 0, s,
                        a, chunk, f);
+  return hipGetLastError();
+}
+
+// Vectors without RoPE (values) on the same token-walking matrix-core
+// kernel: d = n = 128, 2 bits, one scale per vector, fp16 output.
+inline hipError_t dequantize_mfma_tw_norope_launch(const TensorArgs& a, hipStream_t s) {
+  static const RopeFreqs none{};   // not read without RoPE
+  const int64_t SH = a.n_vec / a.T;
+  const int64_t n_tt = (a.T + 15) / 16;
+  const int64_t waves = SH * ((n_tt + kDtRun - 1) / kDtRun);
+  const int64_t blocks = ((waves + kBlock / 64 - 1) / (kBlock / 64) + 7) / 8 * 8;
+  if (a.compact)
+    hipLaunchKernelGGL((dequantize_mfma_tw_kernel<true, false>), dim3((unsigned)blocks),
+                       dim3(kBlock), 0, s, a, none);
+  else
+    hipLaunchKernelGGL((dequantize_mfma_tw_kernel<false, false>), dim3((unsigned)blocks),
+                       dim3(kBlock), 0, s, a, none);
   return hipGetLastError();
 }
 
@@ -3276,6 +3299,9 @@ template <int N, int BITS, typename T>
 hipError_t dequantize_n(const TensorArgs& a, const RopeFreqs* f, hipStream_t s) {
   if constexpr (N == 128 && BITS == 2 && std::is_same<T, __half>::value) {
     if (f != nullptr && forms_rope_rows(a, 0)) return dequantize_mfma_launch(a, *f, s);
+    if (a.rope == nullptr && a.n == 128 && a.d == 128 && a.n_scales == 1 &&
+        max64(a.T, a.pT) * 256 < ((int64_t)1 << 31))
+      return dequantize_mfma_tw_norope_launch(a, s);
   }
   if constexpr ((N == 64 || N == 128) && (N * BITS / 8) % 16 == 0) {
     if (a.rope == nullptr) return dequantize_tw_launch<N, BITS, T>(a, s);
