@@ -1360,7 +1360,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dm_rsrc(char* p, int64_t bytes
 // buffer yr.  Rows from `rows` on are not stored: their stores take an
 // offset past the buffer's end, which the hardware drops, so no store is
 // conditional and the compiler's wait counts stay exact.  The stores are
-// non-temporal, as every dequantized output is.
+// non-temporal, as every dequantized output is.  ROPE = false skips the
+// rotation (rc, rn unused).
 template <bool CMP, bool ROPE = true>
 __device__ __forceinline__ void dm_tile(const DmFrags& h, const DmMeta& m, float half_rs,
                                         const float (&rc)[4][4], const float (&rn)[4][4],
@@ -1518,7 +1519,11 @@ __global__ __launch_bounds__(kBlock) void dequantize_mfma_kernel(TensorArgs a, i
 // (host-computed cos / sin of 16 omega) from tile to tile: after at most
 // kDtRun - 1 rotations they are within 4e-7 of the directly formed
 // values.  Runs of one chunk measured faster than runs of 16 or 32 tiles,
-// although each run forms its 16 cos / sin pairs afresh.
+// although each run forms its 16 cos / sin pairs afresh.  Without ROPE
+// (values, keys with theta = 0) no cos / sin are formed and the tile is
+// only scaled; f is then not read.  One scale per vector only: with a scale
+// per 64 coordinates the scales would apply before the inverse rotation,
+// inside the product, not to its output.
 constexpr int kDtRun = 8;
 constexpr int kDtChunk = 8;
 constexpr int kDtTok = 16 * kDtChunk;   // tokens per chunk
