@@ -227,15 +227,16 @@ int nq_quantize_kv_noalloc(const nq_config* cfg, const void* k, const void* v,
  * the device; [RM] "How it works": RoPE re-applied after quantization):
  * p = idx - L/2 + c/2, z = s16 * p, x = (H z / sqrt(n))[:d], keys get RoPE
  * at `positions` (rope_theta > 0), rounded to the output dtype (RNE).
- * Arithmetic: fp32.  For fp16 keys with RoPE at d = n = 128, 2 bits, one
- * scale per vector, H p is formed exactly on the matrix cores and scaled by
- * s16 / sqrt(n) once; otherwise z = s16 / sqrt(n) * p goes through butterfly
- * stages.  RoPE cos / sin: fp64 angle reduction, then fp32 sincos (the
- * quantize path's values), except for those matrix-core keys with positions
- * == NULL: there the kernel forms them at the start of each 512-token run
- * and rotates them by the 16-token angle step (within 2e-6 of the directly
- * formed values), so a window read at token_offset may differ from a read
- * with explicit positions by one step of the output dtype.
+ * Arithmetic: fp32.  For fp16 output at d = n = 128, 2 bits, one scale per
+ * vector (keys with RoPE, and vectors without it), H p is formed exactly on
+ * the matrix cores and scaled by s16 / sqrt(n) once; otherwise
+ * z = s16 / sqrt(n) * p goes through butterfly stages.  RoPE cos / sin: fp64
+ * angle reduction, then fp32 sincos (the quantize path's values), except
+ * for those matrix-core keys with positions == NULL: there the kernel forms
+ * them at the start of each 128-token run and rotates them by the 16-token
+ * angle step (within 4e-7 of the directly formed values), so a window read
+ * at token_offset may differ from a read with explicit positions by one step
+ * of the output dtype.
  *  k_out, v_out  device [S][H][T][d] outputs (either may be NULL)
  *  workspace     with keys and rope_theta > 0: at least the fp32 RoPE table
  *                (T * d/2 * 8 bytes, e.g. a workspace of nq_workspace_bytes);
