@@ -186,6 +186,10 @@ def test_score_parity(cfg, grp):
     (96, S_, 0, F16, 4, 777, 0),        # d < n
     (128, R_, 0, F16, 4, 600, 13),      # window at an odd token offset
     (128, S_, 0, F16, 12, 1, 0),        # two passes of 6 heads, one key
+    # 5-8 heads a pass with rows a multiple of 4 keys: 16-byte score stores
+    # (window at an odd offset; two key chunks a plane)
+    (128, R_, 0, F16, 6, 1024, 5),
+    (128, S_, 0, F16, 5, 8192, 0),
 ])
 def test_score_one_scale_shapes(d, parity, packing, dt, grp, T, t0):
     """2-bit keys with one scale per vector (the matrix-core scorer): head
