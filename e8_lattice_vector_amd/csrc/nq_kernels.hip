@@ -3141,10 +3141,12 @@ inline int sh_chunk_for(int64_t SH, int64_t n_tt) {
 }
 
 // (slab, head) planes per quantize wave: up to 64, so that a wave reads its
-// token tile's RoPE rows once for many planes, but no fewer than about 8192
-// waves in all (short caches would otherwise leave most SIMDs idle).
+// token tile's RoPE rows once for many planes, but no fewer than about 16384
+// waves in all (short caches would otherwise leave most SIMDs idle; at the
+// Mistral-7B shape 16384 waves measured 1.2 % faster than 8192 and the same
+// as 32768).
 inline int quantize_chunk(int64_t SH, int64_t n_tt) {
-  int64_t c = SH * n_tt / 8192;
+  int64_t c = SH * n_tt / 16384;
   if (c > 64) c = 64;
   if (c > SH) c = SH;
   if (c < 1) c = 1;
